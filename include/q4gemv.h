@@ -1,0 +1,125 @@
+/*
+ * q4gemv.h -- C ABI of the MI355X (gfx950) int4 decode-GEMV library.
+ *
+ * The library computes the bandwidth-bound decode GEMV over block-quantised
+ * 4-bit weights,
+ *
+ *     y[m, n] = sum_k x[m, k] * (q(n, k) - z(n, k / g)) * s(n, k / g),
+ *
+ * (gerbil "WGSL Kernel Reference", section 3 MatMulInt4: "Computes",
+ * "INT4 Packing", "Dequantization"), plus a dense fp32 control GEMV, a
+ * dequantiser for debugging and two HBM bandwidth probes (webgpu-bench 0.1.0
+ * README, "What it measures": read-bandwidth and write-bandwidth).
+ *
+ * Storage format (all row-major, N-major weights W_q[N, K]):
+ *   x       float32 [M, K]
+ *   wq      uint8   [N, K/2]        code of (n, k) in byte n*K/2 + k/2:
+ *                                   low nibble for even k, high for odd k
+ *   scales  uint16  [N, G]          IEEE binary16 bit patterns, G = K / g
+ *   zeros   uint8   [N, (G+1)/2]    zero point of group j of row n in byte
+ *                                   n*((G+1)/2) + j/2: low nibble for even j
+ *   y       float32 [M, N]
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors) owned
+ *     by the caller.  The library never allocates, frees or keeps them.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL selects the
+ *     default stream) and may be captured into a HIP graph.
+ *   - Return value: Q4_OK (0) or a negative q4_status.  Arguments are fully
+ *     validated before anything is launched; on an argument error nothing is
+ *     launched and no output memory is touched.  A launch failure returns
+ *     Q4_ELAUNCH.  No call ever returns Q4_OK without having launched its
+ *     work, except where a size argument makes the output empty (N == 0 or
+ *     n_floats == 0), which is documented per call.
+ *   - The library runs on gfx950 only; any other device gives Q4_EDEVICE.
+ */
+#ifndef Q4GEMV_H
+#define Q4GEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q4GEMV_ABI_VERSION 1
+
+enum q4_status {
+    Q4_OK = 0,
+    Q4_EINVAL = -1,  /* a size, shape or group-size argument is out of range */
+    Q4_ENULL = -2,   /* a required pointer is NULL */
+    Q4_EALIGN = -3,  /* a pointer breaks its alignment rule */
+    Q4_EDEVICE = -4, /* no HIP device, or the current device is not gfx950 */
+    Q4_ELAUNCH = -5  /* the kernel launch reported an error */
+};
+
+/* int4 decode GEMV: y[M, N] = x[M, K] . dequant(W_q[N, K])^T, fp32 accumulate.
+ * Dequantisation (q - z) * s is exact in fp32; products with x are fused
+ * multiply-adds in fp32 (gerbil "WGSL Kernel Reference", section 3
+ * MatMulInt4, "Dequantization").
+ *   1 <= M <= 8;  N >= 0 (N == 0 launches nothing);  group_size in {32, 128};
+ *   K >= group_size and K % group_size == 0.
+ *   x and wq 16-byte aligned; scales 2-byte aligned; y 4-byte aligned.
+ *   y must not overlap any input. */
+int gemv_q4(const float *x, const uint8_t *wq, const uint16_t *scales,
+            const uint8_t *zeros, float *y, int M, int N, int K, int group_size,
+            void *stream);
+
+/* Dense fp32 control GEMV, y[M, N] = x[M, K] . w[N, K]^T (cera 0.5.0
+ * wgpu_gemv_bench.rs: the f32 kernel kept in the table as the control).
+ *   1 <= M <= 8;  N >= 0 (N == 0 launches nothing);  K >= 4, K % 4 == 0.
+ *   x and w 16-byte aligned; y 4-byte aligned. */
+int gemv_f32(const float *x, const float *w, float *y, int M, int N, int K, void *stream);
+
+/* Debug dequantiser (gerbil "WGSL Kernel Reference", section 3 MatMulInt4,
+ * "INT4 Packing" and "Dequantization").  Writes, for every (n, k):
+ *   w_out[n*K + k]     = (float)(q - z) * s      (bit-exact; may be NULL)
+ *   codes_out[n*K + k] = q                        (0..15;   may be NULL)
+ * At least one output must be non-NULL.
+ *   N >= 0 (N == 0 launches nothing); group_size in {32, 128}; K >= group_size,
+ *   K % group_size == 0.  wq 16-byte aligned, scales 2-byte aligned, w_out
+ *   16-byte aligned, codes_out 8-byte aligned. */
+int dequant_q4(const uint8_t *wq, const uint16_t *scales, const uint8_t *zeros,
+               float *w_out, uint8_t *codes_out, int N, int K, int group_size,
+               void *stream);
+
+/* Read-bandwidth probe (webgpu-bench 0.1.0 README, read-bandwidth; Refractometer
+ * "What each sweep measures", bandwidth: vec4 read-reduce).  Streams buf with
+ * 16-byte loads folded by addition only and writes one partial sum per
+ * workgroup: exactly n_partials workgroups are launched and
+ * partials[0 .. n_partials) are all written.  The caller adds the partials.
+ *   buf 16-byte aligned, n_floats % 4 == 0 (n_floats == 0 writes zeros);
+ *   1 <= n_partials <= 65536; partials 4-byte aligned. */
+int read_reduce(const float *buf, size_t n_floats, float *partials, int n_partials,
+                void *stream);
+
+/* Write-bandwidth probe (webgpu-bench 0.1.0 README, write-bandwidth): stores
+ * `value` to every element with 16-byte stores and no reads.
+ *   buf 16-byte aligned, n_floats % 4 == 0 (n_floats == 0 launches nothing);
+ *   0 <= n_blocks <= 65536 (0 picks the default grid). */
+int write_fill(float *buf, size_t n_floats, float value, int n_blocks, void *stream);
+
+/* Launch geometry that gemv_q4 would use for a shape, for reporting and
+ * tests; host-only, launches nothing and needs no device.  Any output
+ * pointer may be NULL.  Returns Q4_EINVAL for an invalid shape.
+ *   grid         workgroups launched
+ *   block        threads per workgroup
+ *   rows_per_wave output rows one wavefront owns
+ *   lanes_per_row lanes that share one row's K range (16, 32 or 64)
+ *   ksplit       wavefronts that split one row block's K range
+ *   segments     x segments staged through LDS one after another */
+int gemv_q4_geometry(int M, int N, int K, int group_size, int *grid, int *block,
+                     int *rows_per_wave, int *lanes_per_row, int *ksplit, int *segments);
+
+/* Human-readable text for a q4_status value (never NULL). */
+const char *q4_strerror(int status);
+
+/* Q4GEMV_ABI_VERSION of the built library. */
+int q4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4GEMV_H */

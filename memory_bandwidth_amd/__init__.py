@@ -1,0 +1,196 @@
+"""Thin Python binding of libq4gemv.so (the MI355X int4 decode-GEMV library).
+
+Every function has the name of the C entry point it calls and only marshals
+arguments: it checks dtypes, shapes, contiguity and device, passes raw device
+pointers and torch's current HIP stream, and raises Q4Error on a non-zero
+status.  All arithmetic runs in the library's HIP kernels; there is no other
+implementation here.  Importing this module without the built library works
+(so CPU-only tooling can inspect it), but every call then raises.
+
+Storage format (see include/q4gemv.h): x float32 [M, K]; wq uint8 [N, K/2]
+(two codes per byte, low nibble = even k); scales float16 or uint16 [N, K/g]
+(binary16 bits); zeros uint8 [N, ceil(K/g / 2)] (low nibble = even group).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libq4gemv.so")
+
+Q4_OK, Q4_EINVAL, Q4_ENULL, Q4_EALIGN, Q4_EDEVICE, Q4_ELAUNCH = 0, -1, -2, -3, -4, -5
+
+# Exported C symbols, in the order include/q4gemv.h declares them.
+EXPORTS = ("gemv_q4", "gemv_f32", "dequant_q4", "read_reduce", "write_fill",
+           "gemv_q4_geometry", "q4_strerror", "q4_abi_version")
+
+_lib = None
+
+
+class Q4Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {strerror(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library {LIB_PATH} is not built; run "
+                           "`python -m memory_bandwidth_amd.build` first")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.gemv_q4.argtypes = [P, P, P, P, P, I, I, I, I, P]
+    L.gemv_f32.argtypes = [P, P, P, I, I, I, P]
+    L.dequant_q4.argtypes = [P, P, P, P, P, I, I, I, P]
+    L.read_reduce.argtypes = [P, Z, P, I, P]
+    L.write_fill.argtypes = [P, Z, ctypes.c_float, I, P]
+    IP = ctypes.POINTER(ctypes.c_int)
+    L.gemv_q4_geometry.argtypes = [I, I, I, I, IP, IP, IP, IP, IP, IP]
+    L.q4_strerror.argtypes = [I]
+    L.q4_strerror.restype = ctypes.c_char_p
+    L.q4_abi_version.argtypes = []
+    for f in ("gemv_q4", "gemv_f32", "dequant_q4", "read_reduce", "write_fill",
+              "gemv_q4_geometry", "q4_abi_version"):
+        getattr(L, f).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def strerror(status: int) -> str:
+    return lib().q4_strerror(status).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != Q4_OK:
+        raise Q4Error(fn, status)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtypes, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def gemv_q4(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+            group_size: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """y[M, N] = x[M, K] . dequant(W_q[N, K])^T on the current stream."""
+    _need(x, "x", (torch.float32,))
+    dev = x.device
+    _need(wq, "wq", (torch.uint8,), dev)
+    _need(scales, "scales", (torch.float16, torch.uint16, torch.int16), dev)
+    _need(zeros, "zeros", (torch.uint8,), dev)
+    if x.dim() != 2 or wq.dim() != 2:
+        raise ValueError("x must be [M, K] and wq [N, K/2]")
+    M, K = x.shape
+    N = wq.shape[0]
+    g = int(group_size)
+    G = K // g if g else 0
+    if wq.shape[1] * 2 != K or tuple(scales.shape) != (N, G) or tuple(zeros.shape) != (N, (G + 1) // 2):
+        raise ValueError(f"shape mismatch: x{tuple(x.shape)} wq{tuple(wq.shape)} "
+                         f"scales{tuple(scales.shape)} zeros{tuple(zeros.shape)} g={g}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    else:
+        _need(out, "out", (torch.float32,), dev)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out must be [M, N]")
+    _check("gemv_q4", lib().gemv_q4(_ptr(x), _ptr(wq), _ptr(scales), _ptr(zeros), _ptr(out),
+                                    M, N, K, g, _stream(dev)))
+    return out
+
+
+def gemv_f32(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Dense control: y[M, N] = x[M, K] . w[N, K]^T on the current stream."""
+    _need(x, "x", (torch.float32,))
+    dev = x.device
+    _need(w, "w", (torch.float32,), dev)
+    if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
+        raise ValueError("x must be [M, K] and w [N, K]")
+    M, K = x.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    else:
+        _need(out, "out", (torch.float32,), dev)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out must be [M, N]")
+    _check("gemv_f32", lib().gemv_f32(_ptr(x), _ptr(w), _ptr(out), M, N, K, _stream(dev)))
+    return out
+
+
+def dequant_q4(wq: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, group_size: int,
+               want_weights: bool = True, want_codes: bool = True):
+    """Returns (W float32 [N, K] or None, codes uint8 [N, K] or None)."""
+    _need(wq, "wq", (torch.uint8,))
+    dev = wq.device
+    _need(scales, "scales", (torch.float16, torch.uint16, torch.int16), dev)
+    _need(zeros, "zeros", (torch.uint8,), dev)
+    N, K = wq.shape[0], wq.shape[1] * 2
+    g = int(group_size)
+    G = K // g if g else 0
+    if tuple(scales.shape) != (N, G) or tuple(zeros.shape) != (N, (G + 1) // 2):
+        raise ValueError("scales/zeros shape mismatch")
+    w = torch.empty((N, K), dtype=torch.float32, device=dev) if want_weights else None
+    c = torch.empty((N, K), dtype=torch.uint8, device=dev) if want_codes else None
+    _check("dequant_q4", lib().dequant_q4(_ptr(wq), _ptr(scales), _ptr(zeros), _ptr(w), _ptr(c),
+                                          N, K, g, _stream(dev)))
+    return w, c
+
+
+def read_reduce(buf: torch.Tensor, n_partials: int, partials: torch.Tensor | None = None) -> torch.Tensor:
+    """Launches the read probe; returns the per-workgroup partial sums (add them for the total)."""
+    _need(buf, "buf", (torch.float32,))
+    dev = buf.device
+    if partials is None:
+        partials = torch.empty(n_partials, dtype=torch.float32, device=dev)
+    else:
+        _need(partials, "partials", (torch.float32,), dev)
+        if partials.numel() < n_partials:
+            raise ValueError("partials too small")
+    _check("read_reduce", lib().read_reduce(_ptr(buf), buf.numel(), _ptr(partials), n_partials,
+                                            _stream(dev)))
+    return partials
+
+
+def write_fill(buf: torch.Tensor, value: float, n_blocks: int = 0) -> torch.Tensor:
+    """Fills buf with value using the write probe."""
+    _need(buf, "buf", (torch.float32,))
+    _check("write_fill", lib().write_fill(_ptr(buf), buf.numel(), float(value), n_blocks,
+                                          _stream(buf.device)))
+    return buf
+
+
+def gemv_q4_geometry(M: int, N: int, K: int, group_size: int) -> dict:
+    """Launch geometry gemv_q4 picks for a shape (host-only, needs no GPU)."""
+    vals = [ctypes.c_int() for _ in range(6)]
+    _check("gemv_q4_geometry", lib().gemv_q4_geometry(M, N, K, group_size,
+                                                      *[ctypes.byref(v) for v in vals]))
+    keys = ("grid", "block", "rows_per_wave", "lanes_per_row", "ksplit", "segments")
+    return {k: v.value for k, v in zip(keys, vals)}
+
+
+def abi_version() -> int:
+    return lib().q4_abi_version()

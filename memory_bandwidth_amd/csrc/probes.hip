@@ -1,0 +1,87 @@
+// probes.hip -- HBM bandwidth probes for gfx950.
+//
+// read_reduce streams a buffer with 16-byte loads folded by addition only
+// and writes one partial sum per workgroup (webgpu-bench 0.1.0 README,
+// read-bandwidth; Refractometer "What each sweep measures", bandwidth: vec4
+// read-reduce).  write_fill stores a constant with 16-byte stores and reads
+// nothing (webgpu-bench 0.1.0 README, write-bandwidth).  Both walk the buffer
+// grid-stride, so at every step the whole grid covers one contiguous span.
+#include "q4_common.h"
+#include "q4_device.h"
+
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kUnroll = 8;                     // 16-byte loads in flight per lane
+constexpr int kDefaultFillBlocks = 4096;
+
+__global__ __launch_bounds__(kBlock) void read_reduce_kernel(const float4 *__restrict__ buf,
+                                                             size_t n4, float *__restrict__ partials) {
+    __shared__ float wsum[kBlock / 64];
+    const size_t stride = (size_t)gridDim.x * kBlock;
+    size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x;
+    float a[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) a[u] = 0.f;
+    for (; i + (kUnroll - 1) * stride < n4; i += kUnroll * stride) {
+        float4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) v[u] = buf[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) a[u] += (v[u].x + v[u].y) + (v[u].z + v[u].w);
+    }
+    for (; i < n4; i += stride) {
+        const float4 v = buf[i];
+        a[0] += (v.x + v.y) + (v.z + v.w);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) s += a[u];
+    s = q4::group_sum<64>(s);
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float t = 0.f;
+#pragma unroll
+        for (int w = 0; w < kBlock / 64; ++w) t += wsum[w];
+        partials[blockIdx.x] = t;
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void write_fill_kernel(float4 *__restrict__ buf, size_t n4,
+                                                            float value) {
+    const float4 v = make_float4(value, value, value, value);
+    const size_t stride = (size_t)gridDim.x * kBlock;
+    for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < n4; i += stride) buf[i] = v;
+}
+
+}  // namespace
+
+extern "C" int read_reduce(const float *buf, size_t n_floats, float *partials, int n_partials,
+                           void *stream) {
+    if (n_floats % 4 != 0 || n_partials < 1 || n_partials > 65536) return Q4_EINVAL;
+    if (!partials || (n_floats && !buf)) return Q4_ENULL;
+    if ((buf && !q4::aligned(buf, 16)) || !q4::aligned(partials, 4)) return Q4_EALIGN;
+    const int dev = q4::check_device();
+    if (dev != Q4_OK) return dev;
+    hipLaunchKernelGGL(read_reduce_kernel, dim3(n_partials), dim3(kBlock), 0,
+                       static_cast<hipStream_t>(stream), reinterpret_cast<const float4 *>(buf),
+                       n_floats / 4, partials);
+    return q4::launch_status();
+}
+
+extern "C" int write_fill(float *buf, size_t n_floats, float value, int n_blocks, void *stream) {
+    if (n_floats % 4 != 0 || n_blocks < 0 || n_blocks > 65536) return Q4_EINVAL;
+    if (n_floats == 0) return Q4_OK;
+    if (!buf) return Q4_ENULL;
+    if (!q4::aligned(buf, 16)) return Q4_EALIGN;
+    const int dev = q4::check_device();
+    if (dev != Q4_OK) return dev;
+    const size_t n4 = n_floats / 4;
+    size_t blocks = n_blocks ? (size_t)n_blocks : (size_t)kDefaultFillBlocks;
+    const size_t need = (n4 + kBlock - 1) / kBlock;
+    if (blocks > need) blocks = need;
+    hipLaunchKernelGGL(write_fill_kernel, dim3((unsigned)blocks), dim3(kBlock), 0,
+                       static_cast<hipStream_t>(stream), reinterpret_cast<float4 *>(buf), n4, value);
+    return q4::launch_status();
+}

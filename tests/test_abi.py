@@ -1,0 +1,128 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/q4gemv.h declares, and rejects bad arguments before touching the
+device.  Calls here either fail validation or stop at the device check; none
+launches a kernel."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4gemv.h")
+
+import memory_bandwidth_amd as q4  # noqa: E402
+import workloads  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(q4.LIB_PATH):
+        from memory_bandwidth_amd import build
+        build.build()
+    return q4.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_expected_functions():
+    assert sorted(header_functions()) == sorted(q4.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", q4.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for name in header_functions():
+        assert name in exported, name
+        assert getattr(L, name) is not None
+
+
+def test_abi_version_and_strerror(L):
+    assert q4.abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5, 7):
+        assert isinstance(q4.strerror(code), str) and q4.strerror(code)
+
+
+A16 = 0x10000          # fake, aligned, never dereferenced device addresses
+A16B = 0x20000
+
+
+@pytest.mark.parametrize("M,N,K,g,want", [
+    (0, 8, 128, 32, q4.Q4_EINVAL), (9, 8, 128, 32, q4.Q4_EINVAL),
+    (1, -1, 128, 32, q4.Q4_EINVAL), (1, 8, 0, 32, q4.Q4_EINVAL),
+    (1, 8, 96, 64, q4.Q4_EINVAL), (1, 8, 160, 128, q4.Q4_EINVAL),
+    (1, 8, 100, 32, q4.Q4_EINVAL), (1, 8, 64, 128, q4.Q4_EINVAL),
+    (1, 0, 128, 32, q4.Q4_OK),      # empty output: nothing launched
+])
+def test_gemv_q4_shape_validation(L, M, N, K, g, want):
+    assert L.gemv_q4(A16, A16, A16, A16, A16, M, N, K, g, None) == want
+
+
+def test_gemv_q4_pointer_validation(L):
+    assert L.gemv_q4(None, A16, A16, A16, A16, 1, 8, 128, 32, None) == q4.Q4_ENULL
+    assert L.gemv_q4(A16, A16, A16, None, A16, 1, 8, 128, 32, None) == q4.Q4_ENULL
+    assert L.gemv_q4(A16 + 4, A16, A16, A16, A16, 1, 8, 128, 32, None) == q4.Q4_EALIGN
+    assert L.gemv_q4(A16, A16 + 8, A16, A16, A16, 1, 8, 128, 32, None) == q4.Q4_EALIGN
+    assert L.gemv_q4(A16, A16, A16 + 1, A16, A16, 1, 8, 128, 32, None) == q4.Q4_EALIGN
+    assert L.gemv_q4(A16, A16, A16, A16, A16 + 2, 1, 8, 128, 32, None) == q4.Q4_EALIGN
+    # zeros need only byte alignment
+    st = L.gemv_q4(A16, A16, A16, A16 + 1, A16, 1, 8, 128, 32, None)
+    assert st in (q4.Q4_EDEVICE, q4.Q4_OK, q4.Q4_ELAUNCH) and st != q4.Q4_EALIGN
+
+
+def test_other_entry_points_validation(L):
+    assert L.gemv_f32(A16, A16, A16, 1, 8, 6, None) == q4.Q4_EINVAL
+    assert L.gemv_f32(A16, A16, A16, 0, 8, 8, None) == q4.Q4_EINVAL
+    assert L.gemv_f32(A16, A16, A16, 1, 0, 8, None) == q4.Q4_OK
+    assert L.gemv_f32(A16 + 4, A16, A16, 1, 8, 8, None) == q4.Q4_EALIGN
+    assert L.dequant_q4(A16, A16, A16, None, None, 4, 64, 32, None) == q4.Q4_ENULL
+    assert L.dequant_q4(A16, A16, A16, A16 + 4, None, 4, 64, 32, None) == q4.Q4_EALIGN
+    assert L.dequant_q4(A16, A16, A16, None, A16 + 4, 4, 64, 32, None) == q4.Q4_EALIGN
+    assert L.dequant_q4(A16, A16, A16, A16, None, 4, 96, 128, None) == q4.Q4_EINVAL
+    assert L.read_reduce(A16, 6, A16B, 4, None) == q4.Q4_EINVAL
+    assert L.read_reduce(A16, 8, A16B, 0, None) == q4.Q4_EINVAL
+    assert L.read_reduce(A16, 8, A16B, 65537, None) == q4.Q4_EINVAL
+    assert L.read_reduce(A16 + 4, 8, A16B, 4, None) == q4.Q4_EALIGN
+    assert L.read_reduce(A16, 8, None, 4, None) == q4.Q4_ENULL
+    assert L.write_fill(A16, 6, ctypes.c_float(1.0), 0, None) == q4.Q4_EINVAL
+    assert L.write_fill(A16 + 8, 8, ctypes.c_float(1.0), 0, None) == q4.Q4_EALIGN
+    assert L.write_fill(None, 0, ctypes.c_float(1.0), 0, None) == q4.Q4_OK
+
+
+def test_no_device_reports_edevice(L):
+    """On a host without a gfx950 GPU, a valid call stops at the device check."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert L.gemv_q4(A16, A16, A16, A16, A16, 1, 8, 128, 32, None) == q4.Q4_EDEVICE
+    assert L.read_reduce(A16, 8, A16B, 4, None) == q4.Q4_EDEVICE
+
+
+SHAPES = ([workloads.SMALL_896, workloads.LM_HEAD, workloads.STREAM_SHAPE]
+          + list(workloads.DECODER_LAYER) + [s for M in (1, 4, 8) for s in workloads.ffn_8b(M)])
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{s.label}" for s in SHAPES])
+def test_geometry_covers_every_row(shape):
+    geo = q4.gemv_q4_geometry(shape.M, shape.N, shape.K, shape.g)
+    lpr, S = geo["lanes_per_row"], geo["ksplit"]
+    assert lpr in (16, 32, 64) and S in (1, 2, 4) and geo["block"] == 256
+    waves = geo["block"] // 64
+    rows_per_wg = geo["rows_per_wave"] * waves // S
+    assert geo["grid"] * rows_per_wg >= shape.N > (geo["grid"] - 1) * rows_per_wg
+    C = shape.K // 32
+    seg = -(-C // geo["segments"])
+    # x segment fits the 64 KiB LDS budget
+    assert shape.M * seg * 128 <= 64 * 1024
+
+
+def test_geometry_rejects_bad_shapes():
+    with pytest.raises(q4.Q4Error):
+        q4.gemv_q4_geometry(1, 8, 100, 32)

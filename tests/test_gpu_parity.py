@@ -1,0 +1,314 @@
+"""GPU parity: the HIP library against the CPU oracle, through the C ABI.
+
+Bars (all per element):
+  * codes and dequantised weights: bit-exact;
+  * GEMVs on integer-exact inputs: bit-exact;
+  * GEMVs otherwise: |y - y_ref| <= 1e-4 * sum|w x| + 1e-6, y_ref in f64.
+Small and ragged shapes are compared in full; the configured full-size
+shapes are run in the launch configuration the benchmark times and compared
+on sampled rows the oracle computes one by one.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import memory_bandwidth_amd as q4
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def dev(d):
+    return {k: torch.from_numpy(np.ascontiguousarray(v)).to(DEV) for k, v in d.items()}
+
+
+def run_q4(t, g, M=None):
+    y = q4.gemv_q4(t["x"], t["wq"], t["scales"], t["zeros"], g)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def assert_within(y, y_ref, bound, label):
+    err = np.abs(y.astype(np.float64) - y_ref)
+    tol = oracle.gemv_tolerance(bound)
+    bad = err > tol
+    assert not bad.any(), (f"{label}: {int(bad.sum())}/{bad.size} outputs out of tolerance, "
+                           f"worst err/tol {np.max(err / tol):.3g}")
+
+
+def sample_rows(N, n, seed):
+    rng = np.random.default_rng(seed)
+    edge = np.r_[0:min(N, 40), max(0, N - 40):N]
+    mid = rng.choice(N, size=min(N, n), replace=False)
+    return np.unique(np.r_[edge, mid]).astype(np.int64)
+
+
+# ---------------------------------------------------------------- configs
+
+def test_config0_single_896():
+    s = wl.SMALL_896
+    d = wl.make_q4_problem(wl.config_seed(0), s)
+    y = run_q4(dev(d), s.g)
+    y_ref, b = oracle.gemv_q4(d["x"], d["wq"], d["scales"], d["zeros"], s.g)
+    assert_within(y, y_ref, b, s.label)
+
+
+def test_config1_decoder_layer():
+    for i, s in enumerate(wl.DECODER_LAYER):
+        d = wl.make_q4_problem(wl.config_seed(1), s, index=i)
+        t = dev(d)
+        y = run_q4(t, s.g)
+        y_ref, b = oracle.gemv_q4(d["x"], d["wq"], d["scales"], d["zeros"], s.g)
+        assert_within(y, y_ref, b, s.label)
+        # the same shape as the dense fp32 control, on the exact dequantised weights
+        w, _ = oracle.dequant(d["wq"], d["scales"], d["zeros"], s.K, s.g)
+        yf = q4.gemv_f32(t["x"], torch.from_numpy(w).to(DEV))
+        torch.cuda.synchronize()
+        yf_ref, bf = oracle.gemv_f32(d["x"], w)
+        assert_within(yf.cpu().numpy(), yf_ref, bf, "f32 " + s.label)
+
+
+def test_config2_lm_head_sampled():
+    s = wl.LM_HEAD
+    d = wl.make_q4_problem(wl.config_seed(2), s)
+    y = run_q4(dev(d), s.g)
+    rows = sample_rows(s.N, 3000, 2)
+    y_ref, b = oracle.gemv_q4(d["x"], d["wq"], d["scales"], d["zeros"], s.g, rows=rows)
+    assert_within(y[:, rows], y_ref, b, s.label)
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_config3_ffn_sampled(M):
+    for i, s in enumerate(wl.ffn_8b(M)):
+        d = wl.make_q4_problem(wl.config_seed(3), s, index=i)
+        y = run_q4(dev(d), s.g)
+        rows = sample_rows(s.N, 200, 3 + M)
+        y_ref, b = oracle.gemv_q4(d["x"], d["wq"], d["scales"], d["zeros"], s.g, rows=rows)
+        assert_within(y[:, rows], y_ref, b, s.label)
+
+
+def test_config4_stream_sampled():
+    s = wl.STREAM_SHAPE
+    seed = wl.config_seed(4)
+    x = wl.make_x(seed, 1, s.K)
+    xt = torch.from_numpy(x).to(DEV)
+    for idx in (0, 13, 31):
+        d = wl.make_q4_weights(seed, s.N, s.K, s.g, s.s_lo, s.s_hi, index=idx)
+        t = dev(d)
+        y = q4.gemv_q4(xt, t["wq"], t["scales"], t["zeros"], s.g)
+        torch.cuda.synchronize()
+        rows = sample_rows(s.N, 300, idx)
+        y_ref, b = oracle.gemv_q4(x, d["wq"], d["scales"], d["zeros"], s.g, rows=rows)
+        assert_within(y.cpu().numpy()[:, rows], y_ref, b, f"{s.label} matrix {idx}")
+    # dense control on the same shape, weights dequantised by the oracle
+    w, _ = oracle.dequant(d["wq"], d["scales"], d["zeros"], s.K, s.g)
+    yf = q4.gemv_f32(xt, torch.from_numpy(w).to(DEV))
+    torch.cuda.synchronize()
+    yf_ref, bf = oracle.gemv_f32(x, w, rows=rows)
+    assert_within(yf.cpu().numpy()[:, rows], yf_ref, bf, "f32 control " + s.label)
+
+
+# ---------------------------------------------------------------- ragged / edge shapes
+
+RAGGED = [
+    # M, N, K, g
+    (1, 1, 32, 32), (1, 3, 64, 32), (2, 5, 96, 32), (1, 7, 128, 128), (3, 17, 256, 128),
+    (1, 31, 512, 32), (4, 33, 544, 32), (1, 63, 1024, 32), (5, 64, 1056, 32), (1, 65, 2048, 128),
+    (8, 67, 2080, 32), (1, 127, 4096, 128), (6, 129, 4224, 128), (1, 1000, 896, 32),
+    (7, 257, 4864, 32), (8, 67, 14336, 128), (1, 45, 14336, 128), (2, 300, 8192, 128),
+    (1, 1, 16384, 128), (8, 9, 18432, 128), (1, 4097, 384, 128), (8, 1, 32, 32),
+]
+
+
+@pytest.mark.parametrize("M,N,K,g", RAGGED, ids=[f"M{a}N{b}K{c}g{d}" for a, b, c, d in RAGGED])
+def test_gemv_q4_ragged(M, N, K, g):
+    s = wl.Q4Shape(M, N, K, g, 0.002, 0.02)
+    d = wl.make_q4_problem(1000 + N, s)
+    y = run_q4(dev(d), g)
+    y_ref, b = oracle.gemv_q4(d["x"], d["wq"], d["scales"], d["zeros"], g)
+    assert_within(y, y_ref, b, f"M{M} N{N} K{K} g{g}")
+
+
+EXACT = [(1, 14336, 4096, 128), (1, 4096, 14336, 128), (8, 333, 14336, 128), (4, 515, 4096, 128),
+         (1, 896, 896, 32), (3, 2000, 4864, 32), (8, 77, 640, 32), (2, 1024, 32768, 128)]
+
+
+@pytest.mark.parametrize("M,N,K,g", EXACT, ids=[f"M{a}N{b}K{c}g{d}" for a, b, c, d in EXACT])
+def test_gemv_q4_integer_exact(M, N, K, g):
+    d = wl.make_exact_problem(77 + M, M, N, K, g)
+    y = run_q4(dev(d), g)
+    y_ref, _ = oracle.gemv_q4(d["x"], d["wq"], d["scales"], d["zeros"], g)
+    assert np.array_equal(y.astype(np.float64), y_ref), np.max(np.abs(y - y_ref))
+
+
+def test_gemv_q4_q_equals_z_is_exactly_zero():
+    M, N, K, g = 4, 300, 4096, 128
+    d = wl.make_q4_problem(5, wl.Q4Shape(M, N, K, g, 0.002, 0.01))
+    z = np.stack([d["zeros"] & 15, d["zeros"] >> 4], -1).reshape(N, -1)[:, :K // g]
+    codes = np.repeat(z, g, axis=1).astype(np.uint8)
+    d["wq"] = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    y = run_q4(dev(d), g)
+    assert np.all(y == 0.0)
+
+
+def test_gemv_q4_linearity_and_rows():
+    """Doubling x doubles y exactly; row m of an M=8 call matches M=1 on x[m]."""
+    s = wl.Q4Shape(8, 1234, 4096, 128, 0.002, 0.01)
+    d = wl.make_q4_problem(9, s)
+    t = dev(d)
+    y = run_q4(t, s.g)
+    t2 = dict(t, x=t["x"] * 2)
+    y2 = run_q4(t2, s.g)
+    assert np.array_equal(y2, 2 * y)
+    y_ref, b = oracle.gemv_q4(d["x"], d["wq"], d["scales"], d["zeros"], s.g)
+    for m in (0, 5, 7):
+        t1 = dict(t, x=t["x"][m:m + 1].contiguous())
+        assert_within(run_q4(t1, s.g), y_ref[m:m + 1], b[m:m + 1], f"row {m} as M=1")
+
+
+def test_gemv_q4_deterministic_and_guarded():
+    s = wl.Q4Shape(2, 1001, 4096, 128, 0.002, 0.01)
+    d = wl.make_q4_problem(10, s)
+    t = dev(d)
+    buf = torch.full((s.M * s.N + 4096,), float("nan"), device=DEV)
+    out = buf[: s.M * s.N].view(s.M, s.N)
+    q4.gemv_q4(t["x"], t["wq"], t["scales"], t["zeros"], s.g, out=out)
+    a = out.clone()
+    q4.gemv_q4(t["x"], t["wq"], t["scales"], t["zeros"], s.g, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(a, out)
+    assert torch.isnan(buf[s.M * s.N:]).all(), "write past the end of y"
+
+
+def test_gemv_q4_empty_n():
+    x = torch.zeros((1, 128), device=DEV)
+    wq = torch.zeros((0, 64), dtype=torch.uint8, device=DEV)
+    sc = torch.zeros((0, 4), dtype=torch.float16, device=DEV)
+    zp = torch.zeros((0, 2), dtype=torch.uint8, device=DEV)
+    y = q4.gemv_q4(x, wq, sc, zp, 32)
+    assert y.shape == (1, 0)
+
+
+def test_gemv_q4_graph_replay():
+    s = wl.STREAM_SHAPE
+    d = wl.make_q4_problem(11, s)
+    t = dev(d)
+    eager = q4.gemv_q4(t["x"], t["wq"], t["scales"], t["zeros"], s.g)
+    torch.cuda.synchronize()
+    out = torch.empty_like(eager)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g):
+            q4.gemv_q4(t["x"], t["wq"], t["scales"], t["zeros"], s.g, out=out)
+    for i in range(4):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+
+
+# ---------------------------------------------------------------- dequant_q4
+
+DQ = [(1, 32, 32), (3, 96, 32), (17, 256, 128), (64, 896, 32), (1000, 4096, 128), (7, 4864, 32)]
+
+
+@pytest.mark.parametrize("N,K,g", DQ, ids=[f"N{a}K{b}g{c}" for a, b, c in DQ])
+def test_dequant_bit_exact(N, K, g):
+    d = wl.make_q4_weights(20 + N, N, K, g, 0.002, 0.02)
+    t = dev(d)
+    w, c = q4.dequant_q4(t["wq"], t["scales"], t["zeros"], g)
+    torch.cuda.synchronize()
+    w_ref, c_ref = oracle.dequant(d["wq"], d["scales"], d["zeros"], K, g)
+    assert np.array_equal(c.cpu().numpy(), c_ref)
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), w_ref.view(np.uint32))
+
+
+def test_dequant_special_scales():
+    """Subnormal, negative, huge and zero binary16 scales; NaN/Inf where the math gives them."""
+    N, K, g = 64, 256, 32
+    d = wl.make_q4_weights(30, N, K, g, 0.01, 0.02)
+    rng = np.random.default_rng(30)
+    specials = np.array([0x0001, 0x03FF, 0x0400, 0x8001, 0xBC00, 0x7BFF, 0xFBFF, 0x0000,
+                         0x8000, 0x7C00, 0xFC00, 0x7E00], np.uint16)
+    d["scales"] = rng.choice(specials, size=d["scales"].shape).astype(np.uint16)
+    t = dev(d)
+    w, c = q4.dequant_q4(t["wq"], t["scales"], t["zeros"], g)
+    torch.cuda.synchronize()
+    w_ref, c_ref = oracle.dequant(d["wq"], d["scales"], d["zeros"], K, g)
+    w = w.cpu().numpy()
+    nan = np.isnan(w_ref)
+    assert np.array_equal(np.isnan(w), nan)
+    assert np.array_equal(w[~nan].view(np.uint32), w_ref[~nan].view(np.uint32))
+    assert np.array_equal(c.cpu().numpy(), c_ref)
+
+
+def test_dequant_codes_only_and_weights_only():
+    N, K, g = 50, 512, 128
+    d = wl.make_q4_weights(31, N, K, g, 0.002, 0.01)
+    t = dev(d)
+    w, c = q4.dequant_q4(t["wq"], t["scales"], t["zeros"], g, want_weights=False)
+    assert w is None
+    w2, c2 = q4.dequant_q4(t["wq"], t["scales"], t["zeros"], g, want_codes=False)
+    torch.cuda.synchronize()
+    w_ref, c_ref = oracle.dequant(d["wq"], d["scales"], d["zeros"], K, g)
+    assert c2 is None and np.array_equal(c.cpu().numpy(), c_ref)
+    assert np.array_equal(w2.cpu().numpy().view(np.uint32), w_ref.view(np.uint32))
+
+
+# ---------------------------------------------------------------- gemv_f32
+
+F32 = [(1, 1, 4), (1, 33, 60), (2, 65, 128), (1, 1000, 896), (8, 129, 4096), (3, 77, 16400),
+       (1, 4097, 4096), (5, 31, 20000)]
+
+
+@pytest.mark.parametrize("M,N,K", F32, ids=[f"M{a}N{b}K{c}" for a, b, c in F32])
+def test_gemv_f32(M, N, K):
+    rng = np.random.default_rng(M * 1000 + N)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    w = (rng.standard_normal((N, K)) * 0.05).astype(np.float32)
+    y = q4.gemv_f32(torch.from_numpy(x).to(DEV), torch.from_numpy(w).to(DEV))
+    torch.cuda.synchronize()
+    y_ref, b = oracle.gemv_f32(x, w)
+    assert_within(y.cpu().numpy(), y_ref, b, f"f32 M{M} N{N} K{K}")
+
+
+def test_gemv_f32_integer_exact():
+    rng = np.random.default_rng(3)
+    x = rng.integers(-3, 4, size=(2, 4096)).astype(np.float32)
+    w = rng.integers(-64, 65, size=(515, 4096)).astype(np.float32)
+    y = q4.gemv_f32(torch.from_numpy(x).to(DEV), torch.from_numpy(w).to(DEV))
+    torch.cuda.synchronize()
+    y_ref, _ = oracle.gemv_f32(x, w)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), y_ref)
+
+
+# ---------------------------------------------------------------- probes
+
+@pytest.mark.parametrize("n,parts", [(0, 3), (4, 1), (1 << 20, 7), ((1 << 24) + 36, 2048)])
+def test_read_reduce_ones(n, parts):
+    buf = torch.ones(n, device=DEV)
+    p = q4.read_reduce(buf, parts)
+    torch.cuda.synchronize()
+    assert float(p.double().sum()) == float(n)
+
+
+def test_read_reduce_random():
+    host = wl.make_probe_buffer(3 * (1 << 22) + 12) - np.float32(0.5)
+    p = q4.read_reduce(torch.from_numpy(host).to(DEV), 1024)
+    torch.cuda.synchronize()
+    s, a = oracle.buffer_sum(host)
+    assert abs(float(p.double().sum()) - s) <= 1e-5 * a + 1e-6
+
+
+@pytest.mark.parametrize("n,blocks", [(4, 0), (4096, 3), ((1 << 22) + 8, 0), ((1 << 22) + 8, 65536)])
+def test_write_fill(n, blocks):
+    buf = torch.full((n + 64,), float("nan"), device=DEV)
+    q4.write_fill(buf[:n], -1.5, blocks)
+    torch.cuda.synchronize()
+    assert bool((buf[:n] == -1.5).all())
+    assert bool(torch.isnan(buf[n:]).all())
