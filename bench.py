@@ -1,0 +1,439 @@
+#!/usr/bin/env python3
+"""Benchmark of the int4 decode GEMV on one MI355X.
+
+Default run (the headline metric): the cache-defeating stream, 32 distinct
+int4 group-128 matrices K=4096 x N=14336 (976,224,256 B of codes, scales and
+zero points, more than L2 + Infinity Cache) cycled at M=1.  One step is one
+pass over the 32 matrices (32 gemv_q4 calls, replayed from one HIP graph).
+W warm-up steps, then exactly K timed steps between two device syncs, timed
+with HIP events on the stream the graph runs on.  Prints ONE JSON line.
+
+Alongside, in the same process and in ABBA order (forward, then reversed), the
+measurement method of cera 0.5.0 wgpu_gemv_bench.rs is applied to three
+kernels: gemv_q4 (the metric), gemv_f32 on the same shape (the control,
+4 distinct 235 MB matrices cycled) and read_reduce over 2 GiB (the measured
+HBM read peak).  Each cell is a two-point difference, per_iter =
+(t(2n) - t(n)) / n, which cancels every fixed per-measurement cost; a cell is
+"noise" unless t(2n) >= 1.2 t(n); n is swept; the first round is discarded;
+medians of >= 3 runs are reported with min and p10-p90.
+
+Other modes:
+  --full            every workload (all five configurations), JSONL table
+  --pmc-workload    a short fixed sequence of dispatches for rocprofv3 --pmc
+  --summarize DIR   turn rocprofv3 CSV output in DIR into a profiles/ summary
+The CPU oracle is timed on a bounded sample of the same workload
+(cpu_baseline); it is the only use of oracle/ here.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+METRIC = "int4 GEMV achieved GB/s (% of HBM peak), M=1 K=4096 N=14336 streamed"
+SPEC_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published peak
+PROFILES = os.path.join(ROOT, "profiles")
+PMC_SUMMARY = os.path.join(PROFILES, "gemv_q4_stream_4096x14336_g128_pmc.json")
+KERNEL_SOURCE = os.path.join(ROOT, "memory_bandwidth_amd", "csrc", "gemv_q4.hip")
+NOISE_RATIO = 1.2
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- timing method (pure)
+
+def two_point(t_n: float, t_2n: float, n: int) -> float:
+    """Per-iteration time from timings of n and 2n iterations; fixed costs cancel."""
+    return (t_2n - t_n) / n
+
+
+def resolvable(t_n: float, t_2n: float, ratio: float = NOISE_RATIO) -> bool:
+    """Doubling the work must lengthen the run by at least `ratio`, else the cell is noise."""
+    return t_2n >= ratio * t_n and t_2n > t_n
+
+
+def summarize(values: list[float]) -> dict:
+    v = sorted(values)
+    if not v:
+        return {"median": None, "min": None, "p10": None, "p90": None, "n": 0}
+
+    def pct(p):
+        k = (len(v) - 1) * p
+        lo, hi = int(k), min(int(k) + 1, len(v) - 1)
+        return v[lo] + (v[hi] - v[lo]) * (k - lo)
+    return {"median": statistics.median(v), "min": v[0], "p10": pct(0.1), "p90": pct(0.9),
+            "n": len(v)}
+
+
+def abba_orders(kernels: list[str], runs: int) -> list[list[str]]:
+    """Run r uses the forward order when r is even and the reversed order when odd."""
+    return [list(kernels) if r % 2 == 0 else list(reversed(kernels)) for r in range(runs)]
+
+
+def sweep(timer, kernels: list[str], iters: list[int], runs: int) -> dict:
+    """Two-point timing of every kernel at every n, ABBA-ordered, first round discarded.
+
+    timer(kernel, n) -> seconds for n iterations.  Returns, per kernel, the
+    per-iteration samples that were resolvable and the count of noise cells.
+    """
+    out = {k: {"samples": [], "noise": 0, "cells": []} for k in kernels}
+    for r, order in enumerate(abba_orders(kernels, runs + 1)):
+        for k in order:
+            for n in iters:
+                t_n = timer(k, n)
+                t_2n = timer(k, 2 * n)
+                if r == 0:
+                    continue                      # the first round only warms up
+                ok = resolvable(t_n, t_2n)
+                per = two_point(t_n, t_2n, n)
+                out[k]["cells"].append({"run": r, "n": n, "t_n": t_n, "t_2n": t_2n,
+                                        "per_iter": per if ok else None})
+                if ok and per > 0:
+                    out[k]["samples"].append(per)
+                else:
+                    out[k]["noise"] += 1
+    return out
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(launch_bytes: int):
+    """HBM bytes per gemv_q4 launch from the committed --pmc summary, or None
+    when there is none or the kernel source changed since it was taken."""
+    try:
+        s = json.load(open(PMC_SUMMARY))
+    except (OSError, ValueError):
+        return None
+    if s.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return s.get("gemv_q4_hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------- GPU side
+
+class Graph:
+    """A captured batch of launches replayed on the current stream."""
+
+    def __init__(self, fn, torch):
+        self.torch = torch
+        fn()                                   # eager run: first touch, device check
+        torch.cuda.synchronize()
+        self.g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.g):
+            fn()
+        torch.cuda.synchronize()
+
+    def time(self, reps: int) -> float:
+        """Seconds for `reps` back-to-back replays, by HIP events on the replay stream."""
+        torch = self.torch
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            self.g.replay()
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b) / 1e3
+
+
+def setup_stream(torch, q4, dev):
+    s = wl.STREAM_SHAPE
+    seed = wl.config_seed(4)
+    x = torch.from_numpy(wl.make_x(seed, 1, s.K)).to(dev)
+    mats = []
+    t0 = time.time()
+    for i in range(wl.STREAM_MATRICES):
+        d = wl.make_q4_weights(seed, s.N, s.K, s.g, s.s_lo, s.s_hi, index=i)
+        mats.append({k: torch.from_numpy(v).to(dev) for k, v in d.items()})
+    ys = [torch.empty((1, s.N), dtype=torch.float32, device=dev) for _ in mats]
+    # dense control: four of the matrices, dequantised on the device
+    wf = [q4.dequant_q4(m["wq"], m["scales"], m["zeros"], s.g, want_codes=False)[0]
+          for m in mats[:wl.STREAM_F32_MATRICES]]
+    yf = [torch.empty((1, s.N), dtype=torch.float32, device=dev) for _ in wf]
+    n_probe = wl.PROBE_BYTES // 4
+    probe = torch.empty(n_probe, dtype=torch.float32, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    probe.uniform_(0.0, 1.0, generator=gen)
+    partials = torch.empty(4096, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log(f"inputs resident in HBM ({time.time() - t0:.1f} s)")
+    return {"shape": s, "x": x, "mats": mats, "ys": ys, "wf": wf, "yf": yf, "probe": probe,
+            "partials": partials}
+
+
+def gate(torch, q4, W):
+    """Refuse to time a wrong kernel: gemv_q4 must agree with gemv_f32 on the
+    device-dequantised weights within the GEMV tolerance (bound from |x|.|W|^T)."""
+    s = W["shape"]
+    for i in range(wl.STREAM_F32_MATRICES):
+        m = W["mats"][i]
+        y4 = q4.gemv_q4(W["x"], m["wq"], m["scales"], m["zeros"], s.g)
+        yf = q4.gemv_f32(W["x"], W["wf"][i])
+        bound = q4.gemv_f32(W["x"].abs(), W["wf"][i].abs())
+        err = (y4.double() - yf.double()).abs()
+        tol = 2 * (1e-4 * bound.double() + 1e-6)
+        if not bool((err <= tol).all()):
+            raise SystemExit(f"parity gate failed on matrix {i}: worst err/tol "
+                             f"{float((err / tol).max()):.3g}")
+    torch.cuda.synchronize()
+
+
+def cpu_baseline(budget_s: float = 12.0) -> dict:
+    """The oracle, as it stands, on a bounded sample of the stream workload."""
+    import oracle
+    s = wl.STREAM_SHAPE
+    seed = wl.config_seed(4)
+    x = wl.make_x(seed, 1, s.K)
+    nbytes, done, t_used = 0, 0, 0.0
+    while done < wl.STREAM_MATRICES and (t_used < budget_s or done == 0):
+        d = wl.make_q4_weights(seed, s.N, s.K, s.g, s.s_lo, s.s_hi, index=done)
+        t0 = time.perf_counter()
+        oracle.gemv_q4(x, d["wq"], d["scales"], d["zeros"], s.g)
+        t_used += time.perf_counter() - t0
+        nbytes += wl.q4_weight_bytes(s.N, s.K, s.g)
+        done += 1
+    return {"value": round(nbytes / t_used / 1e9, 5), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{done} of the 32 stream matrices, full 14336x4096 GEMV each, "
+                      f"single-threaded f64 C oracle, {t_used:.1f} s",
+            "host_cpu": host_cpu(), "host_nproc": os.cpu_count()}
+
+
+def host_cpu() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def run_default(args):
+    import torch
+    import memory_bandwidth_amd as q4
+
+    dev = torch.device("cuda:0")
+    W = setup_stream(torch, q4, dev)
+    s = W["shape"]
+    g = s.g
+    gate(torch, q4, W)
+    log("parity gate passed")
+
+    def q4_pass():
+        for m, y in zip(W["mats"], W["ys"]):
+            q4.gemv_q4(W["x"], m["wq"], m["scales"], m["zeros"], g, out=y)
+
+    def f32_pass():
+        for w, y in zip(W["wf"], W["yf"]):
+            q4.gemv_f32(W["x"], w, out=y)
+
+    def probe_pass():
+        q4.read_reduce(W["probe"], 4096, partials=W["partials"])
+
+    graphs = {"gemv_q4": Graph(q4_pass, torch), "gemv_f32": Graph(f32_pass, torch),
+              "read_reduce": Graph(probe_pass, torch)}
+    calls = {"gemv_q4": wl.STREAM_MATRICES, "gemv_f32": wl.STREAM_F32_MATRICES, "read_reduce": 1}
+    bytes_per_call = {"gemv_q4": wl.q4_weight_bytes(s.N, s.K, s.g),
+                      "gemv_f32": wl.f32_weight_bytes(s.N, s.K),
+                      "read_reduce": wl.PROBE_BYTES}
+
+    # ---- the contract's timed region: W warm-up steps, then exactly K steps
+    G = graphs["gemv_q4"]
+    for _ in range(args.warmup):
+        G.g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        G.g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    elapsed = start.elapsed_time(end) / 1e3
+    launches = args.steps * wl.STREAM_MATRICES
+    per_launch = elapsed / launches
+    value = bytes_per_call["gemv_q4"] / per_launch / 1e9
+    log(f"timed region: {args.steps} steps, {launches} launches, {elapsed * 1e3:.3f} ms events, "
+        f"{wall * 1e3:.3f} ms wall; {per_launch * 1e6:.3f} us/launch -> {value:.1f} GB/s")
+
+    # ---- two-point / ITERS sweep / ABBA, in the same process
+    result = {}
+    if not args.quick:
+        iters = [int(v) for v in args.iters.split(",")]
+        # n counts gemv launches; one 2 GiB read_reduce streams as much as ~70
+        # of them, so its sweep uses n / 16 launches.
+        scale = {"gemv_q4": 1, "gemv_f32": 1, "read_reduce": 16}
+
+        def timer(k, n):
+            launches = max(1, n // scale[k])
+            reps = max(1, launches // calls[k])
+            return graphs[k].time(reps) / (reps * calls[k]) * n
+
+        res = sweep(timer, list(graphs), iters, args.runs)
+        for k, r in res.items():
+            st = summarize(r["samples"])
+            gbs = {q: (bytes_per_call[k] / v / 1e9 if v else None) for q, v in st.items() if q != "n"}
+            result[k] = {"per_launch_us": {q: (v * 1e6 if isinstance(v, float) else v)
+                                           for q, v in st.items()},
+                         "GBps_median": gbs["median"], "GBps_best": gbs["min"],
+                         "noise_cells": r["noise"], "resolvable_cells": st["n"]}
+            log(f"{k:12s} median {gbs['median'] and round(gbs['median'], 1)} GB/s "
+                f"(per launch {st['median'] and st['median'] * 1e6:.3f} us; p10-p90 "
+                f"{st['p10'] and st['p10'] * 1e6:.3f}-{st['p90'] and st['p90'] * 1e6:.3f}); "
+                f"noise cells {r['noise']}")
+    measured_peak = result.get("read_reduce", {}).get("GBps_median")
+
+    traffic = traffic_from_profile(bytes_per_call["gemv_q4"])
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "stream: 32 distinct int4 g128 matrices, K=4096 N=14336, "
+                               "cycled at M=1 (976,224,256 B > L2 + MALL)",
+                   "M": 1, "K": 4096, "N": 14336, "group_size": 128,
+                   "matrices": wl.STREAM_MATRICES, "bytes_per_call": bytes_per_call["gemv_q4"],
+                   "launches_per_step": wl.STREAM_MATRICES,
+                   "weights": "int4 codes, fp16 scale + int4 zero per 128, fp32 x/y/accumulate"},
+        "roofline": {"bound": "hbm", "achieved": round(value, 2), "peak": SPEC_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(value / SPEC_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "pct_of_spec_peak": round(100 * value / SPEC_PEAK_GBS, 2),
+        "measured_peak_GBps": measured_peak and round(measured_peak, 1),
+        "pct_of_measured_peak": measured_peak and round(100 * value / measured_peak, 2),
+        "two_point": result or None,
+        "cache_class": "hbm-streaming",
+    }
+    if not args.no_cpu:
+        log("timing the CPU oracle on a bounded sample ...")
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+# ---------------------------------------------------------------- --pmc-workload
+
+def run_pmc_workload(args):
+    """A short, fixed dispatch sequence for counter collection: 64 gemv_q4 launches
+    over the 32 stream matrices, 2 read_reduce and 2 write_fill over 2 GiB (the
+    calibration kernels of known size), 4 gemv_f32 launches."""
+    import torch
+    import memory_bandwidth_amd as q4
+    dev = torch.device("cuda:0")
+    W = setup_stream(torch, q4, dev)
+    s = W["shape"]
+    for _ in range(2):
+        q4.read_reduce(W["probe"], 4096, partials=W["partials"])
+        q4.write_fill(W["probe"], 1.0)
+    for _ in range(2):
+        for m, y in zip(W["mats"], W["ys"]):
+            q4.gemv_q4(W["x"], m["wq"], m["scales"], m["zeros"], s.g, out=y)
+    for w, y in zip(W["wf"], W["yf"]):
+        q4.gemv_f32(W["x"], w, out=y)
+    torch.cuda.synchronize()
+    log("pmc workload done")
+
+
+# ---------------------------------------------------------------- --summarize
+
+def _rows(pattern):
+    out = []
+    for f in glob.glob(pattern, recursive=True):
+        with open(f, newline="") as fh:
+            out.extend(csv.DictReader(fh))
+    return out
+
+
+def summarize_profile(args):
+    """Reads rocprofv3 CSV output under DIR and writes the summaries under profiles/."""
+    d = args.summarize
+    os.makedirs(PROFILES, exist_ok=True)
+    stats = _rows(os.path.join(d, "**", "*kernel_stats.csv"))
+    if stats:
+        lines = [f"# rocprofv3 kernel stats\n", f"command: {args.command}\n", "",
+                 "| kernel | calls | avg ns | min ns | max ns | total % |",
+                 "|---|---|---|---|---|---|"]
+        for r in sorted(stats, key=lambda r: -float(r.get("Percentage", 0) or 0)):
+            name = r["Name"].split("(")[0][:90]
+            lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                         f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} | "
+                         f"{float(r['Percentage']):.1f} |")
+        out = os.path.join(PROFILES, args.name + ".md")
+        open(out, "w").write("\n".join(lines) + "\n")
+        log("wrote", out)
+    pmc = _rows(os.path.join(d, "**", "*counter_collection.csv"))
+    if pmc:
+        acc = {}
+        for r in pmc:
+            k = (r["Kernel_Name"].split("(")[0], r["Counter_Name"])
+            acc.setdefault(k, []).append(float(r["Counter_Value"]))
+        lines = [f"# rocprofv3 counters\n", f"command: {args.command}\n", "",
+                 "| kernel | counter | dispatches | mean per dispatch |", "|---|---|---|---|"]
+        for (kern, ctr), v in sorted(acc.items()):
+            lines.append(f"| {kern[:90]} | {ctr} | {len(v)} | {statistics.mean(v):.1f} |")
+        out = os.path.join(PROFILES, args.name + ".md")
+        open(out, "w").write("\n".join(lines) + "\n")
+        log("wrote", out)
+
+
+# ---------------------------------------------------------------- main
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--iters", default="64,256,1024", help="ITERS sweep, in launches")
+    ap.add_argument("--runs", type=int, default=3, help="kept runs per cell (>= 3)")
+    ap.add_argument("--quick", action="store_true", help="skip the two-point sweep")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--pmc-workload", action="store_true")
+    ap.add_argument("--summarize", metavar="DIR")
+    ap.add_argument("--name", default="summary")
+    ap.add_argument("--command", default="")
+    args = ap.parse_args(argv)
+    if args.summarize:
+        return summarize_profile(args)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the int4 GEMV shards by output rows, see DESIGN.md)", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0 or args.runs < 1:
+        print("--steps must be >= 1, --warmup >= 0, --runs >= 1", file=sys.stderr)
+        return 2
+    if args.pmc_workload:
+        return run_pmc_workload(args)
+    return run_default(args)
+
+
+if __name__ == "__main__":
+    sys.exit(main() or 0)

@@ -41,7 +41,6 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 4;                     // wavefronts per workgroup
 constexpr int kBlock = kWaves * q4::kWave;
 constexpr int kLdsBytes = 64 * 1024;          // dynamic LDS budget per workgroup
-constexpr int kXBatch = 8;                    // x float4 per thread fetched ahead of the weights
 
 // Row slots per wavefront as a function of M: keeps the per-lane register
 // footprint (codes in flight + x slice + accumulators) near 128 VGPRs.
@@ -81,16 +80,24 @@ __device__ __forceinline__ void dot_word(uint32_t wd, half2_t z1, half2_t z16, u
     }
 }
 
+// x staging batch: float4 per thread per activation row fetched ahead of the
+// weight loads (all of x for M = 1 and K <= 8192).
+constexpr int x_batch(int M) { return M >= 8 ? 1 : 8 / M; }
+
 // M: activation rows.  LPR: lanes per output row.  JP: chunk positions per
-// lane per segment (a lane's chunks are LPR apart).
-template <int M, int LPR, int JP>
+// lane per segment (a lane's chunks are LPR apart).  R: row slots per wave.
+//
+// Addressing: every pointer the wavefront uses is a wave-uniform base (kept in
+// SGPRs) plus a 32-bit per-lane byte offset, so each load is a single
+// global_load with saddr and no 64-bit address arithmetic in VALU.
+template <int M, int LPR, int JP, int R>
 __global__ __launch_bounds__(kBlock) void gemv_q4_kernel(
-    const float *__restrict__ x, const uint4 *__restrict__ wq,
+    const float *__restrict__ x, const uint8_t *__restrict__ wq,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
     float *__restrict__ y, int N, int K, int gshift, int S, int seg_chunks) {
-    constexpr int R = row_slots(M);
     constexpr int RG = q4::kWave / LPR;   // rows sharing one load instruction
     constexpr int RPW = R * RG;           // output rows per wavefront
+    constexpr int XB = x_batch(M);
     extern __shared__ float lds[];
     float *xs = lds;                                        // [M][segC][32] swizzled
     float *comb = lds + M * seg_chunks * 32;                // [waves][RPW][M]
@@ -98,14 +105,25 @@ __global__ __launch_bounds__(kBlock) void gemv_q4_kernel(
     const int C = K >> 5;              // chunks per row
     const int G = K >> (gshift + 5);   // groups per row
     const int ZB = (G + 1) >> 1;       // zero-point bytes per row
+    const int RB = K >> 1;             // code bytes per row
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int rb = wave / S;           // row block of this wavefront within the workgroup
     const int ks = wave - rb * S;      // K-split index
-    const int row0 = (blockIdx.x * (kWaves / S) + rb) * RPW + lane / LPR;
+    const int row_first = (blockIdx.x * (kWaves / S) + rb) * RPW;   // may be >= N
+    const int row_base = min(row_first, N - 1);
+    const int rgl = lane / LPR;
     const int li = lane % LPR;
     const uint32_t magic = 0x64006400u;
+
+    // Wave-uniform bases and per-lane row offsets (rows past N re-read row N-1).
+    const uint8_t *wq_b = wq + (size_t)row_base * RB;
+    const uint16_t *sc_b = scales + (size_t)row_base * G;
+    const uint8_t *zp_b = zeros + (size_t)row_base * ZB;
+    uint32_t rrel[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) rrel[r] = (uint32_t)(min(row_first + r * RG + rgl, N - 1) - row_base);
 
     float acc[R][M];
 #pragma unroll
@@ -118,63 +136,58 @@ __global__ __launch_bounds__(kBlock) void gemv_q4_kernel(
         const int part = (segC + S - 1) / S;
         const int lo = seg0 + ks * part;
         const int hi = min(seg0 + segC, lo + part);
-
-        // x segment, first batch: global -> registers before the weight
-        // loads, so that its latency overlaps theirs and waiting for it does
-        // not wait for the weights (vmcnt retires loads in issue order).
         const int nx4 = segC * 8;                       // float4 per x row in this segment
-        const int total4 = M * nx4;
         const float *xseg = x + seg0 * 32;
-        float4 xr[kXBatch];
-#pragma unroll
-        for (int t = 0; t < kXBatch; ++t) {
-            const int i = tid + t * kBlock;
-            if (i < total4) {
-                const int m = i / nx4, r4 = i - m * nx4;
-                xr[t] = *reinterpret_cast<const float4 *>(xseg + (size_t)m * K + r4 * 4);
-            }
-        }
 
-        // Weight stream for this segment: every load of the lane is issued
-        // before any arithmetic so that all of them are in flight together.
+        // x segment, first batch: global -> registers ahead of the weight
+        // loads, so that waiting for x does not wait for the weights (vmcnt
+        // retires loads in issue order).
+        float4 xr[M][XB];
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int t = 0; t < XB; ++t) {
+                const int i = tid + t * kBlock;
+                xr[m][t] = i < nx4 ? reinterpret_cast<const float4 *>(xseg + (size_t)m * K)[i]
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+
+        // Weight stream: every load of the lane is issued before any
+        // arithmetic.  Positions past this wave's range re-read its last
+        // chunk (always in bounds) and are skipped below.
         uint4 w[JP][R];
         uint32_t sr[JP][R];
         uint32_t zr[JP][R];
+        const int clast = max(lo, hi - 1) < seg0 + segC ? max(lo, hi - 1) : seg0 + segC - 1;
 #pragma unroll
         for (int j = 0; j < JP; ++j) {
-            const int c = lo + li + j * LPR;
-            const bool ok = c < hi;
+            const int c = min(lo + li + j * LPR, clast);
+            const int gi = c >> gshift;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const int row = min(row0 + r * RG, N - 1);
-                const int gi = c >> gshift;
-                if (ok) {
-                    w[j][r] = wq[(size_t)row * C + c];
-                    sr[j][r] = scales[(size_t)row * G + gi];
-                    zr[j][r] = zeros[(size_t)row * ZB + (gi >> 1)];
-                } else {
-                    w[j][r] = make_uint4(0, 0, 0, 0);
-                    sr[j][r] = 0;
-                    zr[j][r] = 0;
-                }
+                w[j][r] = *reinterpret_cast<const uint4 *>(wq_b + (rrel[r] * (uint32_t)RB + (uint32_t)c * 16u));
+                sr[j][r] = sc_b[rrel[r] * (uint32_t)G + (uint32_t)gi];
+                zr[j][r] = zp_b[rrel[r] * (uint32_t)ZB + (uint32_t)(gi >> 1)];
             }
         }
+
         if (seg0 > 0) __syncthreads();                  // previous segment fully read
 #pragma unroll
-        for (int t = 0; t < kXBatch; ++t) {
-            const int i = tid + t * kBlock;
-            if (i < total4) {
-                const int m = i / nx4, r4 = i - m * nx4;
-                const int c = r4 >> 3, sl = r4 & 7;
-                *reinterpret_cast<float4 *>(xs + ((m * segC + c) << 5) + ((sl ^ (c & 7)) << 2)) = xr[t];
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int t = 0; t < XB; ++t) {
+                const int i = tid + t * kBlock;
+                if (i < nx4) {
+                    const int c = i >> 3, sl = i & 7;
+                    *reinterpret_cast<float4 *>(xs + ((m * segC + c) << 5) + ((sl ^ (c & 7)) << 2)) = xr[m][t];
+                }
             }
-        }
-        for (int i = tid + kXBatch * kBlock; i < total4; i += kBlock) {
-            const int m = i / nx4, r4 = i - m * nx4;
-            const int c = r4 >> 3, sl = r4 & 7;
-            const float4 v = *reinterpret_cast<const float4 *>(xseg + (size_t)m * K + r4 * 4);
-            *reinterpret_cast<float4 *>(xs + ((m * segC + c) << 5) + ((sl ^ (c & 7)) << 2)) = v;
-        }
+        for (int m = 0; m < M; ++m)
+            for (int i = tid + XB * kBlock; i < nx4; i += kBlock) {
+                const int c = i >> 3, sl = i & 7;
+                *reinterpret_cast<float4 *>(xs + ((m * segC + c) << 5) + ((sl ^ (c & 7)) << 2)) =
+                    reinterpret_cast<const float4 *>(xseg + (size_t)m * K)[i];
+            }
         __syncthreads();                                // x segment visible
 
 #pragma unroll
@@ -225,7 +238,7 @@ __global__ __launch_bounds__(kBlock) void gemv_q4_kernel(
         }
     }
 
-    // Reduce over the LPR lanes of each row; lane li == 0 of each row holds the result.
+    // Reduce over the LPR lanes of each row; every lane of the row gets the sum.
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -235,7 +248,7 @@ __global__ __launch_bounds__(kBlock) void gemv_q4_kernel(
         if (li == 0) {
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const int row = row0 + r * RG;
+                const int row = row_first + r * RG + rgl;
                 if (row < N)
 #pragma unroll
                     for (int m = 0; m < M; ++m) y[(size_t)m * N + row] = acc[r][m];
@@ -248,18 +261,17 @@ __global__ __launch_bounds__(kBlock) void gemv_q4_kernel(
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int m = 0; m < M; ++m)
-                comb[(wave * RPW + r * RG + lane / LPR) * M + m] = acc[r][m];
+            for (int m = 0; m < M; ++m) comb[(wave * RPW + r * RG + rgl) * M + m] = acc[r][m];
     }
     __syncthreads();
     if (ks == 0 && li == 0) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int row = row0 + r * RG;
+            const int row = row_first + r * RG + rgl;
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 float v = acc[r][m];
-                for (int t = 1; t < S; ++t) v += comb[((wave + t) * RPW + r * RG + lane / LPR) * M + m];
+                for (int t = 1; t < S; ++t) v += comb[((wave + t) * RPW + r * RG + rgl) * M + m];
                 if (row < N) y[(size_t)m * N + row] = v;
             }
         }
@@ -330,9 +342,8 @@ size_t lds_bytes(const Geometry &p) {
 template <int M, int LPR, int JP>
 void launch(const Geometry &p, const float *x, const uint8_t *wq, const uint16_t *scales,
             const uint8_t *zeros, float *y, int N, int K, int gshift, hipStream_t st) {
-    hipLaunchKernelGGL((gemv_q4_kernel<M, LPR, JP>), dim3(p.grid), dim3(kBlock), lds_bytes(p), st,
-                       x, reinterpret_cast<const uint4 *>(wq), scales, zeros, y, N, K, gshift,
-                       p.S, p.seg_chunks);
+    hipLaunchKernelGGL((gemv_q4_kernel<M, LPR, JP, row_slots(M)>), dim3(p.grid), dim3(kBlock),
+                       lds_bytes(p), st, x, wq, scales, zeros, y, N, K, gshift, p.S, p.seg_chunks);
 }
 
 template <int M, int LPR>
