@@ -366,42 +366,94 @@ def run_pmc_workload(args):
 
 def _rows(pattern):
     out = []
-    for f in glob.glob(pattern, recursive=True):
+    for f in sorted(glob.glob(pattern, recursive=True)):
         with open(f, newline="") as fh:
             out.extend(csv.DictReader(fh))
     return out
 
 
-def summarize_profile(args):
-    """Reads rocprofv3 CSV output under DIR and writes the summaries under profiles/."""
-    d = args.summarize
-    os.makedirs(PROFILES, exist_ok=True)
+def _kernel_short(name: str) -> str:
+    import re
+    m = re.search(r"(gemv_q4_kernel<[^>]*>|gemv_f32_kernel<[^>]*>|read_reduce_kernel|"
+                  r"write_fill_kernel|dequant_q4_kernel|at::native::\w+|__amd_rocclr_\w+)", name)
+    return m.group(1) if m else name.split("(")[0][:60]
+
+
+def summarize_stats(d: str, name: str, command: str) -> str:
+    """rocprofv3 --kernel-trace --stats CSV under d -> profiles/<name>.md."""
     stats = _rows(os.path.join(d, "**", "*kernel_stats.csv"))
-    if stats:
-        lines = [f"# rocprofv3 kernel stats\n", f"command: {args.command}\n", "",
-                 "| kernel | calls | avg ns | min ns | max ns | total % |",
-                 "|---|---|---|---|---|---|"]
-        for r in sorted(stats, key=lambda r: -float(r.get("Percentage", 0) or 0)):
-            name = r["Name"].split("(")[0][:90]
-            lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
-                         f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} | "
-                         f"{float(r['Percentage']):.1f} |")
-        out = os.path.join(PROFILES, args.name + ".md")
-        open(out, "w").write("\n".join(lines) + "\n")
-        log("wrote", out)
-    pmc = _rows(os.path.join(d, "**", "*counter_collection.csv"))
-    if pmc:
-        acc = {}
-        for r in pmc:
-            k = (r["Kernel_Name"].split("(")[0], r["Counter_Name"])
-            acc.setdefault(k, []).append(float(r["Counter_Value"]))
-        lines = [f"# rocprofv3 counters\n", f"command: {args.command}\n", "",
-                 "| kernel | counter | dispatches | mean per dispatch |", "|---|---|---|---|"]
-        for (kern, ctr), v in sorted(acc.items()):
-            lines.append(f"| {kern[:90]} | {ctr} | {len(v)} | {statistics.mean(v):.1f} |")
-        out = os.path.join(PROFILES, args.name + ".md")
-        open(out, "w").write("\n".join(lines) + "\n")
-        log("wrote", out)
+    lines = [f"# {name}: rocprofv3 kernel statistics", "", f"command: `{command}`", "",
+             "| kernel | calls | avg ns | min ns | max ns | % of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r.get("Percentage", 0) or 0)):
+        lines.append(f"| {_kernel_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                     f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    q = [r for r in stats if "gemv_q4_kernel" in r["Name"]]
+    if q:
+        avg = float(q[0]["AverageNs"]) * 1e-9
+        b = wl.q4_weight_bytes(wl.STREAM_SHAPE.N, wl.STREAM_SHAPE.K, wl.STREAM_SHAPE.g)
+        lines += ["", f"gemv_q4 average kernel duration {avg * 1e6:.3f} us -> "
+                      f"{b / avg / 1e9:.1f} GB/s of algorithmic bytes ({b} B per launch)."]
+    out = os.path.join(PROFILES, name + ".md")
+    open(out, "w").write("\n".join(lines) + "\n")
+    return out
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, name: str, command: str) -> str:
+    """Two rocprofv3 --pmc runs of --pmc-workload (FETCH_SIZE, then WRITE_SIZE,
+    KiB per dispatch) -> profiles/<name>.md and the JSON bench.py reads for
+    roofline.traffic.  Each counter is scaled by what it reads for a probe of
+    known size: read_reduce streams PROBE_BYTES, write_fill writes PROBE_BYTES."""
+    per = {}
+    for d, ctr in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        for r in _rows(os.path.join(d, "**", "*counter_collection.csv")):
+            if r["Counter_Name"] == ctr:
+                per.setdefault((_kernel_short(r["Kernel_Name"]), ctr), []).append(float(r["Counter_Value"]))
+    mean = {k: statistics.mean(v) for k, v in per.items()}
+    fetch_factor = wl.PROBE_BYTES / (mean[("read_reduce_kernel", "FETCH_SIZE")] * 1024)
+    write_factor = wl.PROBE_BYTES / (mean[("write_fill_kernel", "WRITE_SIZE")] * 1024)
+    qk = next(k for k, _ in mean if k.startswith("gemv_q4_kernel"))
+    s = wl.STREAM_SHAPE
+    alg = wl.q4_weight_bytes(s.N, s.K, s.g)
+    fetch_b = mean[(qk, "FETCH_SIZE")] * 1024 * fetch_factor
+    write_b = mean[(qk, "WRITE_SIZE")] * 1024 * write_factor
+    summary = {"kernel": qk, "workload": "stream 4096x14336 g128, M=1, 32 distinct matrices",
+               "kernel_source_sha256_16": kernel_source_hash(),
+               "fetch_factor": round(fetch_factor, 5), "write_factor": round(write_factor, 5),
+               "gemv_q4_fetch_bytes_per_launch": round(fetch_b),
+               "gemv_q4_write_bytes_per_launch": round(write_b),
+               "gemv_q4_hbm_bytes_per_launch": round(fetch_b + write_b),
+               "algorithmic_bytes_per_launch": alg,
+               "x_and_y_bytes_per_launch": 4 * s.K + 4 * s.N,
+               "command": command}
+    json.dump(summary, open(PMC_SUMMARY, "w"), indent=1)
+    lines = [f"# {name}: HBM traffic from rocprofv3 counters", "", f"command: `{command}`", "",
+             f"Calibration: read_reduce over {wl.PROBE_BYTES} B reads FETCH_SIZE "
+             f"{mean[('read_reduce_kernel', 'FETCH_SIZE')]:.1f} KiB -> factor {fetch_factor:.4f}; "
+             f"write_fill over {wl.PROBE_BYTES} B reads WRITE_SIZE "
+             f"{mean[('write_fill_kernel', 'WRITE_SIZE')]:.1f} KiB -> factor {write_factor:.4f}.", "",
+             "| kernel | counter | dispatches | mean KiB/dispatch | scaled bytes/dispatch |",
+             "|---|---|---|---|---|"]
+    for (k, ctr), v in sorted(per.items()):
+        f = fetch_factor if ctr == "FETCH_SIZE" else write_factor
+        lines.append(f"| {k} | {ctr} | {len(v)} | {statistics.mean(v):.1f} | "
+                     f"{statistics.mean(v) * 1024 * f:.0f} |")
+    lines += ["", f"gemv_q4 per launch: {fetch_b + write_b:.0f} B of HBM traffic against "
+                  f"{alg} algorithmic bytes (+{4 * s.K + 4 * s.N} B of x and y): ratio "
+                  f"{(fetch_b + write_b) / alg:.4f}.",
+              f"Kernel source sha256[:16] {summary['kernel_source_sha256_16']}."]
+    out = os.path.join(PROFILES, name + ".md")
+    open(out, "w").write("\n".join(lines) + "\n")
+    return out
+
+
+def summarize_profile(args):
+    os.makedirs(PROFILES, exist_ok=True)
+    if args.summarize_write:
+        log("wrote", summarize_pmc(args.summarize, args.summarize_write, args.name, args.command))
+    else:
+        log("wrote", summarize_stats(args.summarize, args.name, args.command))
 
 
 # ---------------------------------------------------------------- main
@@ -417,7 +469,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--pmc-workload", action="store_true")
-    ap.add_argument("--summarize", metavar="DIR")
+    ap.add_argument("--summarize", metavar="DIR", help="rocprofv3 CSV dir (stats, or FETCH_SIZE pmc)")
+    ap.add_argument("--summarize-write", metavar="DIR", help="WRITE_SIZE pmc dir (with --summarize)")
     ap.add_argument("--name", default="summary")
     ap.add_argument("--command", default="")
     args = ap.parse_args(argv)

@@ -81,17 +81,35 @@ __device__ __forceinline__ void dot_word(uint32_t wd, half2_t z1, half2_t z16, u
 }
 
 // x staging batch: float4 per thread per activation row fetched ahead of the
-// weight loads (all of x for M = 1 and K <= 8192).
-constexpr int x_batch(int M) { return M >= 8 ? 1 : 8 / M; }
+// weight loads (all of x for M = 1 and K <= 4096).
+constexpr int x_batch(int M) { return M == 1 ? 4 : (M == 2 ? 2 : 1); }
+
+// LDS layout of the x segment: chunk c of activation row m (32 floats) at
+// float offset (m * segC + c) * kXStride.  The 4-float pad makes the stride
+// 144 bytes, so the 16 lanes of one LDS pass reading the same 16-byte slot of
+// 16 consecutive chunks land in 16 distinct 4-bank groups.
+constexpr int kXStride = 36;
+
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));   // a plain vector, never an aggregate copy
+
+// Buffer resource for a raw (untyped) byte range on gfx9: base, no stride,
+// num_records bytes (reads past it return zero), default dword-3 format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Cache-policy bits of a buffer load: non-temporal, for the weight stream
+// that is read once.
+constexpr int kNonTemporal = 2;
 
 // M: activation rows.  LPR: lanes per output row.  JP: chunk positions per
 // lane per segment (a lane's chunks are LPR apart).  R: row slots per wave.
 //
-// Addressing: every pointer the wavefront uses is a wave-uniform base (kept in
-// SGPRs) plus a 32-bit per-lane byte offset, so each load is a single
-// global_load with saddr and no 64-bit address arithmetic in VALU.
+// Addressing: pointers are wave-uniform bases (SGPRs) plus one 32-bit
+// per-lane offset shared by all rows of the wave when LPR = 64.
 template <int M, int LPR, int JP, int R>
-__global__ __launch_bounds__(kBlock) void gemv_q4_kernel(
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) void gemv_q4_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ wq,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
     float *__restrict__ y, int N, int K, int gshift, int S, int seg_chunks) {
@@ -99,8 +117,8 @@ __global__ __launch_bounds__(kBlock) void gemv_q4_kernel(
     constexpr int RPW = R * RG;           // output rows per wavefront
     constexpr int XB = x_batch(M);
     extern __shared__ float lds[];
-    float *xs = lds;                                        // [M][segC][32] swizzled
-    float *comb = lds + M * seg_chunks * 32;                // [waves][RPW][M]
+    float *xs = lds;                                        // [M][segC][kXStride]
+    float *comb = lds + M * seg_chunks * kXStride;          // [waves][RPW][M]
 
     const int C = K >> 5;              // chunks per row
     const int G = K >> (gshift + 5);   // groups per row
@@ -113,17 +131,26 @@ __global__ __launch_bounds__(kBlock) void gemv_q4_kernel(
     const int ks = wave - rb * S;      // K-split index
     const int row_first = (blockIdx.x * (kWaves / S) + rb) * RPW;   // may be >= N
     const int row_base = min(row_first, N - 1);
-    const int rgl = lane / LPR;
-    const int li = lane % LPR;
+    const int rgl = RG == 1 ? 0 : lane / LPR;
+    const int li = RG == 1 ? lane : lane % LPR;
     const uint32_t magic = 0x64006400u;
 
-    // Wave-uniform bases and per-lane row offsets (rows past N re-read row N-1).
-    const uint8_t *wq_b = wq + (size_t)row_base * RB;
-    const uint16_t *sc_b = scales + (size_t)row_base * G;
-    const uint8_t *zp_b = zeros + (size_t)row_base * ZB;
-    uint32_t rrel[R];
+    // Wave-uniform buffer resources starting at the wave's first row; per-row
+    // byte offsets are uniform (SGPR soffset) when RG == 1 and per-lane
+    // otherwise.  Rows past N re-read row N-1 and are not stored.
+    const uint32_t rows_left = (uint32_t)(N - row_base);
+    const __amdgpu_buffer_rsrc_t wq_r = raw_rsrc(wq + (size_t)row_base * RB,
+        (uint32_t)std::min<uint64_t>((uint64_t)rows_left * RB, 0xFFFFFFFFull));
+    const __amdgpu_buffer_rsrc_t sc_r = raw_rsrc(scales + (size_t)row_base * G, rows_left * (uint32_t)G * 2u);
+    const __amdgpu_buffer_rsrc_t zp_r = raw_rsrc(zeros + (size_t)row_base * ZB, rows_left * (uint32_t)ZB);
+    uint32_t roff[R], soff[R], zoff[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) rrel[r] = (uint32_t)(min(row_first + r * RG + rgl, N - 1) - row_base);
+    for (int r = 0; r < R; ++r) {
+        const uint32_t rr = (uint32_t)(min(row_first + r * RG + rgl, N - 1) - row_base);
+        roff[r] = rr * (uint32_t)RB;
+        soff[r] = rr * (uint32_t)G * 2u;
+        zoff[r] = rr * (uint32_t)ZB;
+    }
 
     float acc[R][M];
 #pragma unroll
@@ -141,16 +168,16 @@ __global__ __launch_bounds__(kBlock) void gemv_q4_kernel(
 
         // x segment, first batch: global -> registers ahead of the weight
         // loads, so that waiting for x does not wait for the weights (vmcnt
-        // retires loads in issue order).
-        float4 xr[M][XB];
+        // retires loads in issue order).  Guards are uniform except in a
+        // batch that straddles the end of the segment.
+        f32x4_t xr[M][XB];
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
-            for (int t = 0; t < XB; ++t) {
-                const int i = tid + t * kBlock;
-                xr[m][t] = i < nx4 ? reinterpret_cast<const float4 *>(xseg + (size_t)m * K)[i]
-                                   : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
+            for (int t = 0; t < XB; ++t)   // indexes past the segment re-read its last float4
+                xr[m][t] = reinterpret_cast<const f32x4_t *>(xseg + (size_t)m * K)[min(t * kBlock + tid, nx4 - 1)];
+        // Keep the x loads ahead of the weight loads in issue order.
+        __builtin_amdgcn_sched_barrier(0);
 
         // Weight stream: every load of the lane is issued before any
         // arithmetic.  Positions past this wave's range re-read its last
@@ -162,49 +189,52 @@ __global__ __launch_bounds__(kBlock) void gemv_q4_kernel(
 #pragma unroll
         for (int j = 0; j < JP; ++j) {
             const int c = min(lo + li + j * LPR, clast);
-            const int gi = c >> gshift;
+            const uint32_t coff = (uint32_t)c * 16u;
+            const uint32_t gi = (uint32_t)c >> gshift;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                w[j][r] = *reinterpret_cast<const uint4 *>(wq_b + (rrel[r] * (uint32_t)RB + (uint32_t)c * 16u));
-                sr[j][r] = sc_b[rrel[r] * (uint32_t)G + (uint32_t)gi];
-                zr[j][r] = zp_b[rrel[r] * (uint32_t)ZB + (uint32_t)(gi >> 1)];
+                // RG == 1: row offset in soffset (SGPR), chunk offset in voffset.
+                const uint32_t vw = RG == 1 ? coff : coff + roff[r];
+                const uint32_t sw = RG == 1 ? roff[r] : 0u;
+                const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(wq_r, vw, sw, kNonTemporal);
+                w[j][r] = make_uint4(t.x, t.y, t.z, t.w);
+                sr[j][r] = __builtin_amdgcn_raw_buffer_load_b16(
+                    sc_r, RG == 1 ? gi * 2u : gi * 2u + soff[r], RG == 1 ? soff[r] : 0u, 0);
+                zr[j][r] = __builtin_amdgcn_raw_buffer_load_b8(
+                    zp_r, RG == 1 ? (gi >> 1) : (gi >> 1) + zoff[r], RG == 1 ? zoff[r] : 0u, 0);
             }
         }
 
-        if (seg0 > 0) __syncthreads();                  // previous segment fully read
+        // Unconditional stores (lanes past the segment rewrite its last float4
+        // with the value it already holds): a guarded store would let the
+        // compiler sink the x loads behind the weight loads.
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
             for (int t = 0; t < XB; ++t) {
-                const int i = tid + t * kBlock;
-                if (i < nx4) {
-                    const int c = i >> 3, sl = i & 7;
-                    *reinterpret_cast<float4 *>(xs + ((m * segC + c) << 5) + ((sl ^ (c & 7)) << 2)) = xr[m][t];
-                }
+                const int i = min(t * kBlock + tid, nx4 - 1);
+                *reinterpret_cast<f32x4_t *>(xs + (m * segC + (i >> 3)) * kXStride + (i & 7) * 4) = xr[m][t];
             }
         for (int m = 0; m < M; ++m)
-            for (int i = tid + XB * kBlock; i < nx4; i += kBlock) {
-                const int c = i >> 3, sl = i & 7;
-                *reinterpret_cast<float4 *>(xs + ((m * segC + c) << 5) + ((sl ^ (c & 7)) << 2)) =
-                    reinterpret_cast<const float4 *>(xseg + (size_t)m * K)[i];
-            }
+            for (int i = XB * kBlock + tid; i < nx4; i += kBlock)
+                *reinterpret_cast<f32x4_t *>(xs + (m * segC + (i >> 3)) * kXStride + (i & 7) * 4) =
+                    reinterpret_cast<const f32x4_t *>(xseg + (size_t)m * K)[i];
         __syncthreads();                                // x segment visible
 
 #pragma unroll
         for (int j = 0; j < JP; ++j) {
             const int c = lo + li + j * LPR;
             if (c < hi) {
-                const int cl = c - seg0;
-                const int sw = cl & 7;
-                const int gi = c >> gshift;
+                const float *xc = xs + (c - seg0) * kXStride;
+                const uint32_t gi = (uint32_t)c >> gshift;
+                const uint32_t zsh = (gi & 1u) << 2;
                 half2_t z1[R], z16[R];
                 float ae[R][M], ao[R][M];
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    const uint32_t z = (zr[j][r] >> ((gi & 1) << 2)) & 0xFu;
-                    const uint32_t zz = z | (z << 16);
-                    z1[r] = as_h2(zz | magic);
-                    z16[r] = as_h2((zz << 4) | magic);
+                    const uint32_t z = (zr[j][r] >> zsh) & 0xFu;
+                    z1[r] = as_h2(z * 0x00010001u + magic);
+                    z16[r] = as_h2(z * 0x00100010u + magic);
 #pragma unroll
                     for (int m = 0; m < M; ++m) ae[r][m] = ao[r][m] = 0.f;
                 }
@@ -213,9 +243,9 @@ __global__ __launch_bounds__(kBlock) void gemv_q4_kernel(
                     float xv[M][8];
 #pragma unroll
                     for (int m = 0; m < M; ++m) {
-                        const float *base = xs + ((m * segC + cl) << 5);
-                        const float4 a = *reinterpret_cast<const float4 *>(base + (((2 * wd) ^ sw) << 2));
-                        const float4 b = *reinterpret_cast<const float4 *>(base + (((2 * wd + 1) ^ sw) << 2));
+                        const float *base = xc + m * segC * kXStride + wd * 8;
+                        const float4 a = *reinterpret_cast<const float4 *>(base);
+                        const float4 b = *reinterpret_cast<const float4 *>(base + 4);
                         xv[m][0] = a.x; xv[m][1] = a.y; xv[m][2] = a.z; xv[m][3] = a.w;
                         xv[m][4] = b.x; xv[m][5] = b.y; xv[m][6] = b.z; xv[m][7] = b.w;
                     }
@@ -236,43 +266,91 @@ __global__ __launch_bounds__(kBlock) void gemv_q4_kernel(
                 }
             }
         }
+        if (seg0 + seg_chunks < C) __syncthreads();    // x segment fully read before the next overwrites it
     }
 
-    // Reduce over the LPR lanes of each row; every lane of the row gets the sum.
+    if constexpr (LPR == 64) {
+        // One transposing reduction for all R rows; on 16-lane row h, out[m][q]
+        // holds the sum of row slot reduced_row<R>(q, h).  Lane 16h stores it.
+        constexpr int NQ = (R + 3) / 4;
+        float out[M][NQ];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+        for (int m = 0; m < M; ++m) {
+            float v[R];
 #pragma unroll
-        for (int m = 0; m < M; ++m) acc[r][m] = q4::group_sum<LPR>(acc[r][m]);
-
-    if (S == 1) {
-        if (li == 0) {
+            for (int r = 0; r < R; ++r) v[r] = acc[r][m];
+            q4::wave_reduce_rows<R>(v, out[m]);
+        }
+        const int h = lane >> 4;
+        const bool writer = (lane & 15) == 0 && (R >= 4 || (h & (R == 2 ? 1 : 3)) == 0);
+        if (S == 1) {
+            if (writer) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const int row = row_first + r * RG + rgl;
-                if (row < N)
+                for (int q = 0; q < NQ; ++q) {
+                    const int row = row_first + q4::reduced_row<R>(q, h);
+                    if (row < N)
 #pragma unroll
-                    for (int m = 0; m < M; ++m) y[(size_t)m * N + row] = acc[r][m];
+                        for (int m = 0; m < M; ++m) y[(size_t)m * N + row] = out[m][q];
+                }
+            }
+            return;
+        }
+        if (writer) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    comb[(wave * RPW + q4::reduced_row<R>(q, h)) * M + m] = out[m][q];
+        }
+        __syncthreads();
+        if (ks == 0 && writer) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const int rs = q4::reduced_row<R>(q, h);
+                const int row = row_first + rs;
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    float v = out[m][q];
+                    for (int t = 1; t < S; ++t) v += comb[((wave + t) * RPW + rs) * M + m];
+                    if (row < N) y[(size_t)m * N + row] = v;
+                }
             }
         }
-        return;
-    }
-    // K-split: wavefronts ks = 0..S-1 of one row block meet in LDS.
-    if (li == 0) {
+    } else {
+        // Rows narrower than a wavefront: reduce each over its LPR lanes.
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int m = 0; m < M; ++m) comb[(wave * RPW + r * RG + rgl) * M + m] = acc[r][m];
-    }
-    __syncthreads();
-    if (ks == 0 && li == 0) {
+            for (int m = 0; m < M; ++m) acc[r][m] = q4::group_sum<LPR>(acc[r][m]);
+        if (S == 1) {
+            if (li == 0) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int row = row_first + r * RG + rgl;
+                for (int r = 0; r < R; ++r) {
+                    const int row = row_first + r * RG + rgl;
+                    if (row < N)
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-                float v = acc[r][m];
-                for (int t = 1; t < S; ++t) v += comb[((wave + t) * RPW + r * RG + rgl) * M + m];
-                if (row < N) y[(size_t)m * N + row] = v;
+                        for (int m = 0; m < M; ++m) y[(size_t)m * N + row] = acc[r][m];
+                }
+            }
+            return;
+        }
+        if (li == 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int m = 0; m < M; ++m) comb[(wave * RPW + r * RG + rgl) * M + m] = acc[r][m];
+        }
+        __syncthreads();
+        if (ks == 0 && li == 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int row = row_first + r * RG + rgl;
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    float v = acc[r][m];
+                    for (int t = 1; t < S; ++t) v += comb[((wave + t) * RPW + r * RG + rgl) * M + m];
+                    if (row < N) y[(size_t)m * N + row] = v;
+                }
             }
         }
     }
@@ -295,7 +373,7 @@ Geometry plan(int M, int N, int K, int g) {
     // K-split, decided on the length of one x segment: enough wavefronts to
     // fill the chip (>= 2 per SIMD) and at most two chunk positions per lane,
     // while every split keeps a full lane sweep.
-    const int seg_len = std::min(C, kLdsBytes / (M * 32 * (int)sizeof(float)));
+    const int seg_len = std::min(C, kLdsBytes / (M * kXStride * (int)sizeof(float)));
     p.S = 1;
     while (p.S < kWaves && 2 * p.S * p.LPR <= seg_len &&
            (row_waves * p.S < 2048 || (seg_len + p.S * p.LPR - 1) / (p.S * p.LPR) > 2))
@@ -303,7 +381,7 @@ Geometry plan(int M, int N, int K, int g) {
     // x segment: the LDS left after the K-split partial sums, in whole chunks;
     // when x needs several segments, each is a whole number of lane sweeps.
     const int comb = p.S > 1 ? kWaves * p.rows_per_wave * M * (int)sizeof(float) : 0;
-    const int max_seg = (kLdsBytes - comb) / (M * 32 * (int)sizeof(float));
+    const int max_seg = (kLdsBytes - comb) / (M * kXStride * (int)sizeof(float));
     if (C <= max_seg) {
         p.seg_chunks = C;
     } else {
@@ -334,7 +412,7 @@ int validate(int M, int N, int K, int g) {
 // LDS bytes a launch needs: the x segment plus, with a K-split, one partial
 // sum per (wavefront, row, m).
 size_t lds_bytes(const Geometry &p) {
-    size_t b = (size_t)p.M * p.seg_chunks * 32 * sizeof(float);
+    size_t b = (size_t)p.M * p.seg_chunks * kXStride * sizeof(float);
     if (p.S > 1) b += (size_t)kWaves * p.rows_per_wave * p.M * sizeof(float);
     return b;
 }
