@@ -180,17 +180,31 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
         __builtin_amdgcn_sched_barrier(0);
 
         // Weight stream: every load of the lane is issued before any
-        // arithmetic.  Positions past this wave's range re-read its last
-        // chunk (always in bounds) and are skipped below.
+        // arithmetic, the small scale and zero-point loads first, then the
+        // codes in the order they are consumed.  Loads retire in issue order
+        // (vmcnt), so with the metadata ahead the arithmetic on the first
+        // chunk waits for that chunk only, not for the whole wave's data.
+        // Positions past this wave's range re-read its last chunk (always in
+        // bounds) and are skipped below.
         uint4 w[JP][R];
         uint32_t sr[JP][R];
         uint32_t zr[JP][R];
         const int clast = max(lo, hi - 1) < seg0 + segC ? max(lo, hi - 1) : seg0 + segC - 1;
 #pragma unroll
         for (int j = 0; j < JP; ++j) {
-            const int c = min(lo + li + j * LPR, clast);
-            const uint32_t coff = (uint32_t)c * 16u;
-            const uint32_t gi = (uint32_t)c >> gshift;
+            const uint32_t gi = (uint32_t)min(lo + li + j * LPR, clast) >> gshift;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                sr[j][r] = __builtin_amdgcn_raw_buffer_load_b16(
+                    sc_r, RG == 1 ? gi * 2u : gi * 2u + soff[r], RG == 1 ? soff[r] : 0u, 0);
+                zr[j][r] = __builtin_amdgcn_raw_buffer_load_b8(
+                    zp_r, RG == 1 ? (gi >> 1) : (gi >> 1) + zoff[r], RG == 1 ? zoff[r] : 0u, 0);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < JP; ++j) {
+            const uint32_t coff = (uint32_t)min(lo + li + j * LPR, clast) * 16u;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 // RG == 1: row offset in soffset (SGPR), chunk offset in voffset.
@@ -198,10 +212,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
                 const uint32_t sw = RG == 1 ? roff[r] : 0u;
                 const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(wq_r, vw, sw, kNonTemporal);
                 w[j][r] = make_uint4(t.x, t.y, t.z, t.w);
-                sr[j][r] = __builtin_amdgcn_raw_buffer_load_b16(
-                    sc_r, RG == 1 ? gi * 2u : gi * 2u + soff[r], RG == 1 ? soff[r] : 0u, 0);
-                zr[j][r] = __builtin_amdgcn_raw_buffer_load_b8(
-                    zp_r, RG == 1 ? (gi >> 1) : (gi >> 1) + zoff[r], RG == 1 ? zoff[r] : 0u, 0);
             }
         }
 
