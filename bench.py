@@ -33,6 +33,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -305,6 +306,9 @@ def run_default(args):
     measured_peak = result.get("read_reduce", {}).get("GBps_median")
 
     traffic = traffic_from_profile(bytes_per_call["gemv_q4"])
+    integer = q4.gemv_q4_path(1, s.N, s.K, s.g) == q4.Q4_PATH_INTEGER
+    arith = ("x per 32 values in 23-bit block fixed point, exact int32 chunk sums, fp32 accumulate"
+             if integer else "(q-z) in fp16, fp32 x, fp32 multiply-add and accumulate")
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -316,14 +320,15 @@ def run_default(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "i32+f32" if integer else "f32",
         "data": "synthetic",
         "config": {"workload": "stream: 32 distinct int4 g128 matrices, K=4096 N=14336, "
                                "cycled at M=1 (976,224,256 B > L2 + MALL)",
                    "M": 1, "K": 4096, "N": 14336, "group_size": 128,
                    "matrices": wl.STREAM_MATRICES, "bytes_per_call": bytes_per_call["gemv_q4"],
                    "launches_per_step": wl.STREAM_MATRICES,
-                   "weights": "int4 codes, fp16 scale + int4 zero per 128, fp32 x/y/accumulate"},
+                   "weights": "int4 codes, fp16 scale + int4 zero per 128, fp32 x and y",
+                   "arithmetic": arith},
         "roofline": {"bound": "hbm", "achieved": round(value, 2), "peak": SPEC_PEAK_GBS,
                      "unit": "GB/s", "frac": round(value / SPEC_PEAK_GBS, 4),
                      "traffic": traffic},
@@ -373,8 +378,8 @@ def _rows(pattern):
 
 
 def _kernel_short(name: str) -> str:
-    import re
-    m = re.search(r"(gemv_q4_kernel<[^>]*>|gemv_f32_kernel<[^>]*>|read_reduce_kernel|"
+
+    m = re.search(r"(gemv_q4(?:_int)?_kernel<[^>]*>|gemv_f32_kernel<[^>]*>|read_reduce_kernel|"
                   r"write_fill_kernel|dequant_q4_kernel|at::native::\w+|__amd_rocclr_\w+)", name)
     return m.group(1) if m else name.split("(")[0][:60]
 
@@ -389,7 +394,7 @@ def summarize_stats(d: str, name: str, command: str) -> str:
         lines.append(f"| {_kernel_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
                      f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} | "
                      f"{float(r['Percentage']):.2f} |")
-    q = [r for r in stats if "gemv_q4_kernel" in r["Name"]]
+    q = [r for r in stats if re.search(r"gemv_q4(_int)?_kernel", r["Name"])]
     if q:
         avg = float(q[0]["AverageNs"]) * 1e-9
         b = wl.q4_weight_bytes(wl.STREAM_SHAPE.N, wl.STREAM_SHAPE.K, wl.STREAM_SHAPE.g)
@@ -413,7 +418,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, name: str, command: str) -> st
     mean = {k: statistics.mean(v) for k, v in per.items()}
     fetch_factor = wl.PROBE_BYTES / (mean[("read_reduce_kernel", "FETCH_SIZE")] * 1024)
     write_factor = wl.PROBE_BYTES / (mean[("write_fill_kernel", "WRITE_SIZE")] * 1024)
-    qk = next(k for k, _ in mean if k.startswith("gemv_q4_kernel"))
+    qk = next(k for k, _ in mean if k.startswith("gemv_q4_"))
     s = wl.STREAM_SHAPE
     alg = wl.q4_weight_bytes(s.N, s.K, s.g)
     fetch_b = mean[(qk, "FETCH_SIZE")] * 1024 * fetch_factor

@@ -54,10 +54,26 @@ enum q4_status {
     Q4_ELAUNCH = -5  /* the kernel launch reported an error */
 };
 
-/* int4 decode GEMV: y[M, N] = x[M, K] . dequant(W_q[N, K])^T, fp32 accumulate.
- * Dequantisation (q - z) * s is exact in fp32; products with x are fused
- * multiply-adds in fp32 (gerbil "WGSL Kernel Reference", section 3
- * MatMulInt4, "Dequantization").
+/* int4 decode GEMV: y[M, N] = x[M, K] . dequant(W_q[N, K])^T, fp32 accumulate
+ * (gerbil "WGSL Kernel Reference", section 3 MatMulInt4, "Dequantization").
+ * Two arithmetic paths (gemv_q4_path tells which one a shape takes):
+ *   - fused multiply-add: (q - z) formed exactly in binary16, multiplied by
+ *     the fp32 x and accumulated in fp32, the group scale applied per
+ *     32-code chunk;
+ *   - integer (M == 1, 1024 < K <= 18688): every chunk of 32 x values
+ *     (x[32c .. 32c+31]) is rounded to integers X = round(x * 2^(22-e)),
+ *     where 2^(e-1) <= max|x| over the chunk < 2^e, so |X| < 2^22; the sum
+ *     of (q - z) * X is formed exactly in int32, converted to fp32 once per
+ *     chunk and scaled by 2^(e-22) and the group scale.  q == z gives
+ *     exactly 0; a chunk of x holding Inf or NaN makes every output NaN.
+ * Accuracy against the exact sum y_ref, with w = (q - z) * s:
+ *   - fused multiply-add path: |y - y_ref| <= 1e-4 * sum_k |x_k w_k| + 1e-6;
+ *   - integer path: the same bound plus the rounding of x, at most
+ *     2^-22 * max|x over the chunk| * |w_k| for each k.  It stays inside
+ *     the first bound whenever no nonzero w_k meets an x_k more than 400
+ *     times smaller than its chunk's largest |x| (x ~ N(0, 1) keeps a margin
+ *     of about 100); a chunk whose large values all meet w = 0 while small
+ *     ones meet w != 0 can exceed it.
  *   1 <= M <= 8;  N >= 0 (N == 0 launches nothing);  group_size in {32, 128};
  *   K >= group_size and K % group_size == 0.
  *   x and wq 16-byte aligned; scales 2-byte aligned; y 4-byte aligned.
@@ -105,12 +121,21 @@ int write_fill(float *buf, size_t n_floats, float value, int n_blocks, void *str
  * pointer may be NULL.  Returns Q4_EINVAL for an invalid shape.
  *   grid         workgroups launched
  *   block        threads per workgroup
- *   rows_per_wave output rows one wavefront owns
+ *   rows_per_wave output rows one wavefront owns (the integer path: at most;
+ *                a workgroup owns ceil(N / grid) rows, dealt evenly to its
+ *                row groups)
  *   lanes_per_row lanes that share one row's K range (16, 32 or 64)
  *   ksplit       wavefronts that split one row block's K range
  *   segments     x segments staged through LDS one after another */
 int gemv_q4_geometry(int M, int N, int K, int group_size, int *grid, int *block,
                      int *rows_per_wave, int *lanes_per_row, int *ksplit, int *segments);
+
+/* Which arithmetic path gemv_q4 takes for a shape (see gemv_q4): returns
+ * Q4_PATH_FMA or Q4_PATH_INTEGER, or Q4_EINVAL for an invalid shape.
+ * Host-only; launches nothing and needs no device. */
+#define Q4_PATH_FMA 0
+#define Q4_PATH_INTEGER 1
+int gemv_q4_path(int M, int N, int K, int group_size);
 
 /* Human-readable text for a q4_status value (never NULL). */
 const char *q4_strerror(int status);

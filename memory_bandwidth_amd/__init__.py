@@ -26,7 +26,9 @@ Q4_OK, Q4_EINVAL, Q4_ENULL, Q4_EALIGN, Q4_EDEVICE, Q4_ELAUNCH = 0, -1, -2, -3, -
 
 # Exported C symbols, in the order include/q4gemv.h declares them.
 EXPORTS = ("gemv_q4", "gemv_f32", "dequant_q4", "read_reduce", "write_fill",
-           "gemv_q4_geometry", "q4_strerror", "q4_abi_version")
+           "gemv_q4_geometry", "gemv_q4_path", "q4_strerror", "q4_abi_version")
+
+Q4_PATH_FMA, Q4_PATH_INTEGER = 0, 1
 
 _lib = None
 
@@ -54,11 +56,12 @@ def lib() -> ctypes.CDLL:
     L.write_fill.argtypes = [P, Z, ctypes.c_float, I, P]
     IP = ctypes.POINTER(ctypes.c_int)
     L.gemv_q4_geometry.argtypes = [I, I, I, I, IP, IP, IP, IP, IP, IP]
+    L.gemv_q4_path.argtypes = [I, I, I, I]
     L.q4_strerror.argtypes = [I]
     L.q4_strerror.restype = ctypes.c_char_p
     L.q4_abi_version.argtypes = []
     for f in ("gemv_q4", "gemv_f32", "dequant_q4", "read_reduce", "write_fill",
-              "gemv_q4_geometry", "q4_abi_version"):
+              "gemv_q4_geometry", "gemv_q4_path", "q4_abi_version"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -190,6 +193,14 @@ def gemv_q4_geometry(M: int, N: int, K: int, group_size: int) -> dict:
                                                       *[ctypes.byref(v) for v in vals]))
     keys = ("grid", "block", "rows_per_wave", "lanes_per_row", "ksplit", "segments")
     return {k: v.value for k, v in zip(keys, vals)}
+
+
+def gemv_q4_path(M: int, N: int, K: int, group_size: int) -> int:
+    """Q4_PATH_FMA or Q4_PATH_INTEGER: the arithmetic path gemv_q4 takes (host-only)."""
+    r = lib().gemv_q4_path(M, N, K, group_size)
+    if r < 0:
+        raise Q4Error("gemv_q4_path", r)
+    return r
 
 
 def abi_version() -> int:

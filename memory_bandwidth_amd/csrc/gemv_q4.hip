@@ -366,9 +366,308 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     }
 }
 
+// ---------------------------------------------------------------- M = 1: exact integer dot products
+//
+// With one activation row the (q - z) * x products are formed exactly in
+// integer arithmetic, eight per instruction.  Each chunk of 32 x values is
+// written in block fixed point: with e the binary exponent of the chunk's
+// largest |x| (|x| < 2^e), X = round(x * 2^(22-e)) is an integer with
+// |X| <= 2^22 and x = X * 2^(e-22) to within half a unit of X, i.e. to
+// within 2^-23 of the chunk's largest |x|.  X is held as six signed 4-bit
+// digits, X = sum_l d_l 16^l with d_l in [-8, 7] (the nibbles of
+// (X + 0x888888) ^ 0x888888), and the digits of 8 consecutive x values are
+// transposed into one 32-bit word per digit, so that v_dot8_i32_i4 of such
+// a word against a word of 8 codes, each read as q - 8 in [-8, 7] by one XOR
+// with 0x88888888, sums the 8 products of one digit.  Then
+//     sum_k (q_k - z) X_k = sum_l 16^l sum_k (q_k - 8) d_l[k] + (8 - z) sum_k X_k
+// holds exactly in int32 (|sum| <= 32 * 15 * 2^22 < 2^31), so q == z still
+// gives exactly 0.  One conversion to fp32 per chunk, scaled by 2^(e-22) and
+// the group scale, accumulates into the row's fp32 sum.
+
+constexpr int kIW = 28;   // LDS dwords per chunk: digit d of word w at 4d+w, then SX low/high, 2^(e-22)
+
+// 8x8 transpose of 4-bit fields: on return nibble p of a[l] is nibble l of
+// the input a[p].  Three butterfly stages: nibbles between neighbouring
+// words, bytes between words two apart, half-words between words four apart.
+__device__ __forceinline__ void transpose_nibbles(uint32_t (&a)[8]) {
+#pragma unroll
+    for (int p = 0; p < 8; p += 2) {
+        const uint32_t lo = a[p], hi = a[p + 1];
+        a[p] = (lo & 0x0F0F0F0Fu) | ((hi << 4) & 0xF0F0F0F0u);
+        a[p + 1] = ((lo >> 4) & 0x0F0F0F0Fu) | (hi & 0xF0F0F0F0u);
+    }
+#pragma unroll
+    for (int p = 0; p < 8; p += (p & 1) ? 3 : 1) {      // pairs (0,2) (1,3) (4,6) (5,7)
+        const uint32_t u = a[p], v = a[p + 2];
+        a[p] = __builtin_amdgcn_perm(v, u, 0x06020400u);
+        a[p + 2] = __builtin_amdgcn_perm(v, u, 0x07030501u);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t u = a[p], v = a[p + 4];
+        a[p] = __builtin_amdgcn_perm(v, u, 0x05040100u);
+        a[p + 4] = __builtin_amdgcn_perm(v, u, 0x07060302u);
+    }
+}
+
+// Converts one chunk of x to its LDS record.  The chunk's 32 values are held
+// by the lane pair (2i, 2i+1), 16 each in order; `half` is lane & 1.  Every
+// lane of the wavefront must call it (the pair exchanges partial results by
+// DPP); only lanes with `store` set write the record.
+__device__ __forceinline__ void store_int_chunk(const f32x4_t (&xr)[4], int half, bool store,
+                                                uint32_t *rec) {
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[4 * i] = xr[i].x; v[4 * i + 1] = xr[i].y; v[4 * i + 2] = xr[i].z; v[4 * i + 3] = xr[i].w;
+    }
+    // NaN-propagating maximum (v_maximum3_f32), so a NaN anywhere reaches m
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = __builtin_elementwise_maximum(m, __builtin_fabsf(v[i]));
+    // quad_perm [1,0,3,2]: each lane reads its pair partner
+    m = __builtin_elementwise_maximum(
+        m, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, m), 0xB1, 0xF, 0xF, false)));
+    const int sh = 22 - __builtin_amdgcn_frexp_expf(m);   // |x| * 2^sh < 2^22 (m == 0: sh = 22)
+    uint32_t dg[16];
+    uint32_t sx = 0;                                       // sum of X, two's complement
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        // adding 1.5 * 2^23 rounds to the nearest integer and leaves it in the low mantissa bits
+        const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_amdgcn_ldexpf(v[i], sh) + 12582912.0f);
+        sx += b - 0x4B400000u;
+        dg[i] = (b + (0x888888u - 0x4B400000u)) ^ 0x888888u;
+    }
+    sx += (uint32_t)__builtin_amdgcn_mov_dpp((int)sx, 0xB1, 0xF, 0xF, false);
+    if (!store) return;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        uint32_t a[8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) a[p] = dg[8 * w + p];
+        transpose_nibbles(a);
+#pragma unroll
+        for (int d = 0; d < 6; ++d) rec[4 * d + 2 * half + w] = a[d];
+    }
+    if (half == 0) {
+        // a chunk holding Inf or NaN gets a NaN scale, so its rows come out NaN
+        const float scale = m <= 3.4028235e38f ? __builtin_amdgcn_ldexpf(1.0f, -sh) : m - m;
+        rec[24] = sx & 0xFFFu;
+        rec[25] = (uint32_t)((int)sx >> 12);   // arithmetic shift: SX = 4096 * high + low
+        rec[26] = __builtin_bit_cast(uint32_t, scale);
+    }
+}
+
+// JP: chunk positions per lane (a lane's chunks are 64 apart).  R: row slots
+// per wavefront.  A workgroup owns rpg consecutive rows, split as evenly as
+// possible over kWaves / S row groups; the S wavefronts of a row group split
+// its K range and meet in LDS.  MULTI: x has more than 128 chunks, so its
+// conversion takes several passes of the workgroup.  S and MULTI are template
+// parameters so that the common case (S = 1, one pass) carries no division
+// and no unused path.
+template <int JP, int R, int S, bool MULTI>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) void gemv_q4_int_kernel(
+    const float *__restrict__ x, const uint8_t *__restrict__ wq,
+    const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
+    float *__restrict__ y, int N, int K, int gshift, int rpg) {
+    extern __shared__ uint32_t ilds[];
+    const int tid = threadIdx.x;
+    // x first, before any address arithmetic: the workgroup cannot start
+    // computing until x has landed, and every load issued later on this CU
+    // returns after it.  Lane pair (2i, 2i+1) loads chunk i, 16 values each;
+    // reads past K return 0.
+    const int hc = tid >> 1, half = tid & 1;
+    const __amdgpu_buffer_rsrc_t x_r = raw_rsrc(x, (uint32_t)K * 4u);
+    f32x4_t xr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        xr[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+            x_r, (uint32_t)(hc * 32 + half * 16 + 4 * i) * 4u, 0, 0));
+    __builtin_amdgcn_sched_barrier(0);
+
+    const int C = K >> 5;
+    const int G = K >> (gshift + 5);
+    const int ZB = (G + 1) >> 1;
+    const int RB = K >> 1;
+    uint32_t *xrec = ilds;                                           // [C][kIW]
+    float *comb = reinterpret_cast<float *>(ilds + C * kIW);         // [kWaves][R]
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int NG = kWaves / S;                 // row groups per workgroup
+    const int rg = wave / S;
+    const int ks = wave - rg * S;
+    const int gq = rpg / NG, grem = rpg - gq * NG;
+    const int gstart = blockIdx.x * rpg + rg * gq + min(rg, grem);
+    const int nrows = max(0, min(gq + (rg < grem ? 1 : 0), N - gstart));   // rows of this group, <= R
+    const int rbase = min(gstart, N - 1);
+    const int part = (C + S - 1) / S;
+    const int lo = ks * part;
+    const int hi = min(C, lo + part);
+    const int clast = min(max(lo, hi - 1), C - 1);   // loads past the slice re-read a valid chunk
+    const uint32_t magic8 = 0x88888888u;
+
+    const uint32_t rows_left = (uint32_t)(N - rbase);
+    const __amdgpu_buffer_rsrc_t wq_r = raw_rsrc(wq + (size_t)rbase * RB,
+        (uint32_t)std::min<uint64_t>((uint64_t)rows_left * RB, 0xFFFFFFFFull));
+    const __amdgpu_buffer_rsrc_t sc_r = raw_rsrc(scales + (size_t)rbase * G, rows_left * (uint32_t)G * 2u);
+    const __amdgpu_buffer_rsrc_t zp_r = raw_rsrc(zeros + (size_t)rbase * ZB, rows_left * (uint32_t)ZB);
+    uint32_t lr[R];   // row offset of each slot: slots past the group's rows re-read its last row
+#pragma unroll
+    for (int r = 0; r < R; ++r) lr[r] = (uint32_t)min(r, max(nrows, 1) - 1);
+
+    // Group metadata, then the codes in the order they are consumed.
+    uint32_t sr[JP][R], zr[JP][R];
+#pragma unroll
+    for (int j = 0; j < JP; ++j) {
+        const uint32_t gi = (uint32_t)min(lo + lane + 64 * j, clast) >> gshift;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            sr[j][r] = __builtin_amdgcn_raw_buffer_load_b16(sc_r, gi * 2u, lr[r] * (uint32_t)G * 2u, 0);
+            zr[j][r] = __builtin_amdgcn_raw_buffer_load_b8(zp_r, gi >> 1, lr[r] * (uint32_t)ZB, 0);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4_t w[JP][R];
+#pragma unroll
+    for (int j = 0; j < JP; ++j) {
+        const uint32_t coff = (uint32_t)min(lo + lane + 64 * j, clast) * 16u;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            w[j][r] = __builtin_amdgcn_raw_buffer_load_b128(wq_r, coff, lr[r] * (uint32_t)RB, kNonTemporal);
+    }
+
+    // x to its integer form in LDS; chunks past the first 128 are loaded here.
+    store_int_chunk(xr, half, hc < C, xrec + hc * kIW);
+    if (MULTI)
+    for (int cb = 128; cb < C; cb += 128) {
+        const int c = cb + hc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            xr[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                x_r, (uint32_t)(c * 32 + half * 16 + 4 * i) * 4u, 0, 0));
+        store_int_chunk(xr, half, c < C, xrec + c * kIW);
+    }
+    __syncthreads();
+
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int j = 0; j < JP; ++j) {
+        const int c = lo + lane + 64 * j;
+        if (c < hi) {
+            const uint32_t *rec = xrec + c * kIW;
+            u32x4_t D[6];
+#pragma unroll
+            for (int d = 0; d < 6; ++d) D[d] = *reinterpret_cast<const u32x4_t *>(rec + 4 * d);
+            const u32x4_t tail = *reinterpret_cast<const u32x4_t *>(rec + 24);
+            const int sxl = (int)tail.x;
+            const int sxh = (int)tail.y;
+            const uint32_t scale_bits = tail.z;   // copied out before the bit cast
+            const float cscale = __builtin_bit_cast(float, scale_bits);
+            const uint32_t zsh = (((uint32_t)c >> gshift) & 1u) << 2;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                if (r < nrows) {
+                    // (8 - z) * SX enters as (8 - z) * SXlow in digit 0 and
+                    // (8 - z) * SXhigh in digit 3 (weight 16^3 = 2^12).
+                    const int nz = 8 - (int)__builtin_amdgcn_ubfe(zr[j][r], zsh, 4);
+                    int a[6];
+                    const uint32_t c0 = w[j][r].x ^ magic8;
+#pragma unroll
+                    for (int d = 0; d < 6; ++d) {
+                        if (d == 0) a[d] = __builtin_amdgcn_sdot8((int)c0, (int)D[d].x, __mul24(nz, sxl), false);
+                        else if (d == 3) a[d] = __builtin_amdgcn_sdot8((int)c0, (int)D[d].x, __mul24(nz, sxh), false);
+                        else asm("v_dot8_i32_i4 %0, %1, %2, 0" : "=v"(a[d]) : "v"(c0), "v"(D[d].x));
+                    }
+#pragma unroll
+                    for (int wd = 1; wd < 4; ++wd) {
+                        const uint32_t cw = (wd == 1 ? w[j][r].y : wd == 2 ? w[j][r].z : w[j][r].w) ^ magic8;
+#pragma unroll
+                        for (int d = 0; d < 6; ++d) {
+                            const uint32_t dw = wd == 1 ? D[d].y : wd == 2 ? D[d].z : D[d].w;
+                            a[d] = __builtin_amdgcn_sdot8((int)cw, (int)dw, a[d], false);
+                        }
+                    }
+                    uint32_t tu = (uint32_t)a[5];
+#pragma unroll
+                    for (int d = 4; d >= 0; --d) tu = (tu << 4) + (uint32_t)a[d];   // mod 2^32; the sum fits int32
+                    const int t = (int)tu;
+                    const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sr[j][r]);
+                    acc[r] = __builtin_fmaf(s, (float)t * cscale, acc[r]);
+                }
+            }
+        }
+    }
+
+    constexpr int NQ = (R + 3) / 4;
+    float out[NQ];
+    q4::wave_reduce_rows<R>(acc, out);
+    const int h = lane >> 4;
+    const bool writer = (lane & 15) == 0 && (R >= 4 || (h & (R == 2 ? 1 : 3)) == 0);
+    if (S == 1) {
+        if (writer) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const int rr = q4::reduced_row<R>(q, h);
+                if (rr < nrows) y[gstart + rr] = out[q];
+            }
+        }
+        return;
+    }
+    if (writer) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) comb[wave * R + q4::reduced_row<R>(q, h)] = out[q];
+    }
+    __syncthreads();
+    if (ks == 0 && writer) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int rr = q4::reduced_row<R>(q, h);
+            if (rr < nrows) {
+                float v = out[q];
+                for (int t = 1; t < S; ++t) v += comb[(wave + t) * R + rr];
+                y[gstart + rr] = v;
+            }
+        }
+    }
+}
+
 struct Geometry {
     int M, LPR, JP, S, seg_chunks, segments, grid, rows_per_wave;
+    bool integer;   // the exact integer path for one activation row
+    int rpg;        // integer path: rows per workgroup
 };
+
+constexpr int kCUs = 256;   // compute units of an MI355X
+
+// The integer path serves one activation row when every lane owns whole
+// chunks (LPR = 64) and x fits the LDS budget in one piece.  Its K-split is
+// raised until a lane holds at most 3 chunk positions.  Rows are dealt to
+// workgroups so that, beyond one workgroup per CU, every CU gets the same
+// number of workgroups (4 x 3.5 rows per wavefront rather than 3.5 x 4).
+void plan_integer(Geometry &p, int N, int K) {
+    const int C = K / 32;
+    if (p.M != 1 || p.LPR != 64) return;
+    int S = p.S;
+    while (S < kWaves && (C + S - 1) / S > 3 * 64) S *= 2;
+    const int part = (C + S - 1) / S;
+    const int JP = (part + 63) / 64;
+    if (JP > 3 || (size_t)C * kIW * 4 + (size_t)kWaves * row_slots(1) * 4 > (size_t)kLdsBytes) return;
+    const int R = row_slots(1);
+    const int groups_per_wg = kWaves / S;
+    const long groups = ((long)N + R - 1) / R;
+    long grid = (groups + groups_per_wg - 1) / groups_per_wg;
+    if (grid > kCUs) grid = (grid + kCUs - 1) / kCUs * kCUs;
+    p.integer = true;
+    p.S = S;
+    p.JP = JP;
+    p.grid = (int)grid;
+    p.rpg = (int)((N + grid - 1) / grid);
+    p.rows_per_wave = R;
+    p.seg_chunks = C;
+    p.segments = 1;
+}
 
 // Chooses the launch geometry for a validated shape.
 Geometry plan(int M, int N, int K, int g) {
@@ -409,6 +708,8 @@ Geometry plan(int M, int N, int K, int g) {
     p.segments = (C + p.seg_chunks - 1) / p.seg_chunks;
     const long rows_per_wg = (long)p.rows_per_wave * (kWaves / p.S);
     p.grid = (int)((N + rows_per_wg - 1) / rows_per_wg);
+    p.rpg = (int)std::min<long>(rows_per_wg, N);
+    plan_integer(p, N, K);
     return p;
 }
 
@@ -422,6 +723,7 @@ int validate(int M, int N, int K, int g) {
 // LDS bytes a launch needs: the x segment plus, with a K-split, one partial
 // sum per (wavefront, row, m).
 size_t lds_bytes(const Geometry &p) {
+    if (p.integer) return (size_t)p.seg_chunks * kIW * 4 + (p.S > 1 ? (size_t)kWaves * p.rows_per_wave * 4 : 0);
     size_t b = (size_t)p.M * p.seg_chunks * kXStride * sizeof(float);
     if (p.S > 1) b += (size_t)kWaves * p.rows_per_wave * p.M * sizeof(float);
     return b;
@@ -441,6 +743,32 @@ void dispatch_jp(const Geometry &p, const float *x, const uint8_t *wq, const uin
     case 1: launch<M, LPR, 1>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
     case 2: launch<M, LPR, 2>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
     default: launch<M, LPR, 4>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
+    }
+}
+
+template <int JP, int S, bool MULTI>
+void launch_integer(const Geometry &p, const float *x, const uint8_t *wq, const uint16_t *scales,
+                    const uint8_t *zeros, float *y, int N, int K, int gshift, hipStream_t st) {
+    hipLaunchKernelGGL((gemv_q4_int_kernel<JP, row_slots(1), S, MULTI>), dim3(p.grid), dim3(kBlock),
+                       lds_bytes(p), st, x, wq, scales, zeros, y, N, K, gshift, p.rpg);
+}
+
+template <int S>
+void dispatch_integer(const Geometry &p, const float *x, const uint8_t *wq, const uint16_t *scales,
+                      const uint8_t *zeros, float *y, int N, int K, int gshift, hipStream_t st) {
+    const bool multi = K / 32 > 128;
+    switch (p.JP) {
+    case 1:
+        if (multi) launch_integer<1, S, true>(p, x, wq, scales, zeros, y, N, K, gshift, st);
+        else launch_integer<1, S, false>(p, x, wq, scales, zeros, y, N, K, gshift, st);
+        break;
+    case 2:
+        if (multi) launch_integer<2, S, true>(p, x, wq, scales, zeros, y, N, K, gshift, st);
+        else launch_integer<2, S, false>(p, x, wq, scales, zeros, y, N, K, gshift, st);
+        break;
+    default:
+        launch_integer<3, S, true>(p, x, wq, scales, zeros, y, N, K, gshift, st);   // JP = 3 needs C > 128
+        break;
     }
 }
 
@@ -471,6 +799,12 @@ extern "C" int gemv_q4_geometry(int M, int N, int K, int group_size, int *grid, 
     return Q4_OK;
 }
 
+extern "C" int gemv_q4_path(int M, int N, int K, int group_size) {
+    const int v = validate(M, N, K, group_size);
+    if (v != Q4_OK) return v;
+    return plan(M, N, K, group_size).integer ? Q4_PATH_INTEGER : Q4_PATH_FMA;
+}
+
 extern "C" int gemv_q4(const float *x, const uint8_t *wq, const uint16_t *scales,
                        const uint8_t *zeros, float *y, int M, int N, int K, int group_size,
                        void *stream) {
@@ -486,6 +820,14 @@ extern "C" int gemv_q4(const float *x, const uint8_t *wq, const uint16_t *scales
     const Geometry p = plan(M, N, K, group_size);
     const int gshift = group_size == 32 ? 0 : 2;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (p.integer) {
+        switch (p.S) {
+        case 1: dispatch_integer<1>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
+        case 2: dispatch_integer<2>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
+        default: dispatch_integer<4>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
+        }
+        return q4::launch_status();
+    }
     switch (M) {
     case 1: dispatch_lpr<1>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
     case 2: dispatch_lpr<2>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;

@@ -116,13 +116,42 @@ def test_geometry_covers_every_row(shape):
     assert lpr in (16, 32, 64) and S in (1, 2, 4) and geo["block"] == 256
     waves = geo["block"] // 64
     rows_per_wg = geo["rows_per_wave"] * waves // S
-    assert geo["grid"] * rows_per_wg >= shape.N > (geo["grid"] - 1) * rows_per_wg
     C = shape.K // 32
-    seg = -(-C // geo["segments"])
-    # x segment fits the 64 KiB LDS budget
-    assert shape.M * seg * 128 <= 64 * 1024
+    if q4.gemv_q4_path(shape.M, shape.N, shape.K, shape.g) == q4.Q4_PATH_INTEGER:
+        # each workgroup owns ceil(N / grid) rows, at most rows_per_wave per row group
+        rpg = -(-shape.N // geo["grid"])
+        assert rpg <= rows_per_wg and geo["grid"] * rpg >= shape.N > (geo["grid"] - 1) * rpg
+        assert geo["segments"] == 1 and C * 112 + waves * geo["rows_per_wave"] * 4 <= 64 * 1024
+        # a lane holds at most 3 chunk positions of its K slice
+        assert -(-C // S) <= 3 * 64
+    else:
+        assert geo["grid"] * rows_per_wg >= shape.N > (geo["grid"] - 1) * rows_per_wg
+        seg = -(-C // geo["segments"])
+        # x segment fits the 64 KiB LDS budget
+        assert shape.M * seg * 128 <= 64 * 1024
+
+
+PATHS = [
+    # M, N, K, g, path: one activation row with more than 32 chunks per row takes the integer path
+    (1, 14336, 4096, 128, 1), (1, 4096, 14336, 128, 1), (1, 65, 2048, 128, 1),
+    (1, 1, 18688, 128, 1), (1, 4, 18816, 128, 0), (1, 896, 896, 32, 0), (1, 151936, 896, 32, 0),
+    (1, 63, 2016, 32, 1), (1, 7, 1024, 32, 0), (2, 14336, 4096, 128, 0), (8, 4096, 14336, 128, 0),
+]
+
+
+@pytest.mark.parametrize("M,N,K,g,path", PATHS, ids=[f"M{a}N{b}K{c}g{d}" for a, b, c, d, _ in PATHS])
+def test_arithmetic_path(M, N, K, g, path):
+    assert q4.gemv_q4_path(M, N, K, g) == path
+
+
+def test_integer_geometry_balances_cus():
+    """14336 rows at M = 1: 1024 workgroups of 14 rows (4 per CU), not 896 of 16."""
+    geo = q4.gemv_q4_geometry(1, 14336, 4096, 128)
+    assert geo["grid"] == 1024 and geo["ksplit"] == 1
 
 
 def test_geometry_rejects_bad_shapes():
     with pytest.raises(q4.Q4Error):
         q4.gemv_q4_geometry(1, 8, 100, 32)
+    with pytest.raises(q4.Q4Error):
+        q4.gemv_q4_path(1, 8, 100, 32)

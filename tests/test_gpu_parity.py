@@ -154,6 +154,72 @@ def test_gemv_q4_q_equals_z_is_exactly_zero():
     assert np.all(y == 0.0)
 
 
+@pytest.mark.parametrize("N,K", [(300, 4096), (77, 14336), (5, 2048)])
+def test_gemv_q4_integer_path_q_equals_z_is_exactly_zero(N, K):
+    """One activation row takes the integer path; q == z must still give exactly 0."""
+    g = 128
+    assert q4.gemv_q4_path(1, N, K, g) == q4.Q4_PATH_INTEGER
+    d = wl.make_q4_problem(6, wl.Q4Shape(1, N, K, g, 0.002, 0.01))
+    z = np.stack([d["zeros"] & 15, d["zeros"] >> 4], -1).reshape(N, -1)[:, :K // g]
+    codes = np.repeat(z, g, axis=1).astype(np.uint8)
+    d["wq"] = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    y = run_q4(dev(d), g)
+    assert np.all(y == 0.0)
+
+
+@pytest.mark.parametrize("N,K", [(257, 4096), (96, 14336), (33, 1056)])
+def test_gemv_q4_wide_dynamic_range_x(N, K):
+    """x magnitudes spread over ten decades inside every 32-value chunk (the
+    integer path rounds each chunk to 23 bits of its largest |x|)."""
+    g = 128 if K % 128 == 0 else 32
+    d = wl.make_q4_problem(12, wl.Q4Shape(1, N, K, g, 0.002, 0.02))
+    rng = np.random.default_rng(12)
+    d["x"] = (d["x"] * 10.0 ** rng.uniform(-6, 4, size=d["x"].shape)).astype(np.float32)
+    y = run_q4(dev(d), g)
+    y_ref, b = oracle.gemv_q4(d["x"], d["wq"], d["scales"], d["zeros"], g)
+    assert_within(y, y_ref, b, f"wide-range x N{N} K{K}")
+
+
+@pytest.mark.parametrize("N,K", [(129, 4096), (40, 2048)])
+def test_gemv_q4_integer_path_x_rounding_bound(N, K):
+    """The integer path's documented bound on inputs the plain bound does not
+    cover: in every 32-value chunk the one large x meets q == z, so only the
+    small x (2^14 to 2^15 times smaller) carry weight.  Each output must stay
+    within the plain bound plus 2^-22 * max|x over the chunk| * |w_k| per k."""
+    g = 128
+    assert q4.gemv_q4_path(1, N, K, g) == q4.Q4_PATH_INTEGER
+    d = wl.make_q4_problem(14, wl.Q4Shape(1, N, K, g, 0.002, 0.01))
+    rng = np.random.default_rng(14)
+    x = rng.uniform(0.5, 1.0, size=(1, K)) * rng.choice([-1.0, 1.0], size=(1, K))
+    x[:, 0::32] = 2.0 ** 14
+    d["x"] = x.astype(np.float32)
+    codes = np.stack([d["wq"] & 15, d["wq"] >> 4], -1).reshape(N, K)
+    z = np.stack([d["zeros"] & 15, d["zeros"] >> 4], -1).reshape(N, -1)[:, :K // g]
+    codes[:, 0::32] = np.repeat(z, g // 32, axis=1)
+    d["wq"] = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    y = run_q4(dev(d), g)
+    y_ref, b = oracle.gemv_q4(d["x"], d["wq"], d["scales"], d["zeros"], g)
+    w, _ = oracle.dequant(d["wq"], d["scales"], d["zeros"], K, g)
+    chunk_max = np.repeat(np.abs(d["x"].astype(np.float64)).reshape(-1, 32).max(1), 32)
+    extra = 2.0 ** -22 * (np.abs(w.astype(np.float64)) @ chunk_max)
+    err = np.abs(y[0].astype(np.float64) - y_ref[0])
+    assert np.all(err <= oracle.gemv_tolerance(b)[0] + extra), np.max(err / (oracle.gemv_tolerance(b)[0] + extra))
+
+
+@pytest.mark.parametrize("M,K", [(1, 4096), (1, 896), (3, 4096)])
+def test_gemv_q4_nan_in_x_propagates(M, K):
+    N, g = 64, 128
+    d = wl.make_q4_problem(13, wl.Q4Shape(M, N, K, g, 0.002, 0.02))
+    d["x"][:, 77] = np.nan
+    y = run_q4(dev(d), g)
+    assert np.isnan(y).all()
+
+
+def test_stream_shape_takes_integer_path():
+    s = wl.STREAM_SHAPE
+    assert q4.gemv_q4_path(s.M, s.N, s.K, s.g) == q4.Q4_PATH_INTEGER
+
+
 def test_gemv_q4_linearity_and_rows():
     """Doubling x doubles y exactly; row m of an M=8 call matches M=1 on x[m]."""
     s = wl.Q4Shape(8, 1234, 4096, 128, 0.002, 0.01)
