@@ -385,6 +385,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
 // the group scale, accumulates into the row's fp32 sum.
 
 constexpr int kIW = 28;   // LDS dwords per chunk: digit d of word w at 4d+w, then SX low/high, 2^(e-22)
+constexpr int kIntVPT = 16;                         // x values one thread converts
+constexpr int kIntTPC = 32 / kIntVPT;               // threads per chunk of x
+constexpr int kIntWaveChunks = q4::kWave / kIntTPC; // chunks of x one wavefront converts per pass
 
 // 8x8 transpose of 4-bit fields: on return nibble p of a[l] is nibble l of
 // the input a[p].  Three butterfly stages: nibbles between neighbouring
@@ -411,45 +414,50 @@ __device__ __forceinline__ void transpose_nibbles(uint32_t (&a)[8]) {
 }
 
 // Converts one chunk of x to its LDS record.  The chunk's 32 values are held
-// by the lane pair (2i, 2i+1), 16 each in order; `half` is lane & 1.  Every
-// lane of the wavefront must call it (the pair exchanges partial results by
-// DPP); only lanes with `store` set write the record.
-__device__ __forceinline__ void store_int_chunk(const f32x4_t (&xr)[4], int half, bool store,
+// by kIntTPC consecutive lanes, kIntVPT each in order; `part` is the lane's
+// index among them.  Every lane of the wavefront must call it (the lanes of a
+// chunk exchange partial results by DPP); only lanes with `store` set write.
+__device__ __forceinline__ void store_int_chunk(const f32x4_t (&xr)[kIntVPT / 4], int part, bool store,
                                                 uint32_t *rec) {
-    float v[16];
+    constexpr int V = kIntVPT;
+    float v[V];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < V / 4; ++i) {
         v[4 * i] = xr[i].x; v[4 * i + 1] = xr[i].y; v[4 * i + 2] = xr[i].z; v[4 * i + 3] = xr[i].w;
     }
     // NaN-propagating maximum (v_maximum3_f32), so a NaN anywhere reaches m
     float m = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) m = __builtin_elementwise_maximum(m, __builtin_fabsf(v[i]));
-    // quad_perm [1,0,3,2]: each lane reads its pair partner
+    for (int i = 0; i < V; ++i) m = __builtin_elementwise_maximum(m, __builtin_fabsf(v[i]));
+    // quad_perm [1,0,3,2], then [2,3,0,1]: the maximum over the chunk's lanes
     m = __builtin_elementwise_maximum(
         m, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, m), 0xB1, 0xF, 0xF, false)));
+    if (kIntTPC == 4)
+        m = __builtin_elementwise_maximum(
+            m, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, m), 0x4E, 0xF, 0xF, false)));
     const int sh = 22 - __builtin_amdgcn_frexp_expf(m);   // |x| * 2^sh < 2^22 (m == 0: sh = 22)
-    uint32_t dg[16];
+    uint32_t dg[V];
     uint32_t sx = 0;                                       // sum of X, two's complement
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < V; ++i) {
         // adding 1.5 * 2^23 rounds to the nearest integer and leaves it in the low mantissa bits
         const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_amdgcn_ldexpf(v[i], sh) + 12582912.0f);
         sx += b - 0x4B400000u;
         dg[i] = (b + (0x888888u - 0x4B400000u)) ^ 0x888888u;
     }
     sx += (uint32_t)__builtin_amdgcn_mov_dpp((int)sx, 0xB1, 0xF, 0xF, false);
+    if (kIntTPC == 4) sx += (uint32_t)__builtin_amdgcn_mov_dpp((int)sx, 0x4E, 0xF, 0xF, false);
     if (!store) return;
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
+    for (int w = 0; w < V / 8; ++w) {
         uint32_t a[8];
 #pragma unroll
         for (int p = 0; p < 8; ++p) a[p] = dg[8 * w + p];
         transpose_nibbles(a);
 #pragma unroll
-        for (int d = 0; d < 6; ++d) rec[4 * d + 2 * half + w] = a[d];
+        for (int d = 0; d < 6; ++d) rec[4 * d + (V / 8) * part + w] = a[d];
     }
-    if (half == 0) {
+    if (part == 0) {
         // a chunk holding Inf or NaN gets a NaN scale, so its rows come out NaN
         const float scale = m <= 3.4028235e38f ? __builtin_amdgcn_ldexpf(1.0f, -sh) : m - m;
         rec[24] = sx & 0xFFFu;
@@ -458,42 +466,47 @@ __device__ __forceinline__ void store_int_chunk(const f32x4_t (&xr)[4], int half
     }
 }
 
-// JP: chunk positions per lane (a lane's chunks are 64 apart).  R: row slots
-// per wavefront.  A workgroup owns rpg consecutive rows, split as evenly as
-// possible over kWaves / S row groups; the S wavefronts of a row group split
-// its K range and meet in LDS.  MULTI: x has more than 128 chunks, so its
-// conversion takes several passes of the workgroup.  S and MULTI are template
-// parameters so that the common case (S = 1, one pass) carries no division
-// and no unused path.
-template <int JP, int R, int S, bool MULTI>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) void gemv_q4_int_kernel(
+// W: wavefronts per workgroup.  JP: chunk positions per lane (a lane's chunks
+// are 64 apart).  R: row slots per wavefront.  A workgroup owns rpg
+// consecutive rows, split as evenly as possible over W / S row groups; the S
+// wavefronts of a row group split its K range and meet in LDS.  MULTI: x has
+// more chunks than one pass of the workgroup converts.  S and MULTI are
+// template parameters so that the common case (S = 1, one pass) carries no
+// division and no unused path.
+template <int W, int JP, int R, int S, bool MULTI>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) void gemv_q4_int_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ wq,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
     float *__restrict__ y, int N, int K, int gshift, int rpg) {
     extern __shared__ uint32_t ilds[];
     const int tid = threadIdx.x;
-    // x first, before any address arithmetic: the workgroup cannot start
-    // computing until x has landed, and every load issued later on this CU
-    // returns after it.  Lane pair (2i, 2i+1) loads chunk i, 16 values each;
-    // reads past K return 0.
-    const int hc = tid >> 1, half = tid & 1;
+    // x first, before any address arithmetic: a CU returns loads in the
+    // order they were issued, so x issued later would wait behind weight
+    // loads.  Lane pair (2i, 2i+1) loads chunk i, 16 values each; reads past K
+    // return 0.  Wavefronts whose chunks all lie past the end of x (the
+    // non-stagers) skip the conversion.
+    constexpr int kPass = W * kIntWaveChunks;          // chunks converted per workgroup pass
+    const int C = K >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool stager = wave * kIntWaveChunks < C;
+    const int hc = tid / kIntTPC, xpart = tid % kIntTPC;
     const __amdgpu_buffer_rsrc_t x_r = raw_rsrc(x, (uint32_t)K * 4u);
-    f32x4_t xr[4];
+    f32x4_t xr[kIntVPT / 4];
+    if (stager) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        xr[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-            x_r, (uint32_t)(hc * 32 + half * 16 + 4 * i) * 4u, 0, 0));
+        for (int i = 0; i < kIntVPT / 4; ++i)
+            xr[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                x_r, (uint32_t)(hc * 32 + xpart * kIntVPT + 4 * i) * 4u, 0, 0));
+    }
     __builtin_amdgcn_sched_barrier(0);
 
-    const int C = K >> 5;
     const int G = K >> (gshift + 5);
     const int ZB = (G + 1) >> 1;
     const int RB = K >> 1;
     uint32_t *xrec = ilds;                                           // [C][kIW]
-    float *comb = reinterpret_cast<float *>(ilds + C * kIW);         // [kWaves][R]
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    float *comb = reinterpret_cast<float *>(ilds + C * kIW);         // [W][R]
     const int lane = tid & 63;
-    const int NG = kWaves / S;                 // row groups per workgroup
+    const int NG = W / S;                      // row groups per workgroup
     const int rg = wave / S;
     const int ks = wave - rg * S;
     const int gq = rpg / NG, grem = rpg - gq * NG;
@@ -515,7 +528,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
 #pragma unroll
     for (int r = 0; r < R; ++r) lr[r] = (uint32_t)min(r, max(nrows, 1) - 1);
 
-    // Group metadata, then the codes in the order they are consumed.
+    // With 8 or 16 wavefronts the stagers convert the first pass of x before
+    // issuing their own weight loads, so that the x loads of every workgroup
+    // on a CU sit ahead of most weight traffic while the non-stagers' loads
+    // keep the stream busy.  With 4 (small shapes, where every wavefront
+    // stages and the kernel is latency-bound) the weights go first.  Then
+    // group metadata, then the codes in the order they are consumed.
+    constexpr bool kStageFirst = W >= 8;
+    if (kStageFirst && stager) store_int_chunk(xr, xpart, hc < C, xrec + hc * kIW);
+    __builtin_amdgcn_sched_barrier(0);
     uint32_t sr[JP][R], zr[JP][R];
 #pragma unroll
     for (int j = 0; j < JP; ++j) {
@@ -536,16 +557,17 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
             w[j][r] = __builtin_amdgcn_raw_buffer_load_b128(wq_r, coff, lr[r] * (uint32_t)RB, kNonTemporal);
     }
 
-    // x to its integer form in LDS; chunks past the first 128 are loaded here.
-    store_int_chunk(xr, half, hc < C, xrec + hc * kIW);
+    // Chunks of x past the first pass are loaded and converted here.
+    if (!kStageFirst && stager) store_int_chunk(xr, xpart, hc < C, xrec + hc * kIW);
     if (MULTI)
-    for (int cb = 128; cb < C; cb += 128) {
+    for (int cb = kPass; cb < C; cb += kPass) {
+        if (cb + wave * kIntWaveChunks >= C) break;
         const int c = cb + hc;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kIntVPT / 4; ++i)
             xr[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                x_r, (uint32_t)(c * 32 + half * 16 + 4 * i) * 4u, 0, 0));
-        store_int_chunk(xr, half, c < C, xrec + c * kIW);
+                x_r, (uint32_t)(c * 32 + xpart * kIntVPT + 4 * i) * 4u, 0, 0));
+        store_int_chunk(xr, xpart, c < C, xrec + c * kIW);
     }
     __syncthreads();
 
@@ -637,29 +659,38 @@ struct Geometry {
     int M, LPR, JP, S, seg_chunks, segments, grid, rows_per_wave;
     bool integer;   // the exact integer path for one activation row
     int rpg;        // integer path: rows per workgroup
+    int waves;      // wavefronts per workgroup
 };
 
 constexpr int kCUs = 256;   // compute units of an MI355X
 
 // The integer path serves one activation row when every lane owns whole
 // chunks (LPR = 64) and x fits the LDS budget in one piece.  Its K-split is
-// raised until a lane holds at most 3 chunk positions.  Rows are dealt to
-// workgroups so that, beyond one workgroup per CU, every CU gets the same
-// number of workgroups (4 x 3.5 rows per wavefront rather than 3.5 x 4).
+// raised until a lane holds at most 3 chunk positions.  Workgroups have 8
+// wavefronts when that still gives every CU a workgroup (each converts x
+// once, so fewer and larger workgroups convert it less often), 16 with a
+// four-way K-split (a long x, read once per workgroup, would otherwise cost
+// as many bytes as the weights of the workgroup's 8 rows), else 4.  Rows
+// are dealt to workgroups so that, beyond one round of workgroups, every CU
+// gets the same number of them (2 x 8 wavefronts of 3.5 rows rather than
+// 1.75 x 8 of 4).
 void plan_integer(Geometry &p, int N, int K) {
     const int C = K / 32;
     if (p.M != 1 || p.LPR != 64) return;
     int S = p.S;
-    while (S < kWaves && (C + S - 1) / S > 3 * 64) S *= 2;
+    while (S < 4 && (C + S - 1) / S > 3 * 64) S *= 2;
     const int part = (C + S - 1) / S;
     const int JP = (part + 63) / 64;
-    if (JP > 3 || (size_t)C * kIW * 4 + (size_t)kWaves * row_slots(1) * 4 > (size_t)kLdsBytes) return;
     const int R = row_slots(1);
-    const int groups_per_wg = kWaves / S;
     const long groups = ((long)N + R - 1) / R;
+    const long waves = groups * S;
+    const int W = S == 4 && waves >= 16L * kCUs ? 16 : (waves >= 8L * kCUs ? 8 : 4);
+    if (JP > 3 || (size_t)C * kIW * 4 + (size_t)W * R * 4 > (size_t)kLdsBytes) return;
+    const int groups_per_wg = W / S;
     long grid = (groups + groups_per_wg - 1) / groups_per_wg;
-    if (grid > kCUs) grid = (grid + kCUs - 1) / kCUs * kCUs;
+    if (grid * W > (long)kCUs * 4) grid = (grid + kCUs - 1) / kCUs * kCUs;
     p.integer = true;
+    p.waves = W;
     p.S = S;
     p.JP = JP;
     p.grid = (int)grid;
@@ -723,7 +754,7 @@ int validate(int M, int N, int K, int g) {
 // LDS bytes a launch needs: the x segment plus, with a K-split, one partial
 // sum per (wavefront, row, m).
 size_t lds_bytes(const Geometry &p) {
-    if (p.integer) return (size_t)p.seg_chunks * kIW * 4 + (p.S > 1 ? (size_t)kWaves * p.rows_per_wave * 4 : 0);
+    if (p.integer) return (size_t)p.seg_chunks * kIW * 4 + (p.S > 1 ? (size_t)p.waves * p.rows_per_wave * 4 : 0);
     size_t b = (size_t)p.M * p.seg_chunks * kXStride * sizeof(float);
     if (p.S > 1) b += (size_t)kWaves * p.rows_per_wave * p.M * sizeof(float);
     return b;
@@ -746,30 +777,38 @@ void dispatch_jp(const Geometry &p, const float *x, const uint8_t *wq, const uin
     }
 }
 
-template <int JP, int S, bool MULTI>
+template <int W, int JP, int S, bool MULTI>
 void launch_integer(const Geometry &p, const float *x, const uint8_t *wq, const uint16_t *scales,
                     const uint8_t *zeros, float *y, int N, int K, int gshift, hipStream_t st) {
-    hipLaunchKernelGGL((gemv_q4_int_kernel<JP, row_slots(1), S, MULTI>), dim3(p.grid), dim3(kBlock),
+    hipLaunchKernelGGL((gemv_q4_int_kernel<W, JP, row_slots(1), S, MULTI>), dim3(p.grid), dim3(W * 64),
                        lds_bytes(p), st, x, wq, scales, zeros, y, N, K, gshift, p.rpg);
+}
+
+template <int W, int S>
+void dispatch_integer_jp(const Geometry &p, const float *x, const uint8_t *wq, const uint16_t *scales,
+                         const uint8_t *zeros, float *y, int N, int K, int gshift, hipStream_t st) {
+    const bool multi = K / 32 > W * kIntWaveChunks;
+    switch (p.JP) {
+    case 1:
+        if (multi) launch_integer<W, 1, S, true>(p, x, wq, scales, zeros, y, N, K, gshift, st);
+        else launch_integer<W, 1, S, false>(p, x, wq, scales, zeros, y, N, K, gshift, st);
+        break;
+    case 2:
+        if (multi) launch_integer<W, 2, S, true>(p, x, wq, scales, zeros, y, N, K, gshift, st);
+        else launch_integer<W, 2, S, false>(p, x, wq, scales, zeros, y, N, K, gshift, st);
+        break;
+    default:   // a multi-pass kernel also serves a single pass
+        launch_integer<W, 3, S, true>(p, x, wq, scales, zeros, y, N, K, gshift, st);
+        break;
+    }
 }
 
 template <int S>
 void dispatch_integer(const Geometry &p, const float *x, const uint8_t *wq, const uint16_t *scales,
                       const uint8_t *zeros, float *y, int N, int K, int gshift, hipStream_t st) {
-    const bool multi = K / 32 > 128;
-    switch (p.JP) {
-    case 1:
-        if (multi) launch_integer<1, S, true>(p, x, wq, scales, zeros, y, N, K, gshift, st);
-        else launch_integer<1, S, false>(p, x, wq, scales, zeros, y, N, K, gshift, st);
-        break;
-    case 2:
-        if (multi) launch_integer<2, S, true>(p, x, wq, scales, zeros, y, N, K, gshift, st);
-        else launch_integer<2, S, false>(p, x, wq, scales, zeros, y, N, K, gshift, st);
-        break;
-    default:
-        launch_integer<3, S, true>(p, x, wq, scales, zeros, y, N, K, gshift, st);   // JP = 3 needs C > 128
-        break;
-    }
+    if (p.waves == 16) dispatch_integer_jp<16, S>(p, x, wq, scales, zeros, y, N, K, gshift, st);
+    else if (p.waves == 8) dispatch_integer_jp<8, S>(p, x, wq, scales, zeros, y, N, K, gshift, st);
+    else dispatch_integer_jp<4, S>(p, x, wq, scales, zeros, y, N, K, gshift, st);
 }
 
 template <int M>
@@ -791,7 +830,7 @@ extern "C" int gemv_q4_geometry(int M, int N, int K, int group_size, int *grid, 
     if (v != Q4_OK) return v;
     const Geometry p = plan(M, N, K, group_size);
     if (grid) *grid = p.grid;
-    if (block) *block = kBlock;
+    if (block) *block = p.integer ? p.waves * q4::kWave : kBlock;
     if (rows_per_wave) *rows_per_wave = p.rows_per_wave;
     if (lanes_per_row) *lanes_per_row = p.LPR;
     if (ksplit) *ksplit = p.S;

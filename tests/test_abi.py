@@ -113,11 +113,13 @@ SHAPES = ([workloads.SMALL_896, workloads.LM_HEAD, workloads.STREAM_SHAPE]
 def test_geometry_covers_every_row(shape):
     geo = q4.gemv_q4_geometry(shape.M, shape.N, shape.K, shape.g)
     lpr, S = geo["lanes_per_row"], geo["ksplit"]
-    assert lpr in (16, 32, 64) and S in (1, 2, 4) and geo["block"] == 256
+    integer = q4.gemv_q4_path(shape.M, shape.N, shape.K, shape.g) == q4.Q4_PATH_INTEGER
+    assert lpr in (16, 32, 64) and S in (1, 2, 4)
+    assert geo["block"] in ((256, 512, 1024) if integer else (256,))
     waves = geo["block"] // 64
     rows_per_wg = geo["rows_per_wave"] * waves // S
     C = shape.K // 32
-    if q4.gemv_q4_path(shape.M, shape.N, shape.K, shape.g) == q4.Q4_PATH_INTEGER:
+    if integer:
         # each workgroup owns ceil(N / grid) rows, at most rows_per_wave per row group
         rpg = -(-shape.N // geo["grid"])
         assert rpg <= rows_per_wg and geo["grid"] * rpg >= shape.N > (geo["grid"] - 1) * rpg
@@ -145,9 +147,20 @@ def test_arithmetic_path(M, N, K, g, path):
 
 
 def test_integer_geometry_balances_cus():
-    """14336 rows at M = 1: 1024 workgroups of 14 rows (4 per CU), not 896 of 16."""
+    """14336 rows at M = 1: 512 workgroups of 8 wavefronts and 28 rows (2 per
+    CU), not 448 of 32; the 14336 -> 4096 projection splits K four ways and
+    takes one 16-wavefront workgroup of 16 rows per CU."""
     geo = q4.gemv_q4_geometry(1, 14336, 4096, 128)
-    assert geo["grid"] == 1024 and geo["ksplit"] == 1
+    assert geo["grid"] == 512 and geo["block"] == 512 and geo["ksplit"] == 1
+    geo = q4.gemv_q4_geometry(1, 4096, 14336, 128)
+    assert geo["grid"] == 256 and geo["block"] == 1024 and geo["ksplit"] == 4
+
+
+@pytest.mark.parametrize("N,K", [(896, 4864), (2048, 2048), (65, 2048)])
+def test_integer_geometry_small_n_keeps_small_workgroups(N, K):
+    """Too few rows to give every CU an 8-wavefront workgroup: 4 wavefronts."""
+    geo = q4.gemv_q4_geometry(1, N, K, 128 if K % 128 == 0 else 32)
+    assert geo["block"] == 256
 
 
 def test_geometry_rejects_bad_shapes():
