@@ -60,12 +60,14 @@ enum q4_status {
  *   - fused multiply-add: (q - z) formed exactly in binary16, multiplied by
  *     the fp32 x and accumulated in fp32, the group scale applied per
  *     32-code chunk;
- *   - integer (M == 1, 1024 < K <= 18688): every chunk of 32 x values
- *     (x[32c .. 32c+31]) is rounded to integers X = round(x * 2^(22-e)),
+ *   - integer (K > 1024; M == 1 up to K = 18688, 2 to 4 rows while their x
+ *     fits one LDS segment, 5 to 8 rows at any K): every chunk of 32 values
+ *     of an x row (x[m][32c .. 32c+31]) is rounded to integers X = round(x * 2^(22-e)),
  *     where 2^(e-1) <= max|x| over the chunk < 2^e, so |X| < 2^22; the sum
  *     of (q - z) * X is formed exactly in int32, converted to fp32 once per
  *     chunk and scaled by 2^(e-22) and the group scale.  q == z gives
- *     exactly 0; a chunk of x holding Inf or NaN makes every output NaN.
+ *     exactly 0; a chunk of x row m holding Inf or NaN makes every output
+ *     of row m NaN.
  * Accuracy against the exact sum y_ref, with w = (q - z) * s:
  *   - fused multiply-add path: |y - y_ref| <= 1e-4 * sum_k |x_k w_k| + 1e-6;
  *   - integer path: the same bound plus the rounding of x, at most

@@ -655,11 +655,235 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     }
 }
 
+// The integer path for 2 to 8 activation rows.  Every row of x is converted
+// as for one row (chunk records of kIW dwords, row m's records after row
+// m-1's); a lane's code word then meets the digit planes of each x row in
+// turn, so the codes are loaded once for all rows.  MP is M rounded up to 2,
+// 4 or 8 (rows past M are skipped by a uniform branch).  x is converted in
+// K segments of seg_chunks chunks when M rows of records would overflow the
+// LDS budget; the weights of a segment are loaded before its x is converted.
+// The S wavefronts of a row group split each segment's chunks and meet in
+// LDS at the end.
+template <int W, int MP, int JP, int R, int S>
+__global__ __launch_bounds__(W * 64) void gemv_q4_intm_kernel(
+    const float *__restrict__ x, const uint8_t *__restrict__ wq,
+    const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
+    float *__restrict__ y, int M, int N, int K, int gshift, int rpg, int seg_chunks) {
+    static_assert(kIntTPC == 2, "two threads convert one chunk");
+    extern __shared__ uint32_t ilds[];
+    const int tid = threadIdx.x;
+    const int C = K >> 5;
+    const int G = K >> (gshift + 5);
+    const int ZB = (G + 1) >> 1;
+    const int RB = K >> 1;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int hc = tid >> 1, half = tid & 1;
+    const int NG = W / S;
+    const int rg = wave / S;
+    const int ks = wave - rg * S;
+    const int gq = rpg / NG, grem = rpg - gq * NG;
+    const int gstart = blockIdx.x * rpg + rg * gq + min(rg, grem);
+    const int nrows = max(0, min(gq + (rg < grem ? 1 : 0), N - gstart));
+    const int rbase = min(gstart, N - 1);
+    const uint32_t magic8 = 0x88888888u;
+    uint32_t *xrec = ilds;                                                 // [M][seg][kIW]
+    float *comb = reinterpret_cast<float *>(ilds + M * seg_chunks * kIW);  // [W][R][MP]
+
+    const __amdgpu_buffer_rsrc_t x_r = raw_rsrc(x, (uint32_t)(M * K) * 4u);
+    const uint32_t rows_left = (uint32_t)(N - rbase);
+    const __amdgpu_buffer_rsrc_t wq_r = raw_rsrc(wq + (size_t)rbase * RB,
+        (uint32_t)std::min<uint64_t>((uint64_t)rows_left * RB, 0xFFFFFFFFull));
+    const __amdgpu_buffer_rsrc_t sc_r = raw_rsrc(scales + (size_t)rbase * G, rows_left * (uint32_t)G * 2u);
+    const __amdgpu_buffer_rsrc_t zp_r = raw_rsrc(zeros + (size_t)rbase * ZB, rows_left * (uint32_t)ZB);
+    uint32_t lr[R];   // row offset of each slot: slots past the group's rows re-read its last row
+#pragma unroll
+    for (int r = 0; r < R; ++r) lr[r] = (uint32_t)min(r, max(nrows, 1) - 1);
+
+    float acc[R][MP];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MP; ++m) acc[r][m] = 0.f;
+
+    for (int seg0 = 0; seg0 < C; seg0 += seg_chunks) {
+        const int segC = min(seg_chunks, C - seg0);
+        const int part = (segC + S - 1) / S;
+        const int lo = seg0 + ks * part;
+        const int hi = min(seg0 + segC, lo + part);
+        const int clast = min(max(lo, hi - 1), seg0 + segC - 1);
+        const int nx = M * segC;                  // chunk records of this segment
+
+        // x first: every pass's loads, then the conversion, then the barrier,
+        // all before any weight load is issued.
+        {
+            f32x4_t xr[2][4];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int p = min(q * W * 32 + hc, nx - 1);
+                const int m = p / segC, c = p - m * segC;
+                const uint32_t off = (uint32_t)(m * K + (seg0 + c) * 32 + half * 16) * 4u;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    xr[q][i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(x_r, off + 16u * i, 0, 0));
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int pb = q * W * 32;
+                if (pb < nx) {
+                    const int p = min(pb + hc, nx - 1);
+                    const int m = p / segC, c = p - m * segC;
+                    store_int_chunk(xr[q], half, pb + hc < nx, xrec + (m * segC + c) * kIW);
+                }
+            }
+            for (int pb = 2 * W * 32; pb < nx; pb += W * 32) {
+                const int p = min(pb + hc, nx - 1);
+                const int m = p / segC, c = p - m * segC;
+                const uint32_t off = (uint32_t)(m * K + (seg0 + c) * 32 + half * 16) * 4u;
+                f32x4_t xq[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    xq[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(x_r, off + 16u * i, 0, 0));
+                store_int_chunk(xq, half, pb + hc < nx, xrec + (m * segC + c) * kIW);
+            }
+        }
+        __syncthreads();
+        uint32_t sr[JP][R], zr[JP][R];
+#pragma unroll
+        for (int j = 0; j < JP; ++j) {
+            const uint32_t gi = (uint32_t)min(lo + lane + 64 * j, clast) >> gshift;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                sr[j][r] = __builtin_amdgcn_raw_buffer_load_b16(sc_r, gi * 2u, lr[r] * (uint32_t)G * 2u, 0);
+                zr[j][r] = __builtin_amdgcn_raw_buffer_load_b8(zp_r, gi >> 1, lr[r] * (uint32_t)ZB, 0);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        u32x4_t w[JP][R];
+#pragma unroll
+        for (int j = 0; j < JP; ++j) {
+            const uint32_t coff = (uint32_t)min(lo + lane + 64 * j, clast) * 16u;
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                w[j][r] = __builtin_amdgcn_raw_buffer_load_b128(wq_r, coff, lr[r] * (uint32_t)RB, kNonTemporal);
+        }
+
+#pragma unroll
+        for (int j = 0; j < JP; ++j) {
+            const int c = lo + lane + 64 * j;
+            if (c < hi) {
+                const uint32_t zsh = (((uint32_t)c >> gshift) & 1u) << 2;
+                int nz[R];
+                float s[R];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    nz[r] = 8 - (int)__builtin_amdgcn_ubfe(zr[j][r], zsh, 4);
+                    s[r] = (float)__builtin_bit_cast(_Float16, (uint16_t)sr[j][r]);
+                    w[j][r] ^= magic8;   // codes as signed nibbles q - 8, once for every x row
+                }
+#pragma unroll
+                for (int m = 0; m < MP; ++m) {
+                    if (m < M) {
+                        const uint32_t *rec = xrec + (m * segC + c - seg0) * kIW;
+                        u32x4_t D[6];
+#pragma unroll
+                        for (int d = 0; d < 6; ++d) D[d] = *reinterpret_cast<const u32x4_t *>(rec + 4 * d);
+                        const u32x4_t tail = *reinterpret_cast<const u32x4_t *>(rec + 24);
+                        const int sxl = (int)tail.x;
+                        const int sxh = (int)tail.y;
+                        const uint32_t scale_bits = tail.z;   // copied out before the bit cast
+                        const float cscale = __builtin_bit_cast(float, scale_bits);
+#pragma unroll
+                        for (int r = 0; r < R; ++r) {
+                            if (r < nrows) {
+                                int a[6];
+                                const uint32_t c0 = w[j][r].x;
+#pragma unroll
+                                for (int d = 0; d < 6; ++d) {
+                                    if (d == 0) a[d] = __builtin_amdgcn_sdot8((int)c0, (int)D[d].x, __mul24(nz[r], sxl), false);
+                                    else if (d == 3) a[d] = __builtin_amdgcn_sdot8((int)c0, (int)D[d].x, __mul24(nz[r], sxh), false);
+                                    else asm("v_dot8_i32_i4 %0, %1, %2, 0" : "=v"(a[d]) : "v"(c0), "v"(D[d].x));
+                                }
+#pragma unroll
+                                for (int wd = 1; wd < 4; ++wd) {
+                                    const uint32_t cw = wd == 1 ? w[j][r].y : wd == 2 ? w[j][r].z : w[j][r].w;
+#pragma unroll
+                                    for (int d = 0; d < 6; ++d) {
+                                        const uint32_t dw = wd == 1 ? D[d].y : wd == 2 ? D[d].z : D[d].w;
+                                        a[d] = __builtin_amdgcn_sdot8((int)cw, (int)dw, a[d], false);
+                                    }
+                                }
+                                uint32_t tu = (uint32_t)a[5];
+#pragma unroll
+                                for (int d = 4; d >= 0; --d) tu = (tu << 4) + (uint32_t)a[d];   // mod 2^32; the sum fits int32
+                                acc[r][m] = __builtin_fmaf(s[r], (float)(int)tu * cscale, acc[r][m]);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        if (seg0 + seg_chunks < C) __syncthreads();   // records fully read before the next segment's
+    }
+
+    constexpr int NQ = (R + 3) / 4;
+    float out[MP][NQ];
+#pragma unroll
+    for (int m = 0; m < MP; ++m) {
+        float v[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) v[r] = acc[r][m];
+        q4::wave_reduce_rows<R>(v, out[m]);
+    }
+    const int h = lane >> 4;
+    const bool writer = (lane & 15) == 0 && (R >= 4 || (h & (R == 2 ? 1 : 3)) == 0);
+    if (S == 1) {
+        if (writer) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const int rr = q4::reduced_row<R>(q, h);
+                if (rr < nrows) {
+#pragma unroll
+                    for (int m = 0; m < MP; ++m)
+                        if (m < M) y[(size_t)m * N + gstart + rr] = out[m][q];
+                }
+            }
+        }
+        return;
+    }
+    if (writer) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int rr = q4::reduced_row<R>(q, h);
+#pragma unroll
+            for (int m = 0; m < MP; ++m) comb[(wave * R + rr) * MP + m] = out[m][q];
+        }
+    }
+    __syncthreads();
+    if (ks == 0 && writer) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int rr = q4::reduced_row<R>(q, h);
+            if (rr < nrows) {
+#pragma unroll
+                for (int m = 0; m < MP; ++m) {
+                    if (m < M) {
+                        float v = out[m][q];
+                        for (int t = 1; t < S; ++t) v += comb[((wave + t) * R + rr) * MP + m];
+                        y[(size_t)m * N + gstart + rr] = v;
+                    }
+                }
+            }
+        }
+    }
+}
+
 struct Geometry {
     int M, LPR, JP, S, seg_chunks, segments, grid, rows_per_wave;
     bool integer;   // the exact integer path for one activation row
     int rpg;        // integer path: rows per workgroup
     int waves;      // wavefronts per workgroup
+    int mp;         // integer path, M > 1: M rounded up to 2, 4 or 8
 };
 
 constexpr int kCUs = 256;   // compute units of an MI355X
@@ -698,6 +922,51 @@ void plan_integer(Geometry &p, int N, int K) {
     p.rows_per_wave = R;
     p.seg_chunks = C;
     p.segments = 1;
+}
+
+constexpr int kLdsMax = 160 * 1024;   // LDS of one CU, and the most one workgroup may use
+
+// The integer path for 2 to 8 activation rows: workgroups of 8 wavefronts, 2
+// per CU (16 and 1 per CU at MP = 8, whose records need more LDS), each
+// owning about N / (workgroups) rows and converting x once.  x is cut into
+// segments of whole lane sweeps when M rows of records exceed the LDS share
+// (only at MP = 8; smaller M takes the multiply-add path then).
+// The K-split S grows while the row groups that remain still hold the
+// workgroup's rows and each split keeps a full lane sweep, and until a lane
+// holds at most 2 chunk positions.
+void plan_integer_m(Geometry &p, int M, int N, int K) {
+    const int C = K / 32;
+    if (M < 2 || p.LPR != 64 || K <= 1024) return;
+    const int MP = M <= 2 ? 2 : (M <= 4 ? 4 : 8);
+    const int W = MP == 8 ? 16 : 8;
+    const int wpc = MP == 8 ? 1 : 2;
+    const int R = 4;
+    const int budget = kLdsMax / wpc - W * R * MP * 4;
+    int seg = std::min(C, budget / (M * kIW * 4));
+    if (seg < C) seg = seg / 64 * 64;
+    // Segmented x costs a barrier and a pipeline drain per segment: below 5
+    // rows the multiply-add path measures faster there.
+    if (seg < 64 || (seg < C && MP <= 4)) return;
+    const long target = (long)kCUs * wpc;
+    const long rpw = std::max<long>((N + target - 1) / target, W);
+    int S = 1;
+    while (S < 4 && (long)(W / (2 * S)) * R >= rpw && seg / (2 * S) >= 64) S *= 2;
+    while (S < 4 && (seg + S - 1) / S > 128) S *= 2;
+    if ((seg + S - 1) / S > 128) seg = 128 * S;
+    const int part = (seg + S - 1) / S;
+    const int JP = (part + 63) / 64;
+    const long cap = (long)(W / S) * R;
+    const long grid = ((long)N + std::min(cap, rpw) - 1) / std::min(cap, rpw);
+    p.integer = true;
+    p.mp = MP;
+    p.waves = W;
+    p.S = S;
+    p.JP = JP;
+    p.grid = (int)grid;
+    p.rpg = (int)((N + grid - 1) / grid);
+    p.rows_per_wave = R;
+    p.seg_chunks = seg;
+    p.segments = (C + seg - 1) / seg;
 }
 
 // Chooses the launch geometry for a validated shape.
@@ -741,6 +1010,7 @@ Geometry plan(int M, int N, int K, int g) {
     p.grid = (int)((N + rows_per_wg - 1) / rows_per_wg);
     p.rpg = (int)std::min<long>(rows_per_wg, N);
     plan_integer(p, N, K);
+    plan_integer_m(p, M, N, K);
     return p;
 }
 
@@ -754,7 +1024,9 @@ int validate(int M, int N, int K, int g) {
 // LDS bytes a launch needs: the x segment plus, with a K-split, one partial
 // sum per (wavefront, row, m).
 size_t lds_bytes(const Geometry &p) {
-    if (p.integer) return (size_t)p.seg_chunks * kIW * 4 + (p.S > 1 ? (size_t)p.waves * p.rows_per_wave * 4 : 0);
+    if (p.integer)
+        return (size_t)p.M * p.seg_chunks * kIW * 4 +
+               (p.S > 1 ? (size_t)p.waves * p.rows_per_wave * std::max(p.mp, 1) * 4 : 0);
     size_t b = (size_t)p.M * p.seg_chunks * kXStride * sizeof(float);
     if (p.S > 1) b += (size_t)kWaves * p.rows_per_wave * p.M * sizeof(float);
     return b;
@@ -811,6 +1083,40 @@ void dispatch_integer(const Geometry &p, const float *x, const uint8_t *wq, cons
     else dispatch_integer_jp<4, S>(p, x, wq, scales, zeros, y, N, K, gshift, st);
 }
 
+template <int W, int MP, int JP, int S>
+void launch_intm(const Geometry &p, const float *x, const uint8_t *wq, const uint16_t *scales,
+                 const uint8_t *zeros, float *y, int M, int N, int K, int gshift, hipStream_t st) {
+    hipLaunchKernelGGL((gemv_q4_intm_kernel<W, MP, JP, 4, S>), dim3(p.grid), dim3(W * 64), lds_bytes(p), st,
+                       x, wq, scales, zeros, y, M, N, K, gshift, p.rpg, p.seg_chunks);
+}
+
+template <int W, int MP>
+void dispatch_intm_mp(const Geometry &p, const float *x, const uint8_t *wq, const uint16_t *scales,
+                      const uint8_t *zeros, float *y, int M, int N, int K, int gshift, hipStream_t st) {
+    if (p.JP == 1) {
+        switch (p.S) {
+        case 1: launch_intm<W, MP, 1, 1>(p, x, wq, scales, zeros, y, M, N, K, gshift, st); break;
+        case 2: launch_intm<W, MP, 1, 2>(p, x, wq, scales, zeros, y, M, N, K, gshift, st); break;
+        default: launch_intm<W, MP, 1, 4>(p, x, wq, scales, zeros, y, M, N, K, gshift, st); break;
+        }
+    } else {
+        switch (p.S) {
+        case 1: launch_intm<W, MP, 2, 1>(p, x, wq, scales, zeros, y, M, N, K, gshift, st); break;
+        case 2: launch_intm<W, MP, 2, 2>(p, x, wq, scales, zeros, y, M, N, K, gshift, st); break;
+        default: launch_intm<W, MP, 2, 4>(p, x, wq, scales, zeros, y, M, N, K, gshift, st); break;
+        }
+    }
+}
+
+void dispatch_intm(const Geometry &p, const float *x, const uint8_t *wq, const uint16_t *scales,
+                   const uint8_t *zeros, float *y, int M, int N, int K, int gshift, hipStream_t st) {
+    switch (p.mp) {
+    case 2: dispatch_intm_mp<8, 2>(p, x, wq, scales, zeros, y, M, N, K, gshift, st); break;
+    case 4: dispatch_intm_mp<8, 4>(p, x, wq, scales, zeros, y, M, N, K, gshift, st); break;
+    default: dispatch_intm_mp<16, 8>(p, x, wq, scales, zeros, y, M, N, K, gshift, st); break;
+    }
+}
+
 template <int M>
 void dispatch_lpr(const Geometry &p, const float *x, const uint8_t *wq, const uint16_t *scales,
                   const uint8_t *zeros, float *y, int N, int K, int gshift, hipStream_t st) {
@@ -859,6 +1165,10 @@ extern "C" int gemv_q4(const float *x, const uint8_t *wq, const uint16_t *scales
     const Geometry p = plan(M, N, K, group_size);
     const int gshift = group_size == 32 ? 0 : 2;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (p.integer && M > 1) {
+        dispatch_intm(p, x, wq, scales, zeros, y, M, N, K, gshift, st);
+        return q4::launch_status();
+    }
     if (p.integer) {
         switch (p.S) {
         case 1: dispatch_integer<1>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;

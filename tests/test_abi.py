@@ -123,9 +123,16 @@ def test_geometry_covers_every_row(shape):
         # each workgroup owns ceil(N / grid) rows, at most rows_per_wave per row group
         rpg = -(-shape.N // geo["grid"])
         assert rpg <= rows_per_wg and geo["grid"] * rpg >= shape.N > (geo["grid"] - 1) * rpg
-        assert geo["segments"] == 1 and C * 112 + waves * geo["rows_per_wave"] * 4 <= 64 * 1024
-        # a lane holds at most 3 chunk positions of its K slice
-        assert -(-C // S) <= 3 * 64
+        seg = -(-C // geo["segments"])
+        if shape.M == 1:
+            assert geo["segments"] == 1 and C * 112 + waves * geo["rows_per_wave"] * 4 <= 64 * 1024
+            # a lane holds at most 3 chunk positions of its K slice
+            assert -(-C // S) <= 3 * 64
+        else:
+            # M rows of 112-byte chunk records per segment, within the CU's LDS
+            mp = 2 if shape.M <= 2 else (4 if shape.M <= 4 else 8)
+            assert shape.M * seg * 112 + waves * geo["rows_per_wave"] * mp * 4 <= 160 * 1024
+            assert -(-seg // S) <= 2 * 64
     else:
         assert geo["grid"] * rows_per_wg >= shape.N > (geo["grid"] - 1) * rows_per_wg
         seg = -(-C // geo["segments"])
@@ -137,7 +144,10 @@ PATHS = [
     # M, N, K, g, path: one activation row with more than 32 chunks per row takes the integer path
     (1, 14336, 4096, 128, 1), (1, 4096, 14336, 128, 1), (1, 65, 2048, 128, 1),
     (1, 1, 18688, 128, 1), (1, 4, 18816, 128, 0), (1, 896, 896, 32, 0), (1, 151936, 896, 32, 0),
-    (1, 63, 2016, 32, 1), (1, 7, 1024, 32, 0), (2, 14336, 4096, 128, 0), (8, 4096, 14336, 128, 0),
+    (1, 63, 2016, 32, 1), (1, 7, 1024, 32, 0), (2, 14336, 4096, 128, 1), (8, 4096, 14336, 128, 1),
+    (4, 896, 896, 32, 0), (2, 64, 1024, 32, 0), (3, 4864, 896, 32, 0), (7, 100, 2048, 128, 1),
+    # x records of 2..4 rows that need segments take the multiply-add path
+    (4, 4096, 14336, 128, 0), (2, 4096, 14336, 128, 0), (2, 300, 8192, 128, 1),
 ]
 
 

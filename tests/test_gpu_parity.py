@@ -167,17 +167,18 @@ def test_gemv_q4_integer_path_q_equals_z_is_exactly_zero(N, K):
     assert np.all(y == 0.0)
 
 
-@pytest.mark.parametrize("N,K", [(257, 4096), (96, 14336), (33, 1056)])
-def test_gemv_q4_wide_dynamic_range_x(N, K):
+@pytest.mark.parametrize("M,N,K", [(1, 257, 4096), (1, 96, 14336), (1, 33, 1056), (4, 129, 4096),
+                                   (8, 40, 14336)])
+def test_gemv_q4_wide_dynamic_range_x(M, N, K):
     """x magnitudes spread over ten decades inside every 32-value chunk (the
     integer path rounds each chunk to 23 bits of its largest |x|)."""
     g = 128 if K % 128 == 0 else 32
-    d = wl.make_q4_problem(12, wl.Q4Shape(1, N, K, g, 0.002, 0.02))
+    d = wl.make_q4_problem(12, wl.Q4Shape(M, N, K, g, 0.002, 0.02))
     rng = np.random.default_rng(12)
     d["x"] = (d["x"] * 10.0 ** rng.uniform(-6, 4, size=d["x"].shape)).astype(np.float32)
     y = run_q4(dev(d), g)
     y_ref, b = oracle.gemv_q4(d["x"], d["wq"], d["scales"], d["zeros"], g)
-    assert_within(y, y_ref, b, f"wide-range x N{N} K{K}")
+    assert_within(y, y_ref, b, f"wide-range x M{M} N{N} K{K}")
 
 
 @pytest.mark.parametrize("N,K", [(129, 4096), (40, 2048)])
