@@ -250,12 +250,21 @@ def run_default(args):
     def probe_pass():
         q4.read_reduce(W["probe"], 4096, partials=W["partials"])
 
+    def swiglu_pass():   # gate = matrix 2i, up = matrix 2i + 1
+        mats = W["mats"]
+        for i in range(wl.STREAM_MATRICES // 2):
+            gm, um = mats[2 * i], mats[2 * i + 1]
+            q4.gemv_q4_swiglu(W["x"], (gm["wq"], gm["scales"], gm["zeros"]),
+                              (um["wq"], um["scales"], um["zeros"]), g, out=W["ys"][i])
+
     graphs = {"gemv_q4": Graph(q4_pass, torch), "gemv_f32": Graph(f32_pass, torch),
-              "read_reduce": Graph(probe_pass, torch)}
-    calls = {"gemv_q4": wl.STREAM_MATRICES, "gemv_f32": wl.STREAM_F32_MATRICES, "read_reduce": 1}
+              "read_reduce": Graph(probe_pass, torch), "gemv_q4_swiglu": Graph(swiglu_pass, torch)}
+    calls = {"gemv_q4": wl.STREAM_MATRICES, "gemv_f32": wl.STREAM_F32_MATRICES, "read_reduce": 1,
+             "gemv_q4_swiglu": wl.STREAM_MATRICES // 2}
     bytes_per_call = {"gemv_q4": wl.q4_weight_bytes(s.N, s.K, s.g),
                       "gemv_f32": wl.f32_weight_bytes(s.N, s.K),
-                      "read_reduce": wl.PROBE_BYTES}
+                      "read_reduce": wl.PROBE_BYTES,
+                      "gemv_q4_swiglu": 2 * wl.q4_weight_bytes(s.N, s.K, s.g)}
 
     # ---- the contract's timed region: W warm-up steps, then exactly K steps
     G = graphs["gemv_q4"]
@@ -284,7 +293,7 @@ def run_default(args):
         iters = [int(v) for v in args.iters.split(",")]
         # n counts gemv launches; one 2 GiB read_reduce streams as much as ~70
         # of them, so its sweep uses n / 16 launches.
-        scale = {"gemv_q4": 1, "gemv_f32": 1, "read_reduce": 16}
+        scale = {"gemv_q4": 1, "gemv_f32": 1, "read_reduce": 16, "gemv_q4_swiglu": 2}
 
         def timer(k, n):
             launches = max(1, n // scale[k])

@@ -84,6 +84,23 @@ int gemv_q4(const float *x, const uint8_t *wq, const uint16_t *scales,
             const uint8_t *zeros, float *y, int M, int N, int K, int group_size,
             void *stream);
 
+/* SwiGLU block of a decoder layer on int4 weights: the gate and up
+ * projections, each a gemv_q4 of the same x, combined as
+ *   y[m, n] = silu(g[m, n]) * u[m, n],   silu(v) = v / (1 + e^-v)
+ * (gerbil "WGSL Kernel Reference", section 9 SiLU for silu, section 12 Mul
+ * for the combine, which the page notes could be fused with the SiLU).
+ * Two launches on the stream: u is written to y, then the gate GEMV combines
+ * in its store, so no separate element-wise pass and no intermediate buffer.
+ * Arguments, rules and the arithmetic path of each projection are those of
+ * gemv_q4 (both matrices [N, K] with the same group_size); y must not overlap
+ * any input.  Each output is within |u| * 1.1 * t_g + |silu(g)| * t_u plus
+ * second-order and rounding terms of the exact value, t_g and t_u being the
+ * gemv_q4 error bounds of the two projections. */
+int gemv_q4_swiglu(const float *x, const uint8_t *wq_gate, const uint16_t *scales_gate,
+                   const uint8_t *zeros_gate, const uint8_t *wq_up, const uint16_t *scales_up,
+                   const uint8_t *zeros_up, float *y, int M, int N, int K, int group_size,
+                   void *stream);
+
 /* Dense fp32 control GEMV, y[M, N] = x[M, K] . w[N, K]^T (cera 0.5.0
  * wgpu_gemv_bench.rs: the f32 kernel kept in the table as the control).
  *   1 <= M <= 8;  N >= 0 (N == 0 launches nothing);  K >= 4, K % 4 == 0.

@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libq4gemv.so")
 Q4_OK, Q4_EINVAL, Q4_ENULL, Q4_EALIGN, Q4_EDEVICE, Q4_ELAUNCH = 0, -1, -2, -3, -4, -5
 
 # Exported C symbols, in the order include/q4gemv.h declares them.
-EXPORTS = ("gemv_q4", "gemv_f32", "dequant_q4", "read_reduce", "write_fill",
+EXPORTS = ("gemv_q4", "gemv_q4_swiglu", "gemv_f32", "dequant_q4", "read_reduce", "write_fill",
            "gemv_q4_geometry", "gemv_q4_path", "q4_strerror", "q4_abi_version")
 
 Q4_PATH_FMA, Q4_PATH_INTEGER = 0, 1
@@ -50,6 +50,7 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     L.gemv_q4.argtypes = [P, P, P, P, P, I, I, I, I, P]
+    L.gemv_q4_swiglu.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, P]
     L.gemv_f32.argtypes = [P, P, P, I, I, I, P]
     L.dequant_q4.argtypes = [P, P, P, P, P, I, I, I, P]
     L.read_reduce.argtypes = [P, Z, P, I, P]
@@ -60,7 +61,7 @@ def lib() -> ctypes.CDLL:
     L.q4_strerror.argtypes = [I]
     L.q4_strerror.restype = ctypes.c_char_p
     L.q4_abi_version.argtypes = []
-    for f in ("gemv_q4", "gemv_f32", "dequant_q4", "read_reduce", "write_fill",
+    for f in ("gemv_q4", "gemv_q4_swiglu", "gemv_f32", "dequant_q4", "read_reduce", "write_fill",
               "gemv_q4_geometry", "gemv_q4_path", "q4_abi_version"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
@@ -97,9 +98,9 @@ def _need(t: torch.Tensor, name: str, dtypes, device=None):
         raise ValueError(f"{name} must be contiguous")
 
 
-def gemv_q4(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
-            group_size: int, out: torch.Tensor | None = None) -> torch.Tensor:
-    """y[M, N] = x[M, K] . dequant(W_q[N, K])^T on the current stream."""
+def _q4_operands(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+                 group_size: int, N: int | None = None):
+    """Checks one int4 matrix against x; returns (M, N, K, g)."""
     _need(x, "x", (torch.float32,))
     dev = x.device
     _need(wq, "wq", (torch.uint8,), dev)
@@ -108,20 +109,45 @@ def gemv_q4(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, zeros: torc
     if x.dim() != 2 or wq.dim() != 2:
         raise ValueError("x must be [M, K] and wq [N, K/2]")
     M, K = x.shape
-    N = wq.shape[0]
+    n = wq.shape[0]
     g = int(group_size)
     G = K // g if g else 0
-    if wq.shape[1] * 2 != K or tuple(scales.shape) != (N, G) or tuple(zeros.shape) != (N, (G + 1) // 2):
+    if (wq.shape[1] * 2 != K or tuple(scales.shape) != (n, G) or tuple(zeros.shape) != (n, (G + 1) // 2)
+            or (N is not None and n != N)):
         raise ValueError(f"shape mismatch: x{tuple(x.shape)} wq{tuple(wq.shape)} "
                          f"scales{tuple(scales.shape)} zeros{tuple(zeros.shape)} g={g}")
+    return M, n, K, g
+
+
+def _out(out: torch.Tensor | None, M: int, N: int, dev: torch.device) -> torch.Tensor:
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=dev)
-    else:
-        _need(out, "out", (torch.float32,), dev)
-        if tuple(out.shape) != (M, N):
-            raise ValueError("out must be [M, N]")
+        return torch.empty((M, N), dtype=torch.float32, device=dev)
+    _need(out, "out", (torch.float32,), dev)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out must be [M, N]")
+    return out
+
+
+def gemv_q4(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+            group_size: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """y[M, N] = x[M, K] . dequant(W_q[N, K])^T on the current stream."""
+    M, N, K, g = _q4_operands(x, wq, scales, zeros, group_size)
+    out = _out(out, M, N, x.device)
     _check("gemv_q4", lib().gemv_q4(_ptr(x), _ptr(wq), _ptr(scales), _ptr(zeros), _ptr(out),
-                                    M, N, K, g, _stream(dev)))
+                                    M, N, K, g, _stream(x.device)))
+    return out
+
+
+def gemv_q4_swiglu(x: torch.Tensor, gate: tuple, up: tuple, group_size: int,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = silu(x . Wg^T) * (x . Wu^T); gate and up are (wq, scales, zeros)."""
+    M, N, K, g = _q4_operands(x, *gate, group_size)
+    _q4_operands(x, *up, group_size, N=N)
+    out = _out(out, M, N, x.device)
+    (wg, sg, zg), (wu, su, zu) = gate, up
+    _check("gemv_q4_swiglu", lib().gemv_q4_swiglu(
+        _ptr(x), _ptr(wg), _ptr(sg), _ptr(zg), _ptr(wu), _ptr(su), _ptr(zu), _ptr(out),
+        M, N, K, g, _stream(x.device)))
     return out
 
 

@@ -103,6 +103,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, uin
 // that is read once.
 constexpr int kNonTemporal = 2;
 
+// Stores one output.  With epi set the GEMV is the gate projection of a
+// SwiGLU block: y already holds the up projection u, and silu(v) * u, with
+// silu(v) = v / (1 + e^-v), replaces it.
+__device__ __forceinline__ void store_y(float *y, size_t i, float v, int epi) {
+    if (epi) v = v / (1.0f + __expf(-v)) * y[i];
+    y[i] = v;
+}
+
 // M: activation rows.  LPR: lanes per output row.  JP: chunk positions per
 // lane per segment (a lane's chunks are LPR apart).  R: row slots per wave.
 //
@@ -112,7 +120,7 @@ template <int M, int LPR, int JP, int R>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) void gemv_q4_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ wq,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
-    float *__restrict__ y, int N, int K, int gshift, int S, int seg_chunks) {
+    float *__restrict__ y, int N, int K, int gshift, int S, int seg_chunks, int epi) {
     constexpr int RG = q4::kWave / LPR;   // rows sharing one load instruction
     constexpr int RPW = R * RG;           // output rows per wavefront
     constexpr int XB = x_batch(M);
@@ -300,7 +308,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
                     const int row = row_first + q4::reduced_row<R>(q, h);
                     if (row < N)
 #pragma unroll
-                        for (int m = 0; m < M; ++m) y[(size_t)m * N + row] = out[m][q];
+                        for (int m = 0; m < M; ++m) store_y(y, (size_t)m * N + row, out[m][q], epi);
                 }
             }
             return;
@@ -322,7 +330,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
                 for (int m = 0; m < M; ++m) {
                     float v = out[m][q];
                     for (int t = 1; t < S; ++t) v += comb[((wave + t) * RPW + rs) * M + m];
-                    if (row < N) y[(size_t)m * N + row] = v;
+                    if (row < N) store_y(y, (size_t)m * N + row, v, epi);
                 }
             }
         }
@@ -339,7 +347,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
                     const int row = row_first + r * RG + rgl;
                     if (row < N)
 #pragma unroll
-                        for (int m = 0; m < M; ++m) y[(size_t)m * N + row] = acc[r][m];
+                        for (int m = 0; m < M; ++m) store_y(y, (size_t)m * N + row, acc[r][m], epi);
                 }
             }
             return;
@@ -359,7 +367,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
                 for (int m = 0; m < M; ++m) {
                     float v = acc[r][m];
                     for (int t = 1; t < S; ++t) v += comb[((wave + t) * RPW + r * RG + rgl) * M + m];
-                    if (row < N) y[(size_t)m * N + row] = v;
+                    if (row < N) store_y(y, (size_t)m * N + row, v, epi);
                 }
             }
         }
@@ -477,7 +485,7 @@ template <int W, int JP, int R, int S, bool MULTI>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) void gemv_q4_int_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ wq,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
-    float *__restrict__ y, int N, int K, int gshift, int rpg) {
+    float *__restrict__ y, int N, int K, int gshift, int rpg, int epi) {
     extern __shared__ uint32_t ilds[];
     const int tid = threadIdx.x;
     // x first, before any address arithmetic: a CU returns loads in the
@@ -632,7 +640,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
                 const int rr = q4::reduced_row<R>(q, h);
-                if (rr < nrows) y[gstart + rr] = out[q];
+                if (rr < nrows) store_y(y, gstart + rr, out[q], epi);
             }
         }
         return;
@@ -649,7 +657,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
             if (rr < nrows) {
                 float v = out[q];
                 for (int t = 1; t < S; ++t) v += comb[(wave + t) * R + rr];
-                y[gstart + rr] = v;
+                store_y(y, gstart + rr, v, epi);
             }
         }
     }
@@ -668,7 +676,7 @@ template <int W, int MP, int JP, int R, int S>
 __global__ __launch_bounds__(W * 64) void gemv_q4_intm_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ wq,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
-    float *__restrict__ y, int M, int N, int K, int gshift, int rpg, int seg_chunks) {
+    float *__restrict__ y, int M, int N, int K, int gshift, int rpg, int seg_chunks, int epi) {
     static_assert(kIntTPC == 2, "two threads convert one chunk");
     extern __shared__ uint32_t ilds[];
     const int tid = threadIdx.x;
@@ -845,7 +853,7 @@ __global__ __launch_bounds__(W * 64) void gemv_q4_intm_kernel(
                 if (rr < nrows) {
 #pragma unroll
                     for (int m = 0; m < MP; ++m)
-                        if (m < M) y[(size_t)m * N + gstart + rr] = out[m][q];
+                        if (m < M) store_y(y, (size_t)m * N + gstart + rr, out[m][q], epi);
                 }
             }
         }
@@ -870,7 +878,7 @@ __global__ __launch_bounds__(W * 64) void gemv_q4_intm_kernel(
                     if (m < M) {
                         float v = out[m][q];
                         for (int t = 1; t < S; ++t) v += comb[((wave + t) * R + rr) * MP + m];
-                        y[(size_t)m * N + gstart + rr] = v;
+                        store_y(y, (size_t)m * N + gstart + rr, v, epi);
                     }
                 }
             }
@@ -884,6 +892,7 @@ struct Geometry {
     int rpg;        // integer path: rows per workgroup
     int waves;      // wavefronts per workgroup
     int mp;         // integer path, M > 1: M rounded up to 2, 4 or 8
+    int epi;        // launch-time: finish a SwiGLU block in the store (see store_y)
 };
 
 constexpr int kCUs = 256;   // compute units of an MI355X
@@ -1036,7 +1045,7 @@ template <int M, int LPR, int JP>
 void launch(const Geometry &p, const float *x, const uint8_t *wq, const uint16_t *scales,
             const uint8_t *zeros, float *y, int N, int K, int gshift, hipStream_t st) {
     hipLaunchKernelGGL((gemv_q4_kernel<M, LPR, JP, row_slots(M)>), dim3(p.grid), dim3(kBlock),
-                       lds_bytes(p), st, x, wq, scales, zeros, y, N, K, gshift, p.S, p.seg_chunks);
+                       lds_bytes(p), st, x, wq, scales, zeros, y, N, K, gshift, p.S, p.seg_chunks, p.epi);
 }
 
 template <int M, int LPR>
@@ -1053,7 +1062,7 @@ template <int W, int JP, int S, bool MULTI>
 void launch_integer(const Geometry &p, const float *x, const uint8_t *wq, const uint16_t *scales,
                     const uint8_t *zeros, float *y, int N, int K, int gshift, hipStream_t st) {
     hipLaunchKernelGGL((gemv_q4_int_kernel<W, JP, row_slots(1), S, MULTI>), dim3(p.grid), dim3(W * 64),
-                       lds_bytes(p), st, x, wq, scales, zeros, y, N, K, gshift, p.rpg);
+                       lds_bytes(p), st, x, wq, scales, zeros, y, N, K, gshift, p.rpg, p.epi);
 }
 
 template <int W, int S>
@@ -1087,7 +1096,7 @@ template <int W, int MP, int JP, int S>
 void launch_intm(const Geometry &p, const float *x, const uint8_t *wq, const uint16_t *scales,
                  const uint8_t *zeros, float *y, int M, int N, int K, int gshift, hipStream_t st) {
     hipLaunchKernelGGL((gemv_q4_intm_kernel<W, MP, JP, 4, S>), dim3(p.grid), dim3(W * 64), lds_bytes(p), st,
-                       x, wq, scales, zeros, y, M, N, K, gshift, p.rpg, p.seg_chunks);
+                       x, wq, scales, zeros, y, M, N, K, gshift, p.rpg, p.seg_chunks, p.epi);
 }
 
 template <int W, int MP>
@@ -1150,19 +1159,13 @@ extern "C" int gemv_q4_path(int M, int N, int K, int group_size) {
     return plan(M, N, K, group_size).integer ? Q4_PATH_INTEGER : Q4_PATH_FMA;
 }
 
-extern "C" int gemv_q4(const float *x, const uint8_t *wq, const uint16_t *scales,
-                       const uint8_t *zeros, float *y, int M, int N, int K, int group_size,
-                       void *stream) {
-    const int v = validate(M, N, K, group_size);
-    if (v != Q4_OK) return v;
-    if (N == 0) return Q4_OK;
-    if (!x || !wq || !scales || !zeros || !y) return Q4_ENULL;
-    if (!q4::aligned(x, 16) || !q4::aligned(wq, 16) || !q4::aligned(scales, 2) ||
-        !q4::aligned(y, 4))
-        return Q4_EALIGN;
-    const int dev = q4::check_device();
-    if (dev != Q4_OK) return dev;
-    const Geometry p = plan(M, N, K, group_size);
+namespace {
+
+// Launches one GEMV of a validated, checked call (see gemv_q4, gemv_q4_swiglu).
+int launch_gemv_q4(const float *x, const uint8_t *wq, const uint16_t *scales, const uint8_t *zeros,
+                   float *y, int M, int N, int K, int group_size, int epi, void *stream) {
+    Geometry p = plan(M, N, K, group_size);
+    p.epi = epi;
     const int gshift = group_size == 32 ? 0 : 2;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (p.integer && M > 1) {
@@ -1188,4 +1191,45 @@ extern "C" int gemv_q4(const float *x, const uint8_t *wq, const uint16_t *scales
     default: dispatch_lpr<8>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
     }
     return q4::launch_status();
+}
+
+// Argument checks shared by the GEMV entry points.
+int check_q4_args(const float *x, const uint8_t *wq, const uint16_t *scales, const uint8_t *zeros,
+                  const float *y) {
+    if (!x || !wq || !scales || !zeros || !y) return Q4_ENULL;
+    if (!q4::aligned(x, 16) || !q4::aligned(wq, 16) || !q4::aligned(scales, 2) || !q4::aligned(y, 4))
+        return Q4_EALIGN;
+    return Q4_OK;
+}
+
+}  // namespace
+
+extern "C" int gemv_q4(const float *x, const uint8_t *wq, const uint16_t *scales,
+                       const uint8_t *zeros, float *y, int M, int N, int K, int group_size,
+                       void *stream) {
+    const int v = validate(M, N, K, group_size);
+    if (v != Q4_OK) return v;
+    if (N == 0) return Q4_OK;
+    const int a = check_q4_args(x, wq, scales, zeros, y);
+    if (a != Q4_OK) return a;
+    const int dev = q4::check_device();
+    if (dev != Q4_OK) return dev;
+    return launch_gemv_q4(x, wq, scales, zeros, y, M, N, K, group_size, 0, stream);
+}
+
+extern "C" int gemv_q4_swiglu(const float *x, const uint8_t *wq_gate, const uint16_t *scales_gate,
+                              const uint8_t *zeros_gate, const uint8_t *wq_up,
+                              const uint16_t *scales_up, const uint8_t *zeros_up, float *y,
+                              int M, int N, int K, int group_size, void *stream) {
+    const int v = validate(M, N, K, group_size);
+    if (v != Q4_OK) return v;
+    if (N == 0) return Q4_OK;
+    int a = check_q4_args(x, wq_gate, scales_gate, zeros_gate, y);
+    if (a == Q4_OK) a = check_q4_args(x, wq_up, scales_up, zeros_up, y);
+    if (a != Q4_OK) return a;
+    const int dev = q4::check_device();
+    if (dev != Q4_OK) return dev;
+    const int r = launch_gemv_q4(x, wq_up, scales_up, zeros_up, y, M, N, K, group_size, 0, stream);
+    if (r != Q4_OK) return r;
+    return launch_gemv_q4(x, wq_gate, scales_gate, zeros_gate, y, M, N, K, group_size, 1, stream);
 }

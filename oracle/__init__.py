@@ -192,3 +192,27 @@ def quantize(w, scales, zeros, g: int):
 def gemv_tolerance(bound: np.ndarray) -> np.ndarray:
     """Allowed |y - y_ref| for a GEMV output: 1e-4 * sum|w x| + 1e-6."""
     return 1e-4 * bound + 1e-6
+
+
+def silu(v) -> np.ndarray:
+    """silu(v) = v / (1 + e^-v) in f64 (gerbil "WGSL Kernel Reference",
+    section 9 SiLU).  e^-v overflows to inf for v < -709, giving -0."""
+    v = np.asarray(v, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return v / (1.0 + np.exp(-v))
+
+
+def swiglu(x, gate, up, g: int, rows=None):
+    """SwiGLU combine of two int4 GEMVs of the same x (section 12 Mul: the
+    combine is silu(gate) * up).  gate and up are (wq, scales, zeros).
+    Returns (y, tol): y = silu(x . Wg^T) * (x . Wu^T) in f64, and the allowed
+    |y_gpu - y| per output, propagated from the two GEMV tolerances t_g, t_u:
+    |silu'| <= 1.1 everywhere, so the error is at most
+    1.1 t_g (|u| + t_u) + |silu(g)| t_u, plus 1e-6 |y| for the rounding of
+    the exponential, division and product in fp32."""
+    gy, gb = gemv_q4(x, *gate, g, rows)
+    uy, ub = gemv_q4(x, *up, g, rows)
+    y = silu(gy) * uy
+    tg, tu = gemv_tolerance(gb), gemv_tolerance(ub)
+    tol = 1.1 * tg * (np.abs(uy) + tu) + np.abs(silu(gy)) * tu + 1e-6 * np.abs(y)
+    return y, tol

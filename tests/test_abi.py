@@ -77,6 +77,18 @@ def test_gemv_q4_pointer_validation(L):
     assert st in (q4.Q4_EDEVICE, q4.Q4_OK, q4.Q4_ELAUNCH) and st != q4.Q4_EALIGN
 
 
+def test_gemv_q4_swiglu_validation(L):
+    f = L.gemv_q4_swiglu
+    assert f(A16, A16, A16, A16, A16, A16, A16, A16, 9, 8, 128, 32, None) == q4.Q4_EINVAL
+    assert f(A16, A16, A16, A16, A16, A16, A16, A16, 1, 8, 100, 32, None) == q4.Q4_EINVAL
+    assert f(A16, A16, A16, A16, A16, A16, A16, A16, 1, 0, 128, 32, None) == q4.Q4_OK
+    assert f(A16, A16, A16, A16, None, A16, A16, A16, 1, 8, 128, 32, None) == q4.Q4_ENULL
+    assert f(A16, A16, A16, A16, A16, A16, None, A16, 1, 8, 128, 32, None) == q4.Q4_ENULL
+    assert f(A16, A16, A16, A16, A16 + 8, A16, A16, A16, 1, 8, 128, 32, None) == q4.Q4_EALIGN
+    assert f(A16, A16, A16, A16, A16, A16 + 1, A16, A16, 1, 8, 128, 32, None) == q4.Q4_EALIGN
+    assert f(A16, A16, A16, A16, A16, A16, A16, A16 + 2, 1, 8, 128, 32, None) == q4.Q4_EALIGN
+
+
 def test_other_entry_points_validation(L):
     assert L.gemv_f32(A16, A16, A16, 1, 8, 6, None) == q4.Q4_EINVAL
     assert L.gemv_f32(A16, A16, A16, 0, 8, 8, None) == q4.Q4_EINVAL
@@ -102,6 +114,7 @@ def test_no_device_reports_edevice(L):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert L.gemv_q4(A16, A16, A16, A16, A16, 1, 8, 128, 32, None) == q4.Q4_EDEVICE
+    assert L.gemv_q4_swiglu(A16, A16, A16, A16, A16, A16, A16, A16, 1, 8, 128, 32, None) == q4.Q4_EDEVICE
     assert L.read_reduce(A16, 8, A16B, 4, None) == q4.Q4_EDEVICE
 
 

@@ -379,3 +379,42 @@ def test_write_fill(n, blocks):
     torch.cuda.synchronize()
     assert bool((buf[:n] == -1.5).all())
     assert bool(torch.isnan(buf[n:]).all())
+
+
+# ---------------------------------------------------------------- SwiGLU block
+
+SWIGLU = [(1, 14336, 4096, 128), (1, 4864, 896, 32), (4, 515, 4096, 128), (8, 67, 14336, 128),
+          (3, 17, 256, 128), (2, 300, 8192, 128), (5, 129, 4224, 128)]
+
+
+@pytest.mark.parametrize("M,N,K,g", SWIGLU, ids=[f"M{a}N{b}K{c}g{d}" for a, b, c, d in SWIGLU])
+def test_gemv_q4_swiglu(M, N, K, g):
+    s = wl.Q4Shape(M, N, K, g, 0.002, 0.02)
+    dg = wl.make_q4_problem(300 + N, s, index=0)
+    du = wl.make_q4_problem(300 + N, s, index=1)
+    tg, tu = dev(dg), dev(du)
+    y = q4.gemv_q4_swiglu(tg["x"], (tg["wq"], tg["scales"], tg["zeros"]),
+                          (tu["wq"], tu["scales"], tu["zeros"]), g)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy().astype(np.float64)
+    rows = sample_rows(N, 400, N) if N > 2000 else None
+    y_ref, tol = oracle.swiglu(dg["x"], (dg["wq"], dg["scales"], dg["zeros"]),
+                               (du["wq"], du["scales"], du["zeros"]), g, rows=rows)
+    if rows is not None:
+        y = y[:, rows]
+    bad = np.abs(y - y_ref) > tol
+    assert not bad.any(), f"{int(bad.sum())}/{bad.size} outputs out of tolerance"
+
+
+def test_gemv_q4_swiglu_zero_gate_is_exactly_zero():
+    M, N, K, g = 1, 96, 4096, 128
+    s = wl.Q4Shape(M, N, K, g, 0.002, 0.02)
+    d = wl.make_q4_problem(31, s)
+    z = np.stack([d["zeros"] & 15, d["zeros"] >> 4], -1).reshape(N, -1)[:, :K // g]
+    codes = np.repeat(z, g, axis=1).astype(np.uint8)
+    gate = dict(d, wq=(codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8))
+    t, tg = dev(d), dev(gate)
+    y = q4.gemv_q4_swiglu(t["x"], (tg["wq"], tg["scales"], tg["zeros"]),
+                          (t["wq"], t["scales"], t["zeros"]), g)
+    torch.cuda.synchronize()
+    assert np.all(y.cpu().numpy() == 0.0)

@@ -368,3 +368,44 @@ int main(void) {
                     os.path.join(ROOT, "oracle", "q4ref.c"), "-lm"], check=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True)
     assert out.returncode == 0 and out.stdout.strip() == "ok", out.stdout + out.stderr
+
+
+# ---------------------------------------------------------------- SwiGLU combine
+
+def test_silu_odd_part_is_the_identity():
+    """silu(v) - silu(-v) = v (v sigma(v) + v sigma(-v) = v): fixes the sign
+    of the exponent and the 1 + e^-v denominator."""
+    v = np.concatenate([np.linspace(-30, 30, 601), [1e-8, -1e-8, 100.0, -250.0, 700.0]])
+    d = oracle.silu(v) - oracle.silu(-v)
+    assert np.allclose(d, v, rtol=1e-14, atol=0)
+
+
+def test_silu_special_values():
+    assert oracle.silu(0.0) == 0.0
+    assert oracle.silu(1e-9) == pytest.approx(0.5e-9, rel=1e-8)      # slope 1/2 at 0
+    assert oracle.silu(50.0) == pytest.approx(50.0, rel=1e-20)
+    assert 0 > oracle.silu(-50.0) > -50.0 * 2e-22                      # -50 e^-50
+    assert oracle.silu(-800.0) == 0.0                                  # e^800 overflows: -0
+
+
+def test_silu_slope_bound_used_by_the_tolerance():
+    """The SwiGLU tolerance takes |silu'| <= 1.1; the true maximum is about 1.0998."""
+    v = np.linspace(-20, 20, 400001)
+    slope = np.diff(oracle.silu(v)) / np.diff(v)
+    assert 1.09 < slope.max() < 1.1 and slope.min() > -0.11
+
+
+def test_swiglu_invariants():
+    """gate == up gives silu(g) g >= 0; an up matrix with q == z gives exactly 0;
+    a gate with q == z gives exactly 0."""
+    s = workloads.Q4Shape(2, 37, 256, 32, 0.005, 0.02)
+    d = workloads.make_q4_problem(21, s)
+    mat = (d["wq"], d["scales"], d["zeros"])
+    y, tol = oracle.swiglu(d["x"], mat, mat, s.g)
+    assert (y >= 0).all() and (tol > 0).all()
+    z = np.stack([d["zeros"] & 15, d["zeros"] >> 4], -1).reshape(s.N, -1)[:, :s.K // s.g]
+    codes = np.repeat(z, s.g, axis=1).astype(np.uint8)
+    flat = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    dead = (flat, d["scales"], d["zeros"])
+    assert np.all(oracle.swiglu(d["x"], mat, dead, s.g)[0] == 0)
+    assert np.all(oracle.swiglu(d["x"], dead, mat, s.g)[0] == 0)
