@@ -228,11 +228,25 @@ def host_cpu() -> str:
     return "unknown"
 
 
+def apply_tuned_profile(dev) -> dict | None:
+    """Load the device's tuned geometry profile (memory_bandwidth_amd/tuned/)
+    into the library, if one exists; returns what was applied."""
+    from memory_bandwidth_amd import autotune
+    path = autotune.default_profile_path(dev)
+    if not os.path.exists(path):
+        log("no tuned geometry profile for this device; default plan")
+        return None
+    n = autotune.apply_profile(path, dev)
+    log(f"tuned geometry profile {os.path.basename(path)}: {n} shapes differ from the default plan")
+    return {"file": os.path.relpath(path, ROOT), "shapes_set": n}
+
+
 def run_default(args):
     import torch
     import memory_bandwidth_amd as q4
 
     dev = torch.device("cuda:0")
+    profile = apply_tuned_profile(dev)
     W = setup_stream(torch, q4, dev)
     s = W["shape"]
     g = s.g
@@ -337,7 +351,7 @@ def run_default(args):
                    "matrices": wl.STREAM_MATRICES, "bytes_per_call": bytes_per_call["gemv_q4"],
                    "launches_per_step": wl.STREAM_MATRICES,
                    "weights": "int4 codes, fp16 scale + int4 zero per 128, fp32 x and y",
-                   "arithmetic": arith},
+                   "arithmetic": arith, "geometry_profile": profile},
         "roofline": {"bound": "hbm", "achieved": round(value, 2), "peak": SPEC_PEAK_GBS,
                      "unit": "GB/s", "frac": round(value / SPEC_PEAK_GBS, 4),
                      "traffic": traffic},

@@ -162,6 +162,28 @@ const char *q4_strerror(int status);
 /* Q4GEMV_ABI_VERSION of the built library. */
 int q4_abi_version(void);
 
+/* Fixes the launch geometry gemv_q4 (and each projection of gemv_q4_swiglu)
+ * uses for one exact shape (M, N, K, group_size), for autotuning and for
+ * applying a tuned profile (Refractometer, "What each sweep measures", q4
+ * GEMV: columns per workgroup, K-splits and rows are the swept knobs; the
+ * best configuration per device is kept as a profile).
+ *   path     Q4_PATH_FMA or Q4_PATH_INTEGER
+ *   waves    wavefronts per workgroup: 4, 8 or 16, or 0 for the plan's choice
+ *            (the multiply-add path has 4; the integer path for 2 to 8 rows
+ *            has 8, or 16 above 4 rows)
+ *   ksplit   wavefronts splitting one row's K range: 1, 2 or 4, or 0 for the
+ *            plan's choice
+ * Returns Q4_EINVAL for an invalid shape or knob, or a combination the
+ * kernels cannot run (e.g. the integer path at K <= 1024, or more than 3
+ * chunk positions per lane); the previous setting for the shape then stays.
+ * Setting a shape again replaces its entry; up to 256 shapes.  Host-only:
+ * needs no device, launches nothing, and is not safe to call while another
+ * thread calls into the library. */
+int gemv_q4_set_geometry(int M, int N, int K, int group_size, int path, int waves, int ksplit);
+
+/* Forgets every geometry set by gemv_q4_set_geometry.  Returns Q4_OK. */
+int gemv_q4_clear_geometry(void);
+
 #ifdef __cplusplus
 }
 #endif

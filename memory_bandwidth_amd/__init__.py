@@ -26,7 +26,8 @@ Q4_OK, Q4_EINVAL, Q4_ENULL, Q4_EALIGN, Q4_EDEVICE, Q4_ELAUNCH = 0, -1, -2, -3, -
 
 # Exported C symbols, in the order include/q4gemv.h declares them.
 EXPORTS = ("gemv_q4", "gemv_q4_swiglu", "gemv_f32", "dequant_q4", "read_reduce", "write_fill",
-           "gemv_q4_geometry", "gemv_q4_path", "q4_strerror", "q4_abi_version")
+           "gemv_q4_geometry", "gemv_q4_path", "q4_strerror", "q4_abi_version",
+           "gemv_q4_set_geometry", "gemv_q4_clear_geometry")
 
 Q4_PATH_FMA, Q4_PATH_INTEGER = 0, 1
 
@@ -58,11 +59,14 @@ def lib() -> ctypes.CDLL:
     IP = ctypes.POINTER(ctypes.c_int)
     L.gemv_q4_geometry.argtypes = [I, I, I, I, IP, IP, IP, IP, IP, IP]
     L.gemv_q4_path.argtypes = [I, I, I, I]
+    L.gemv_q4_set_geometry.argtypes = [I, I, I, I, I, I, I]
+    L.gemv_q4_clear_geometry.argtypes = []
     L.q4_strerror.argtypes = [I]
     L.q4_strerror.restype = ctypes.c_char_p
     L.q4_abi_version.argtypes = []
     for f in ("gemv_q4", "gemv_q4_swiglu", "gemv_f32", "dequant_q4", "read_reduce", "write_fill",
-              "gemv_q4_geometry", "gemv_q4_path", "q4_abi_version"):
+              "gemv_q4_geometry", "gemv_q4_path", "q4_abi_version",
+              "gemv_q4_set_geometry", "gemv_q4_clear_geometry"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -231,3 +235,15 @@ def gemv_q4_path(M: int, N: int, K: int, group_size: int) -> int:
 
 def abi_version() -> int:
     return lib().q4_abi_version()
+
+
+def gemv_q4_set_geometry(M: int, N: int, K: int, group_size: int, path: int, waves: int = 0,
+                         ksplit: int = 0) -> None:
+    """Fix gemv_q4's geometry for one exact shape (host-only); raises Q4Error
+    when the kernels cannot run that combination."""
+    _check("gemv_q4_set_geometry", lib().gemv_q4_set_geometry(M, N, K, group_size, path, waves, ksplit))
+
+
+def gemv_q4_clear_geometry() -> None:
+    """Forget every geometry fixed by gemv_q4_set_geometry."""
+    _check("gemv_q4_clear_geometry", lib().gemv_q4_clear_geometry())

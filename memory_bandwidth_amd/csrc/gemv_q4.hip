@@ -907,18 +907,26 @@ constexpr int kCUs = 256;   // compute units of an MI355X
 // are dealt to workgroups so that, beyond one round of workgroups, every CU
 // gets the same number of them (2 x 8 wavefronts of 3.5 rows rather than
 // 1.75 x 8 of 4).
-void plan_integer(Geometry &p, int N, int K) {
+// Knobs a caller may fix for one shape (gemv_q4_set_geometry); 0 or -1 = the plan's choice.
+struct Knobs {
+    int path = -1;     // Q4_PATH_FMA or Q4_PATH_INTEGER
+    int waves = 0;     // wavefronts per workgroup
+    int ksplit = 0;    // wavefronts splitting one row's K range
+};
+
+bool plan_integer(Geometry &p, int N, int K, const Knobs &k) {
     const int C = K / 32;
-    if (p.M != 1 || p.LPR != 64) return;
-    int S = p.S;
-    while (S < 4 && (C + S - 1) / S > 3 * 64) S *= 2;
+    if (p.M != 1 || p.LPR != 64) return false;
+    int S = k.ksplit ? k.ksplit : p.S;
+    if (!k.ksplit)
+        while (S < 4 && (C + S - 1) / S > 3 * 64) S *= 2;
     const int part = (C + S - 1) / S;
     const int JP = (part + 63) / 64;
     const int R = row_slots(1);
     const long groups = ((long)N + R - 1) / R;
     const long waves = groups * S;
-    const int W = S == 4 && waves >= 16L * kCUs ? 16 : (waves >= 8L * kCUs ? 8 : 4);
-    if (JP > 3 || (size_t)C * kIW * 4 + (size_t)W * R * 4 > (size_t)kLdsBytes) return;
+    const int W = k.waves ? k.waves : (S == 4 && waves >= 16L * kCUs ? 16 : (waves >= 8L * kCUs ? 8 : 4));
+    if (JP > 3 || W < S || (size_t)C * kIW * 4 + (size_t)W * R * 4 > (size_t)kLdsBytes) return false;
     const int groups_per_wg = W / S;
     long grid = (groups + groups_per_wg - 1) / groups_per_wg;
     if (grid * W > (long)kCUs * 4) grid = (grid + kCUs - 1) / kCUs * kCUs;
@@ -931,6 +939,7 @@ void plan_integer(Geometry &p, int N, int K) {
     p.rows_per_wave = R;
     p.seg_chunks = C;
     p.segments = 1;
+    return true;
 }
 
 constexpr int kLdsMax = 160 * 1024;   // LDS of one CU, and the most one workgroup may use
@@ -943,24 +952,29 @@ constexpr int kLdsMax = 160 * 1024;   // LDS of one CU, and the most one workgro
 // The K-split S grows while the row groups that remain still hold the
 // workgroup's rows and each split keeps a full lane sweep, and until a lane
 // holds at most 2 chunk positions.
-void plan_integer_m(Geometry &p, int M, int N, int K) {
+bool plan_integer_m(Geometry &p, int M, int N, int K, const Knobs &k) {
     const int C = K / 32;
-    if (M < 2 || p.LPR != 64 || K <= 1024) return;
+    if (M < 2 || p.LPR != 64 || K <= 1024) return false;
     const int MP = M <= 2 ? 2 : (M <= 4 ? 4 : 8);
     const int W = MP == 8 ? 16 : 8;
+    if (k.waves && k.waves != W) return false;
     const int wpc = MP == 8 ? 1 : 2;
     const int R = 4;
     const int budget = kLdsMax / wpc - W * R * MP * 4;
     int seg = std::min(C, budget / (M * kIW * 4));
     if (seg < C) seg = seg / 64 * 64;
     // Segmented x costs a barrier and a pipeline drain per segment: below 5
-    // rows the multiply-add path measures faster there.
-    if (seg < 64 || (seg < C && MP <= 4)) return;
+    // rows the multiply-add path measures faster there (unless asked for).
+    if (seg < 64 || (seg < C && MP <= 4 && k.path != Q4_PATH_INTEGER)) return false;
     const long target = (long)kCUs * wpc;
     const long rpw = std::max<long>((N + target - 1) / target, W);
     int S = 1;
-    while (S < 4 && (long)(W / (2 * S)) * R >= rpw && seg / (2 * S) >= 64) S *= 2;
-    while (S < 4 && (seg + S - 1) / S > 128) S *= 2;
+    if (k.ksplit) {
+        S = k.ksplit;
+    } else {
+        while (S < 4 && (long)(W / (2 * S)) * R >= rpw && seg / (2 * S) >= 64) S *= 2;
+        while (S < 4 && (seg + S - 1) / S > 128) S *= 2;
+    }
     if ((seg + S - 1) / S > 128) seg = 128 * S;
     const int part = (seg + S - 1) / S;
     const int JP = (part + 63) / 64;
@@ -976,11 +990,12 @@ void plan_integer_m(Geometry &p, int M, int N, int K) {
     p.rows_per_wave = R;
     p.seg_chunks = seg;
     p.segments = (C + seg - 1) / seg;
+    return true;
 }
 
-// Chooses the launch geometry for a validated shape.
-Geometry plan(int M, int N, int K, int g) {
-    (void)g;
+// Chooses the launch geometry for a validated shape, with any knobs fixed;
+// *ok is cleared when the knobs cannot be met.
+Geometry plan_with(int M, int N, int K, const Knobs &k, bool *ok) {
     Geometry p{};
     p.M = M;
     const int C = K / 32;
@@ -993,9 +1008,13 @@ Geometry plan(int M, int N, int K, int g) {
     // while every split keeps a full lane sweep.
     const int seg_len = std::min(C, kLdsBytes / (M * kXStride * (int)sizeof(float)));
     p.S = 1;
-    while (p.S < kWaves && 2 * p.S * p.LPR <= seg_len &&
-           (row_waves * p.S < 2048 || (seg_len + p.S * p.LPR - 1) / (p.S * p.LPR) > 2))
-        p.S *= 2;
+    if (k.path == Q4_PATH_FMA && k.ksplit) {
+        p.S = k.ksplit;
+    } else {
+        while (p.S < kWaves && 2 * p.S * p.LPR <= seg_len &&
+               (row_waves * p.S < 2048 || (seg_len + p.S * p.LPR - 1) / (p.S * p.LPR) > 2))
+            p.S *= 2;
+    }
     // x segment: the LDS left after the K-split partial sums, in whole chunks;
     // when x needs several segments, each is a whole number of lane sweeps.
     const int comb = p.S > 1 ? kWaves * p.rows_per_wave * M * (int)sizeof(float) : 0;
@@ -1018,9 +1037,36 @@ Geometry plan(int M, int N, int K, int g) {
     const long rows_per_wg = (long)p.rows_per_wave * (kWaves / p.S);
     p.grid = (int)((N + rows_per_wg - 1) / rows_per_wg);
     p.rpg = (int)std::min<long>(rows_per_wg, N);
-    plan_integer(p, N, K);
-    plan_integer_m(p, M, N, K);
+    if (k.path == Q4_PATH_FMA) {
+        if (k.waves && k.waves != kWaves) *ok = false;
+        return p;
+    }
+    const bool integer = M == 1 ? plan_integer(p, N, K, k) : plan_integer_m(p, M, N, K, k);
+    if (k.path == Q4_PATH_INTEGER && !integer) *ok = false;
     return p;
+}
+
+// Geometries fixed by gemv_q4_set_geometry, looked up by exact shape.
+struct Override {
+    int M, N, K, g;
+    Knobs k;
+};
+constexpr int kMaxOverrides = 256;
+Override g_over[kMaxOverrides];
+int g_n_over = 0;
+
+Geometry plan(int M, int N, int K, int g) {
+    for (int i = 0; i < g_n_over; ++i) {
+        const Override &o = g_over[i];
+        if (o.M == M && o.N == N && o.K == K && o.g == g) {
+            bool ok = true;
+            const Geometry p = plan_with(M, N, K, o.k, &ok);
+            if (ok) return p;
+            break;
+        }
+    }
+    bool ok = true;
+    return plan_with(M, N, K, Knobs{}, &ok);
 }
 
 int validate(int M, int N, int K, int g) {
@@ -1157,6 +1203,36 @@ extern "C" int gemv_q4_path(int M, int N, int K, int group_size) {
     const int v = validate(M, N, K, group_size);
     if (v != Q4_OK) return v;
     return plan(M, N, K, group_size).integer ? Q4_PATH_INTEGER : Q4_PATH_FMA;
+}
+
+extern "C" int gemv_q4_set_geometry(int M, int N, int K, int group_size, int path, int waves,
+                                    int ksplit) {
+    const int v = validate(M, N, K, group_size);
+    if (v != Q4_OK) return v;
+    if ((path != Q4_PATH_FMA && path != Q4_PATH_INTEGER) ||
+        (waves != 0 && waves != 4 && waves != 8 && waves != 16) ||
+        (ksplit != 0 && ksplit != 1 && ksplit != 2 && ksplit != 4))
+        return Q4_EINVAL;
+    Knobs k;
+    k.path = path;
+    k.waves = waves;
+    k.ksplit = ksplit;
+    bool ok = true;
+    plan_with(M, N, K, k, &ok);
+    if (!ok) return Q4_EINVAL;
+    int i = 0;
+    while (i < g_n_over && !(g_over[i].M == M && g_over[i].N == N && g_over[i].K == K &&
+                             g_over[i].g == group_size))
+        ++i;
+    if (i == kMaxOverrides) return Q4_EINVAL;
+    g_over[i] = Override{M, N, K, group_size, k};
+    if (i == g_n_over) ++g_n_over;
+    return Q4_OK;
+}
+
+extern "C" int gemv_q4_clear_geometry(void) {
+    g_n_over = 0;
+    return Q4_OK;
 }
 
 namespace {

@@ -191,3 +191,72 @@ def test_geometry_rejects_bad_shapes():
         q4.gemv_q4_geometry(1, 8, 100, 32)
     with pytest.raises(q4.Q4Error):
         q4.gemv_q4_path(1, 8, 100, 32)
+
+
+# ---------------------------------------------------------------- geometry overrides
+
+@pytest.fixture
+def clean_geometry():
+    q4.gemv_q4_clear_geometry()
+    yield
+    q4.gemv_q4_clear_geometry()
+
+
+def test_set_geometry_changes_the_plan(clean_geometry):
+    M, N, K, g = 1, 14336, 4096, 128
+    default = q4.gemv_q4_geometry(M, N, K, g)
+    q4.gemv_q4_set_geometry(M, N, K, g, q4.Q4_PATH_INTEGER, waves=4, ksplit=2)
+    geo = q4.gemv_q4_geometry(M, N, K, g)
+    assert geo["block"] == 256 and geo["ksplit"] == 2 and geo != default
+    assert q4.gemv_q4_path(M, N, K, g) == q4.Q4_PATH_INTEGER
+    q4.gemv_q4_set_geometry(M, N, K, g, q4.Q4_PATH_FMA)            # replaces the entry
+    assert q4.gemv_q4_path(M, N, K, g) == q4.Q4_PATH_FMA
+    assert q4.gemv_q4_path(M, N + 1, K, g) == q4.Q4_PATH_INTEGER  # other shapes keep the plan
+    q4.gemv_q4_clear_geometry()
+    assert q4.gemv_q4_geometry(M, N, K, g) == default
+
+
+@pytest.mark.parametrize("M,N,K,g,path,waves,ksplit", [
+    (1, 896, 896, 32, 1, 0, 0),          # integer path needs K > 1024 (whole 64-lane sweeps)
+    (1, 64, 32768, 128, 1, 0, 1),        # 1024 chunks on one wavefront: > 3 per lane
+    (1, 64, 4096, 128, 1, 4, 8),         # ksplit not in {1, 2, 4}
+    (1, 64, 4096, 128, 0, 8, 0),         # the multiply-add path has 4 wavefronts
+    (4, 64, 4096, 128, 1, 16, 0),        # 2..4 rows use 8 wavefronts
+    (1, 64, 4096, 128, 2, 0, 0),         # no such path
+    (1, 64, 100, 32, 0, 0, 0),           # invalid shape
+])
+def test_set_geometry_rejects_what_cannot_run(clean_geometry, M, N, K, g, path, waves, ksplit):
+    valid = K % g == 0
+    before = q4.gemv_q4_geometry(M, N, K, g) if valid else None
+    with pytest.raises(q4.Q4Error):
+        q4.gemv_q4_set_geometry(M, N, K, g, path, waves, ksplit)
+    if valid:
+        assert q4.gemv_q4_geometry(M, N, K, g) == before   # plan unchanged
+
+
+def test_set_geometry_table_limit(clean_geometry):
+    for n in range(256):
+        q4.gemv_q4_set_geometry(1, 100 + n, 4096, 128, q4.Q4_PATH_FMA)
+    with pytest.raises(q4.Q4Error):
+        q4.gemv_q4_set_geometry(1, 99, 4096, 128, q4.Q4_PATH_FMA)
+    q4.gemv_q4_set_geometry(1, 100, 4096, 128, q4.Q4_PATH_INTEGER)   # replacing still works
+
+
+def test_tuned_profile_is_well_formed_and_applies(clean_geometry):
+    """The committed profile names its device and, for every shape, a winner
+    that passed parity and that the library accepts; cliffs are flagged."""
+    import json
+    import os
+    from memory_bandwidth_amd import autotune
+    files = [f for f in os.listdir(autotune.TUNED_DIR) if f.endswith(".json")]
+    assert files
+    for f in files:
+        prof = json.load(open(os.path.join(autotune.TUNED_DIR, f)))
+        assert f == prof["device"] + ".json"
+        for e in prof["entries"]:
+            b = e["best"]
+            timed = [c for c in e["candidates"] if c["parity"]]
+            assert b["median_us"] == min(c["median_us"] for c in timed)
+            assert all(c["cliff"] == (c["frac_of_best"] < autotune.CLIFF) for c in timed)
+            q4.gemv_q4_set_geometry(e["M"], e["N"], e["K"], e["group_size"], b["path"],
+                                    b["waves"], b["ksplit"])

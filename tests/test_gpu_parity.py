@@ -418,3 +418,31 @@ def test_gemv_q4_swiglu_zero_gate_is_exactly_zero():
                           (t["wq"], t["scales"], t["zeros"]), g)
     torch.cuda.synchronize()
     assert np.all(y.cpu().numpy() == 0.0)
+
+
+# ---------------------------------------------------------------- every tunable geometry
+
+GEOM_SHAPES = [(1, 14336, 4096, 128), (1, 4096, 14336, 128), (4, 515, 4096, 128),
+               (8, 67, 14336, 128), (1, 896, 4864, 32), (2, 300, 8192, 128), (1, 1000, 896, 32)]
+
+
+@pytest.mark.parametrize("M,N,K,g", GEOM_SHAPES, ids=[f"M{a}N{b}K{c}g{d}" for a, b, c, d in GEOM_SHAPES])
+def test_every_geometry_the_tuner_may_pick(M, N, K, g):
+    """Each (path, waves, K-split) that gemv_q4_set_geometry accepts gives
+    results within the tolerance (sampled rows for large N)."""
+    from memory_bandwidth_amd import autotune
+    s = wl.Q4Shape(M, N, K, g, 0.002, 0.02)
+    d = wl.make_q4_problem(400 + N, s)
+    t = dev(d)
+    rows = sample_rows(N, 300, N) if N > 2000 else np.arange(N)
+    y_ref, b = oracle.gemv_q4(d["x"], d["wq"], d["scales"], d["zeros"], g, rows=rows)
+    cands = autotune.candidates(M, N, K, g)
+    assert len(cands) >= 3
+    try:
+        for c in cands:
+            q4.gemv_q4_set_geometry(M, N, K, g, c["path"], c["waves"], c["ksplit"])
+            assert q4.gemv_q4_geometry(M, N, K, g) == c["geometry"]
+            y = run_q4(t, g)
+            assert_within(y[:, rows], y_ref, b, f"{c['path']}/{c['waves']}/{c['ksplit']}")
+    finally:
+        q4.gemv_q4_clear_geometry()
