@@ -888,7 +888,7 @@ __global__ __launch_bounds__(W * 64) void gemv_q4_intm_kernel(
 
 struct Geometry {
     int M, LPR, JP, S, seg_chunks, segments, grid, rows_per_wave;
-    bool integer;   // the exact integer path for one activation row
+    bool integer;   // the exact integer path (gemv_q4_int_kernel, gemv_q4_intm_kernel)
     int rpg;        // integer path: rows per workgroup
     int waves;      // wavefronts per workgroup
     int mp;         // integer path, M > 1: M rounded up to 2, 4 or 8
