@@ -893,6 +893,7 @@ struct Geometry {
     int waves;      // wavefronts per workgroup
     int mp;         // integer path, M > 1: M rounded up to 2, 4 or 8
     int epi;        // launch-time: finish a SwiGLU block in the store (see store_y)
+    int fma_r;      // multiply-add path: row slots per wavefront
 };
 
 constexpr int kCUs = 256;   // compute units of an MI355X
@@ -1000,7 +1001,10 @@ Geometry plan_with(int M, int N, int K, const Knobs &k, bool *ok) {
     p.M = M;
     const int C = K / 32;
     p.LPR = C <= 16 ? 16 : (C <= 32 ? 32 : 64);
-    const int R = row_slots(M);
+    // Short rows (K <= 1024) of one activation row: 2 row slots below 16384
+    // rows (more, smaller wavefronts for these latency-bound shapes), else 4.
+    const int R = M == 1 && p.LPR < 64 && N < 16384 ? 2 : row_slots(M);
+    p.fma_r = R;
     p.rows_per_wave = R * (q4::kWave / p.LPR);
     const long row_waves = ((long)N + p.rows_per_wave - 1) / p.rows_per_wave;
     // K-split, decided on the length of one x segment: enough wavefronts to
@@ -1090,6 +1094,13 @@ size_t lds_bytes(const Geometry &p) {
 template <int M, int LPR, int JP>
 void launch(const Geometry &p, const float *x, const uint8_t *wq, const uint16_t *scales,
             const uint8_t *zeros, float *y, int N, int K, int gshift, hipStream_t st) {
+    if constexpr (M == 1 && LPR < 64) {
+        if (p.fma_r == 2) {
+            hipLaunchKernelGGL((gemv_q4_kernel<1, LPR, JP, 2>), dim3(p.grid), dim3(kBlock), lds_bytes(p), st,
+                               x, wq, scales, zeros, y, N, K, gshift, p.S, p.seg_chunks, p.epi);
+            return;
+        }
+    }
     hipLaunchKernelGGL((gemv_q4_kernel<M, LPR, JP, row_slots(M)>), dim3(p.grid), dim3(kBlock),
                        lds_bytes(p), st, x, wq, scales, zeros, y, N, K, gshift, p.S, p.seg_chunks, p.epi);
 }
