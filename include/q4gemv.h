@@ -60,8 +60,8 @@ enum q4_status {
  *   - fused multiply-add: (q - z) formed exactly in binary16, multiplied by
  *     the fp32 x and accumulated in fp32, the group scale applied per
  *     32-code chunk;
- *   - integer (K > 1024; M == 1 up to K = 18688, 2 to 4 rows while their x
- *     fits one LDS segment, 5 to 8 rows at any K): every chunk of 32 values
+ *   - integer (M == 1: 512 < K <= 18688; 2 to 4 rows: K > 1024 while their
+ *     x fits one LDS segment; 5 to 8 rows: K > 1024): every chunk of 32 values
  *     of an x row (x[m][32c .. 32c+31]) is rounded to integers X = round(x * 2^(22-e)),
  *     where 2^(e-1) <= max|x| over the chunk < 2^e, so |X| < 2^22; the sum
  *     of (q - z) * X is formed exactly in int32, converted to fp32 once per
@@ -174,8 +174,9 @@ int q4_abi_version(void);
  *   ksplit   wavefronts splitting one row's K range: 1, 2 or 4, or 0 for the
  *            plan's choice
  * Returns Q4_EINVAL for an invalid shape or knob, or a combination the
- * kernels cannot run (e.g. the integer path at K <= 1024, or more than 3
- * chunk positions per lane); the previous setting for the shape then stays.
+ * kernels cannot run (e.g. the integer path at K <= 512 or with a K-split at
+ * K <= 1024, or more than 3 chunk positions per lane); the previous setting
+ * for the shape then stays.
  * Setting a shape again replaces its entry; up to 256 shapes.  Host-only:
  * needs no device, launches nothing, and is not safe to call while another
  * thread calls into the library. */

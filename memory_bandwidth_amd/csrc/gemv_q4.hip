@@ -481,7 +481,7 @@ __device__ __forceinline__ void store_int_chunk(const f32x4_t (&xr)[kIntVPT / 4]
 // more chunks than one pass of the workgroup converts.  S and MULTI are
 // template parameters so that the common case (S = 1, one pass) carries no
 // division and no unused path.
-template <int W, int JP, int R, int S, bool MULTI>
+template <int W, int LPR, int JP, int R, int S, bool MULTI>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) void gemv_q4_int_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ wq,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
@@ -514,12 +514,16 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     uint32_t *xrec = ilds;                                           // [C][kIW]
     float *comb = reinterpret_cast<float *>(ilds + C * kIW);         // [W][R]
     const int lane = tid & 63;
+    constexpr int RG = 64 / LPR;               // rows one load instruction covers
+    static_assert(LPR == 64 || (S == 1 && JP == 1), "short rows: no K-split, one chunk per lane");
+    const int li = LPR == 64 ? lane : lane % LPR;    // chunk position within the row
+    const int rgl = LPR == 64 ? 0 : lane / LPR;      // row of the slot this lane works on
     const int NG = W / S;                      // row groups per workgroup
     const int rg = wave / S;
     const int ks = wave - rg * S;
     const int gq = rpg / NG, grem = rpg - gq * NG;
     const int gstart = blockIdx.x * rpg + rg * gq + min(rg, grem);
-    const int nrows = max(0, min(gq + (rg < grem ? 1 : 0), N - gstart));   // rows of this group, <= R
+    const int nrows = max(0, min(gq + (rg < grem ? 1 : 0), N - gstart));   // rows of this group, <= R * RG
     const int rbase = min(gstart, N - 1);
     const int part = (C + S - 1) / S;
     const int lo = ks * part;
@@ -532,9 +536,12 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
         (uint32_t)std::min<uint64_t>((uint64_t)rows_left * RB, 0xFFFFFFFFull));
     const __amdgpu_buffer_rsrc_t sc_r = raw_rsrc(scales + (size_t)rbase * G, rows_left * (uint32_t)G * 2u);
     const __amdgpu_buffer_rsrc_t zp_r = raw_rsrc(zeros + (size_t)rbase * ZB, rows_left * (uint32_t)ZB);
-    uint32_t lr[R];   // row offset of each slot: slots past the group's rows re-read its last row
+    // Row of each slot (of this lane's half, with short rows): slots past the
+    // group's rows re-read its last row.  Uniform (an SGPR offset) for whole
+    // 64-lane rows, per lane (added to the VGPR offset) for short rows.
+    uint32_t lr[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) lr[r] = (uint32_t)min(r, max(nrows, 1) - 1);
+    for (int r = 0; r < R; ++r) lr[r] = (uint32_t)min(r * RG + rgl, max(nrows, 1) - 1);
 
     // With 8 or 16 wavefronts the stagers convert the first pass of x before
     // issuing their own weight loads, so that the x loads of every workgroup
@@ -548,21 +555,27 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     uint32_t sr[JP][R], zr[JP][R];
 #pragma unroll
     for (int j = 0; j < JP; ++j) {
-        const uint32_t gi = (uint32_t)min(lo + lane + 64 * j, clast) >> gshift;
+        const uint32_t gi = (uint32_t)min(lo + li + LPR * j, clast) >> gshift;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            sr[j][r] = __builtin_amdgcn_raw_buffer_load_b16(sc_r, gi * 2u, lr[r] * (uint32_t)G * 2u, 0);
-            zr[j][r] = __builtin_amdgcn_raw_buffer_load_b8(zp_r, gi >> 1, lr[r] * (uint32_t)ZB, 0);
+            const uint32_t rs = LPR == 64 ? lr[r] : 0u, rv = LPR == 64 ? 0u : lr[r];
+            sr[j][r] = __builtin_amdgcn_raw_buffer_load_b16(sc_r, gi * 2u + rv * (uint32_t)G * 2u,
+                                                            rs * (uint32_t)G * 2u, 0);
+            zr[j][r] = __builtin_amdgcn_raw_buffer_load_b8(zp_r, (gi >> 1) + rv * (uint32_t)ZB,
+                                                           rs * (uint32_t)ZB, 0);
         }
     }
     __builtin_amdgcn_sched_barrier(0);
     u32x4_t w[JP][R];
 #pragma unroll
     for (int j = 0; j < JP; ++j) {
-        const uint32_t coff = (uint32_t)min(lo + lane + 64 * j, clast) * 16u;
+        const uint32_t coff = (uint32_t)min(lo + li + LPR * j, clast) * 16u;
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-            w[j][r] = __builtin_amdgcn_raw_buffer_load_b128(wq_r, coff, lr[r] * (uint32_t)RB, kNonTemporal);
+        for (int r = 0; r < R; ++r) {
+            const uint32_t rs = LPR == 64 ? lr[r] : 0u, rv = LPR == 64 ? 0u : lr[r];
+            w[j][r] = __builtin_amdgcn_raw_buffer_load_b128(wq_r, coff + rv * (uint32_t)RB, rs * (uint32_t)RB,
+                                                            kNonTemporal);
+        }
     }
 
     // Chunks of x past the first pass are loaded and converted here.
@@ -584,7 +597,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     for (int r = 0; r < R; ++r) acc[r] = 0.f;
 #pragma unroll
     for (int j = 0; j < JP; ++j) {
-        const int c = lo + lane + 64 * j;
+        const int c = lo + li + LPR * j;
         if (c < hi) {
             const uint32_t *rec = xrec + c * kIW;
             u32x4_t D[6];
@@ -598,7 +611,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
             const uint32_t zsh = (((uint32_t)c >> gshift) & 1u) << 2;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                if (r < nrows) {
+                if (r * RG + rgl < nrows) {
                     // (8 - z) * SX enters as (8 - z) * SXlow in digit 0 and
                     // (8 - z) * SXhigh in digit 3 (weight 16^3 = 2^12).
                     const int nz = 8 - (int)__builtin_amdgcn_ubfe(zr[j][r], zsh, 4);
@@ -630,6 +643,15 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
         }
     }
 
+    if constexpr (LPR < 64) {
+        // Short rows: each slot's sum over its LPR lanes; lane 0 of the group stores.
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float v = q4::group_sum<LPR>(acc[r]);
+            if (li == 0 && r * RG + rgl < nrows) store_y(y, gstart + r * RG + rgl, v, epi);
+        }
+        return;
+    }
     constexpr int NQ = (R + 3) / 4;
     float out[NQ];
     q4::wave_reduce_rows<R>(acc, out);
@@ -917,7 +939,27 @@ struct Knobs {
 
 bool plan_integer(Geometry &p, int N, int K, const Knobs &k) {
     const int C = K / 32;
-    if (p.M != 1 || p.LPR != 64) return false;
+    if (p.M != 1 || (p.LPR != 64 && p.LPR != 32)) return false;
+    if (p.LPR == 32) {
+        // Short rows (512 < K <= 1024): two rows per load instruction, no
+        // K-split, one chunk per lane; 8 wavefronts once that still gives
+        // every CU a workgroup, else 4.
+        if (k.ksplit && k.ksplit != 1) return false;
+        const int R = row_slots(1);
+        const long groups = ((long)N + 2 * R - 1) / (2 * R);
+        const int W = k.waves ? k.waves : (groups >= 8L * kCUs ? 8 : 4);
+        const long grid = (groups + W - 1) / W;
+        p.integer = true;
+        p.waves = W;
+        p.S = 1;
+        p.JP = 1;
+        p.grid = (int)grid;
+        p.rpg = (int)((N + grid - 1) / grid);
+        p.rows_per_wave = 2 * R;
+        p.seg_chunks = C;
+        p.segments = 1;
+        return true;
+    }
     int S = k.ksplit ? k.ksplit : p.S;
     if (!k.ksplit)
         while (S < 4 && (C + S - 1) / S > 3 * 64) S *= 2;
@@ -1115,16 +1157,22 @@ void dispatch_jp(const Geometry &p, const float *x, const uint8_t *wq, const uin
     }
 }
 
-template <int W, int JP, int S, bool MULTI>
+template <int W, int JP, int S, bool MULTI, int LPR = 64>
 void launch_integer(const Geometry &p, const float *x, const uint8_t *wq, const uint16_t *scales,
                     const uint8_t *zeros, float *y, int N, int K, int gshift, hipStream_t st) {
-    hipLaunchKernelGGL((gemv_q4_int_kernel<W, JP, row_slots(1), S, MULTI>), dim3(p.grid), dim3(W * 64),
+    hipLaunchKernelGGL((gemv_q4_int_kernel<W, LPR, JP, row_slots(1), S, MULTI>), dim3(p.grid), dim3(W * 64),
                        lds_bytes(p), st, x, wq, scales, zeros, y, N, K, gshift, p.rpg, p.epi);
 }
 
 template <int W, int S>
 void dispatch_integer_jp(const Geometry &p, const float *x, const uint8_t *wq, const uint16_t *scales,
                          const uint8_t *zeros, float *y, int N, int K, int gshift, hipStream_t st) {
+    if constexpr (S == 1) {
+        if (p.LPR == 32) {
+            launch_integer<W, 1, 1, false, 32>(p, x, wq, scales, zeros, y, N, K, gshift, st);
+            return;
+        }
+    }
     const bool multi = K / 32 > W * kIntWaveChunks;
     switch (p.JP) {
     case 1:

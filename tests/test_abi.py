@@ -154,10 +154,11 @@ def test_geometry_covers_every_row(shape):
 
 
 PATHS = [
-    # M, N, K, g, path: one activation row with more than 32 chunks per row takes the integer path
+    # M, N, K, g, path: one activation row with more than 16 chunks per row takes the integer path
     (1, 14336, 4096, 128, 1), (1, 4096, 14336, 128, 1), (1, 65, 2048, 128, 1),
-    (1, 1, 18688, 128, 1), (1, 4, 18816, 128, 0), (1, 896, 896, 32, 0), (1, 151936, 896, 32, 0),
-    (1, 63, 2016, 32, 1), (1, 7, 1024, 32, 0), (2, 14336, 4096, 128, 1), (8, 4096, 14336, 128, 1),
+    (1, 1, 18688, 128, 1), (1, 4, 18816, 128, 0), (1, 896, 896, 32, 1), (1, 151936, 896, 32, 1),
+    (1, 63, 2016, 32, 1), (1, 7, 1024, 32, 1), (1, 9, 512, 32, 0), (1, 9, 544, 32, 1),
+    (2, 14336, 4096, 128, 1), (8, 4096, 14336, 128, 1),
     (4, 896, 896, 32, 0), (2, 64, 1024, 32, 0), (3, 4864, 896, 32, 0), (7, 100, 2048, 128, 1),
     # x records of 2..4 rows that need segments take the multiply-add path
     (4, 4096, 14336, 128, 0), (2, 4096, 14336, 128, 0), (2, 300, 8192, 128, 1),
@@ -217,7 +218,8 @@ def test_set_geometry_changes_the_plan(clean_geometry):
 
 
 @pytest.mark.parametrize("M,N,K,g,path,waves,ksplit", [
-    (1, 896, 896, 32, 1, 0, 0),          # integer path needs K > 1024 (whole 64-lane sweeps)
+    (1, 896, 512, 32, 1, 0, 0),          # integer path needs K > 512 (32 or 64 lanes per row)
+    (1, 896, 896, 32, 1, 0, 2),          # 32-lane rows: no K-split
     (1, 64, 32768, 128, 1, 0, 1),        # 1024 chunks on one wavefront: > 3 per lane
     (1, 64, 4096, 128, 1, 4, 8),         # ksplit not in {1, 2, 4}
     (1, 64, 4096, 128, 0, 8, 0),         # the multiply-add path has 4 wavefronts
