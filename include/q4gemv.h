@@ -89,8 +89,11 @@ int gemv_q4(const float *x, const uint8_t *wq, const uint16_t *scales,
  *   y[m, n] = silu(g[m, n]) * u[m, n],   silu(v) = v / (1 + e^-v)
  * (gerbil "WGSL Kernel Reference", section 9 SiLU for silu, section 12 Mul
  * for the combine, which the page notes could be fused with the SiLU).
- * Two launches on the stream: u is written to y, then the gate GEMV combines
- * in its store, so no separate element-wise pass and no intermediate buffer.
+ * With one activation row on the integer path without a K-split, one launch
+ * converts x once and streams the gate matrix, then the up matrix, and
+ * combines in registers.  Otherwise two launches: u is written to y, then
+ * the gate GEMV combines in its store.  Either way there is no separate
+ * element-wise pass and no intermediate buffer.
  * Arguments, rules and the arithmetic path of each projection are those of
  * gemv_q4 (both matrices [N, K] with the same group_size); y must not overlap
  * any input.  Each output is within |u| * 1.1 * t_g + |silu(g)| * t_u plus

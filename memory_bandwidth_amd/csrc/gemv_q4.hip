@@ -106,8 +106,10 @@ constexpr int kNonTemporal = 2;
 // Stores one output.  With epi set the GEMV is the gate projection of a
 // SwiGLU block: y already holds the up projection u, and silu(v) * u, with
 // silu(v) = v / (1 + e^-v), replaces it.
+__device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
+
 __device__ __forceinline__ void store_y(float *y, size_t i, float v, int epi) {
-    if (epi) v = v / (1.0f + __expf(-v)) * y[i];
+    if (epi) v = silu(v) * y[i];
     y[i] = v;
 }
 
@@ -481,11 +483,14 @@ __device__ __forceinline__ void store_int_chunk(const f32x4_t (&xr)[kIntVPT / 4]
 // more chunks than one pass of the workgroup converts.  S and MULTI are
 // template parameters so that the common case (S = 1, one pass) carries no
 // division and no unused path.
-template <int W, int LPR, int JP, int R, int S, bool MULTI>
+template <int W, int LPR, int JP, int R, int S, bool MULTI, bool SWI = false>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) void gemv_q4_int_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ wq,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
-    float *__restrict__ y, int N, int K, int gshift, int rpg, int epi) {
+    float *__restrict__ y, int N, int K, int gshift, int rpg, int epi,
+    const uint8_t *__restrict__ wq2, const uint16_t *__restrict__ scales2,
+    const uint8_t *__restrict__ zeros2) {
+    static_assert(!SWI || S == 1, "the SwiGLU form has no K-split");
     extern __shared__ uint32_t ilds[];
     const int tid = threadIdx.x;
     // x first, before any address arithmetic: a CU returns loads in the
@@ -532,10 +537,6 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     const uint32_t magic8 = 0x88888888u;
 
     const uint32_t rows_left = (uint32_t)(N - rbase);
-    const __amdgpu_buffer_rsrc_t wq_r = raw_rsrc(wq + (size_t)rbase * RB,
-        (uint32_t)std::min<uint64_t>((uint64_t)rows_left * RB, 0xFFFFFFFFull));
-    const __amdgpu_buffer_rsrc_t sc_r = raw_rsrc(scales + (size_t)rbase * G, rows_left * (uint32_t)G * 2u);
-    const __amdgpu_buffer_rsrc_t zp_r = raw_rsrc(zeros + (size_t)rbase * ZB, rows_left * (uint32_t)ZB);
     // Row of each slot (of this lane's half, with short rows): slots past the
     // group's rows re-read its last row.  Uniform (an SGPR offset) for whole
     // 64-lane rows, per lane (added to the VGPR offset) for short rows.
@@ -552,6 +553,22 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     constexpr bool kStageFirst = W >= 8;
     if (kStageFirst && stager) store_int_chunk(xr, xpart, hc < C, xrec + hc * kIW);
     __builtin_amdgcn_sched_barrier(0);
+
+    // The SwiGLU form (SWI) runs the loads and arithmetic twice on the same
+    // converted x: phase 0 the gate matrix (wq, scales, zeros), phase 1 the
+    // up matrix (wq2, scales2, zeros2), whose loads are issued after phase
+    // 0's arithmetic.
+    constexpr int NPH = SWI ? 2 : 1;
+    float acc[NPH][R];
+#pragma unroll
+    for (int ph = 0; ph < NPH; ++ph) {
+    const uint8_t *wqp = ph ? wq2 : wq;
+    const uint16_t *scp = ph ? scales2 : scales;
+    const uint8_t *zpp = ph ? zeros2 : zeros;
+    const __amdgpu_buffer_rsrc_t wq_r = raw_rsrc(wqp + (size_t)rbase * RB,
+        (uint32_t)std::min<uint64_t>((uint64_t)rows_left * RB, 0xFFFFFFFFull));
+    const __amdgpu_buffer_rsrc_t sc_r = raw_rsrc(scp + (size_t)rbase * G, rows_left * (uint32_t)G * 2u);
+    const __amdgpu_buffer_rsrc_t zp_r = raw_rsrc(zpp + (size_t)rbase * ZB, rows_left * (uint32_t)ZB);
     uint32_t sr[JP][R], zr[JP][R];
 #pragma unroll
     for (int j = 0; j < JP; ++j) {
@@ -578,23 +595,24 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
         }
     }
 
-    // Chunks of x past the first pass are loaded and converted here.
-    if (!kStageFirst && stager) store_int_chunk(xr, xpart, hc < C, xrec + hc * kIW);
-    if (MULTI)
-    for (int cb = kPass; cb < C; cb += kPass) {
-        if (cb + wave * kIntWaveChunks >= C) break;
-        const int c = cb + hc;
+    if (ph == 0) {
+        // Chunks of x past the first pass are loaded and converted here.
+        if (!kStageFirst && stager) store_int_chunk(xr, xpart, hc < C, xrec + hc * kIW);
+        if (MULTI)
+        for (int cb = kPass; cb < C; cb += kPass) {
+            if (cb + wave * kIntWaveChunks >= C) break;
+            const int c = cb + hc;
 #pragma unroll
-        for (int i = 0; i < kIntVPT / 4; ++i)
-            xr[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                x_r, (uint32_t)(c * 32 + xpart * kIntVPT + 4 * i) * 4u, 0, 0));
-        store_int_chunk(xr, xpart, c < C, xrec + c * kIW);
+            for (int i = 0; i < kIntVPT / 4; ++i)
+                xr[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                    x_r, (uint32_t)(c * 32 + xpart * kIntVPT + 4 * i) * 4u, 0, 0));
+            store_int_chunk(xr, xpart, c < C, xrec + c * kIW);
+        }
+        __syncthreads();
     }
-    __syncthreads();
 
-    float acc[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+    for (int r = 0; r < R; ++r) acc[ph][r] = 0.f;
 #pragma unroll
     for (int j = 0; j < JP; ++j) {
         const int c = lo + li + LPR * j;
@@ -637,24 +655,30 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
                     for (int d = 4; d >= 0; --d) tu = (tu << 4) + (uint32_t)a[d];   // mod 2^32; the sum fits int32
                     const int t = (int)tu;
                     const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sr[j][r]);
-                    acc[r] = __builtin_fmaf(s, (float)t * cscale, acc[r]);
+                    acc[ph][r] = __builtin_fmaf(s, (float)t * cscale, acc[ph][r]);
                 }
             }
         }
     }
+    }   // phases
 
     if constexpr (LPR < 64) {
         // Short rows: each slot's sum over its LPR lanes; lane 0 of the group stores.
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const float v = q4::group_sum<LPR>(acc[r]);
-            if (li == 0 && r * RG + rgl < nrows) store_y(y, gstart + r * RG + rgl, v, epi);
+            const float v = q4::group_sum<LPR>(acc[0][r]);
+            const float u = SWI ? q4::group_sum<LPR>(acc[NPH - 1][r]) : 0.f;
+            if (li == 0 && r * RG + rgl < nrows) {
+                if (SWI) y[gstart + r * RG + rgl] = silu(v) * u;
+                else store_y(y, gstart + r * RG + rgl, v, epi);
+            }
         }
         return;
     }
     constexpr int NQ = (R + 3) / 4;
-    float out[NQ];
-    q4::wave_reduce_rows<R>(acc, out);
+    float out[NQ], outu[NQ];
+    q4::wave_reduce_rows<R>(acc[0], out);
+    if (SWI) q4::wave_reduce_rows<R>(acc[NPH - 1], outu);
     const int h = lane >> 4;
     const bool writer = (lane & 15) == 0 && (R >= 4 || (h & (R == 2 ? 1 : 3)) == 0);
     if (S == 1) {
@@ -662,7 +686,10 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
                 const int rr = q4::reduced_row<R>(q, h);
-                if (rr < nrows) store_y(y, gstart + rr, out[q], epi);
+                if (rr < nrows) {
+                    if (SWI) y[gstart + rr] = silu(out[q]) * outu[q];
+                    else store_y(y, gstart + rr, out[q], epi);
+                }
             }
         }
         return;
@@ -908,6 +935,13 @@ __global__ __launch_bounds__(W * 64) void gemv_q4_intm_kernel(
     }
 }
 
+// One int4 matrix of a call.
+struct Q4Matrix {
+    const uint8_t *wq;
+    const uint16_t *scales;
+    const uint8_t *zeros;
+};
+
 struct Geometry {
     int M, LPR, JP, S, seg_chunks, segments, grid, rows_per_wave;
     bool integer;   // the exact integer path (gemv_q4_int_kernel, gemv_q4_intm_kernel)
@@ -916,6 +950,7 @@ struct Geometry {
     int mp;         // integer path, M > 1: M rounded up to 2, 4 or 8
     int epi;        // launch-time: finish a SwiGLU block in the store (see store_y)
     int fma_r;      // multiply-add path: row slots per wavefront
+    const Q4Matrix *swi;   // launch-time: the up matrix of a one-launch SwiGLU block
 };
 
 constexpr int kCUs = 256;   // compute units of an MI355X
@@ -1160,8 +1195,17 @@ void dispatch_jp(const Geometry &p, const float *x, const uint8_t *wq, const uin
 template <int W, int JP, int S, bool MULTI, int LPR = 64>
 void launch_integer(const Geometry &p, const float *x, const uint8_t *wq, const uint16_t *scales,
                     const uint8_t *zeros, float *y, int N, int K, int gshift, hipStream_t st) {
+    if constexpr (S == 1) {
+        if (p.swi) {
+            hipLaunchKernelGGL((gemv_q4_int_kernel<W, LPR, JP, row_slots(1), S, MULTI, true>), dim3(p.grid),
+                               dim3(W * 64), lds_bytes(p), st, x, wq, scales, zeros, y, N, K, gshift, p.rpg, 0,
+                               p.swi->wq, p.swi->scales, p.swi->zeros);
+            return;
+        }
+    }
     hipLaunchKernelGGL((gemv_q4_int_kernel<W, LPR, JP, row_slots(1), S, MULTI>), dim3(p.grid), dim3(W * 64),
-                       lds_bytes(p), st, x, wq, scales, zeros, y, N, K, gshift, p.rpg, p.epi);
+                       lds_bytes(p), st, x, wq, scales, zeros, y, N, K, gshift, p.rpg, p.epi,
+                       nullptr, nullptr, nullptr);
 }
 
 template <int W, int S>
@@ -1298,9 +1342,11 @@ namespace {
 
 // Launches one GEMV of a validated, checked call (see gemv_q4, gemv_q4_swiglu).
 int launch_gemv_q4(const float *x, const uint8_t *wq, const uint16_t *scales, const uint8_t *zeros,
-                   float *y, int M, int N, int K, int group_size, int epi, void *stream) {
+                   float *y, int M, int N, int K, int group_size, int epi, void *stream,
+                   const Q4Matrix *swi = nullptr) {
     Geometry p = plan(M, N, K, group_size);
     p.epi = epi;
+    p.swi = swi;
     const int gshift = group_size == 32 ? 0 : 2;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (p.integer && M > 1) {
@@ -1364,6 +1410,13 @@ extern "C" int gemv_q4_swiglu(const float *x, const uint8_t *wq_gate, const uint
     if (a != Q4_OK) return a;
     const int dev = q4::check_device();
     if (dev != Q4_OK) return dev;
+    // One activation row on the integer path without a K-split: one launch
+    // that converts x once and runs the gate and then the up matrix.
+    const Geometry p = plan(M, N, K, group_size);
+    if (M == 1 && p.integer && p.S == 1) {
+        const Q4Matrix up{wq_up, scales_up, zeros_up};
+        return launch_gemv_q4(x, wq_gate, scales_gate, zeros_gate, y, M, N, K, group_size, 0, stream, &up);
+    }
     const int r = launch_gemv_q4(x, wq_up, scales_up, zeros_up, y, M, N, K, group_size, 0, stream);
     if (r != Q4_OK) return r;
     return launch_gemv_q4(x, wq_gate, scales_gate, zeros_gate, y, M, N, K, group_size, 1, stream);
