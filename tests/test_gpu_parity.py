@@ -446,3 +446,31 @@ def test_every_geometry_the_tuner_may_pick(M, N, K, g):
             assert_within(y[:, rows], y_ref, b, f"{c['path']}/{c['waves']}/{c['ksplit']}")
     finally:
         q4.gemv_q4_clear_geometry()
+
+
+# ---------------------------------------------------------------- seeded random shapes
+
+def _random_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        M = int(rng.integers(1, 9))
+        g = int(rng.choice([32, 128]))
+        K = g * int(rng.integers(1, max(2, 12288 // g)))
+        N = int(rng.integers(1, 700))
+        out.append((M, N, K, g))
+    return out
+
+
+RANDOM_SHAPES = _random_shapes(40, 2024)
+
+
+@pytest.mark.parametrize("M,N,K,g", RANDOM_SHAPES, ids=[f"M{a}N{b}K{c}g{d}" for a, b, c, d in RANDOM_SHAPES])
+def test_gemv_q4_random_shapes(M, N, K, g):
+    """Seeded random shapes across every planner branch (both paths, 16/32/64
+    lanes per row, K-splits, x segments); each output within the tolerance."""
+    s = wl.Q4Shape(M, N, K, g, 0.002, 0.02)
+    d = wl.make_q4_problem(5000 + N + K, s)
+    y = run_q4(dev(d), g)
+    y_ref, b = oracle.gemv_q4(d["x"], d["wq"], d["scales"], d["zeros"], g)
+    assert_within(y, y_ref, b, f"M{M} N{N} K{K} g{g} path {q4.gemv_q4_path(M, N, K, g)}")
