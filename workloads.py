@@ -146,6 +146,54 @@ def make_exact_problem(seed: int, M: int, N: int, K: int, g: int,
     return d
 
 
+# Block formats named on the cera page (wgpu_gemv_bench, the block-geometry
+# table): format code, elements per block, bytes per block, and the byte
+# offsets of the binary16 fields that scale a block (layout only).
+BLOCK_FORMATS = {
+    "q4_0": (1, 32, 18, (0,)),
+    "q8_0": (2, 32, 34, (0,)),
+    "q4_k": (3, 256, 144, (0, 2)),
+    "q5_k": (4, 256, 176, (0, 2)),
+    "q6_k": (5, 256, 210, (208,)),
+}
+_STREAM_BLK, _STREAM_BLK_S = 31, 32
+
+# The cera page's decode-GEMV shapes (output rows, K), and the stream shape.
+BLOCK_SHAPES = (
+    (2816, 1024, "ffn gate/up"),
+    (1024, 2816, "ffn down"),
+    (1024, 1024, "attn qkv/out"),
+    (65536, 1024, "lm head"),
+)
+
+
+def block_row_bytes(fmt: str, K: int) -> int:
+    _, e, b, _ = BLOCK_FORMATS[fmt]
+    if K % e:
+        raise ValueError(f"K = {K} is not a multiple of the {fmt} block size {e}")
+    return K // e * b
+
+
+def make_block_weights(seed: int, fmt: str, N: int, K: int, s_lo: float = 0.002,
+                       s_hi: float = 0.01, index: int = 0) -> np.ndarray:
+    """One [N, K] matrix in a block format: uint8 [N, (K / elems) * bytes].
+
+    Every byte is uniform over 0..255 (codes, packed sub-block scales and
+    mins, int8 values), except the binary16 fields that scale a block, which
+    are uniform in [s_lo, s_hi] rounded to binary16, so that no block holds an
+    infinity or a NaN.  (The cera page keeps every byte in 0x30..0x37 for the
+    same reason; uniform bytes exercise every code.)
+    """
+    _, e, b, f16_at = BLOCK_FORMATS[fmt]
+    rb = block_row_bytes(fmt, K)
+    w = _rng(seed, _STREAM_BLK, index).integers(0, 256, size=(N, K // e, b), dtype=np.uint8)
+    s = _rng(seed, _STREAM_BLK_S, index).uniform(s_lo, s_hi, size=(N, K // e, len(f16_at)))
+    sb = s.astype(np.float16).view(np.uint8).reshape(N, K // e, len(f16_at), 2)
+    for i, off in enumerate(f16_at):
+        w[:, :, off:off + 2] = sb[:, :, i, :]
+    return w.reshape(N, rb)
+
+
 def make_probe_buffer(n_floats: int, seed: int = 0x5EED0004) -> np.ndarray:
     """A float32 buffer for the read probe, values uniform in [0, 1)."""
     return _rng(seed, 21, 0).random(n_floats, dtype=np.float32)
