@@ -24,10 +24,18 @@ LIB_PATH = os.path.join(_HERE, "libq4gemv.so")
 
 Q4_OK, Q4_EINVAL, Q4_ENULL, Q4_EALIGN, Q4_EDEVICE, Q4_ELAUNCH = 0, -1, -2, -3, -4, -5
 
-# Exported C symbols, in the order include/q4gemv.h declares them.
+# Exported C symbols, in the order include/q4gemv.h and include/q4blocks.h
+# declare them.
 EXPORTS = ("gemv_q4", "gemv_q4_swiglu", "gemv_f32", "dequant_q4", "read_reduce", "write_fill",
            "gemv_q4_geometry", "gemv_q4_path", "q4_strerror", "q4_abi_version",
-           "gemv_q4_set_geometry", "gemv_q4_clear_geometry")
+           "gemv_q4_set_geometry", "gemv_q4_clear_geometry",
+           "block_geometry", "gemv_block", "dequant_block", "gemv_block_set_config",
+           "gemv_block_config")
+
+# Block formats of include/q4blocks.h.
+BLK_Q4_0, BLK_Q8_0, BLK_Q4_K, BLK_Q5_K, BLK_Q6_K = 1, 2, 3, 4, 5
+BLOCK_FORMATS = {"q4_0": BLK_Q4_0, "q8_0": BLK_Q8_0, "q4_k": BLK_Q4_K, "q5_k": BLK_Q5_K,
+                 "q6_k": BLK_Q6_K}
 
 Q4_PATH_FMA, Q4_PATH_INTEGER = 0, 1
 
@@ -61,12 +69,18 @@ def lib() -> ctypes.CDLL:
     L.gemv_q4_path.argtypes = [I, I, I, I]
     L.gemv_q4_set_geometry.argtypes = [I, I, I, I, I, I, I]
     L.gemv_q4_clear_geometry.argtypes = []
+    L.block_geometry.argtypes = [I, IP, IP]
+    L.gemv_block.argtypes = [I, P, P, P, I, I, I, P]
+    L.dequant_block.argtypes = [I, P, P, I, I, P]
+    L.gemv_block_set_config.argtypes = [I, I, I]
+    L.gemv_block_config.argtypes = [I, IP, IP]
     L.q4_strerror.argtypes = [I]
     L.q4_strerror.restype = ctypes.c_char_p
     L.q4_abi_version.argtypes = []
     for f in ("gemv_q4", "gemv_q4_swiglu", "gemv_f32", "dequant_q4", "read_reduce", "write_fill",
               "gemv_q4_geometry", "gemv_q4_path", "q4_abi_version",
-              "gemv_q4_set_geometry", "gemv_q4_clear_geometry"):
+              "gemv_q4_set_geometry", "gemv_q4_clear_geometry", "block_geometry", "gemv_block",
+              "dequant_block", "gemv_block_set_config", "gemv_block_config"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -247,3 +261,63 @@ def gemv_q4_set_geometry(M: int, N: int, K: int, group_size: int, path: int, wav
 def gemv_q4_clear_geometry() -> None:
     """Forget every geometry fixed by gemv_q4_set_geometry."""
     _check("gemv_q4_clear_geometry", lib().gemv_q4_clear_geometry())
+
+
+# ---------------------------------------------------------------- block formats
+
+def _fmt(fmt) -> int:
+    if isinstance(fmt, str):
+        if fmt not in BLOCK_FORMATS:
+            raise ValueError(f"unknown block format {fmt!r}")
+        return BLOCK_FORMATS[fmt]
+    return int(fmt)
+
+
+def block_geometry(fmt) -> tuple[int, int]:
+    """(elements, bytes) of one block of the format (host-only)."""
+    e, b = ctypes.c_int(), ctypes.c_int()
+    _check("block_geometry", lib().block_geometry(_fmt(fmt), ctypes.byref(e), ctypes.byref(b)))
+    return e.value, b.value
+
+
+def _block_matrix(fmt, w: torch.Tensor, K: int, dev=None) -> tuple[int, int]:
+    _need(w, "w", (torch.uint8,), dev)
+    e, b = block_geometry(fmt)
+    if w.dim() != 2 or K % e or w.shape[1] != K // e * b:
+        raise ValueError(f"w must be [N, K / {e} * {b}] bytes for K = {K}, got {tuple(w.shape)}")
+    return w.shape[0], K // e * b
+
+
+def gemv_block(fmt, x: torch.Tensor, w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """y[1, N] = x[1, K] . W^T for a block-format matrix w uint8 [N, row_bytes]."""
+    _need(x, "x", (torch.float32,))
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    M, K = x.shape
+    N, _ = _block_matrix(fmt, w, K, x.device)
+    out = _out(out, M, N, x.device)
+    _check("gemv_block", lib().gemv_block(_fmt(fmt), _ptr(x), _ptr(w), _ptr(out), M, N, K,
+                                          _stream(x.device)))
+    return out
+
+
+def dequant_block(fmt, w: torch.Tensor, K: int) -> torch.Tensor:
+    """W float32 [N, K], bit-exact, from a block-format matrix."""
+    N, _ = _block_matrix(fmt, w, K)
+    out = torch.empty((N, K), dtype=torch.float32, device=w.device)
+    _check("dequant_block", lib().dequant_block(_fmt(fmt), _ptr(w), _ptr(out), N, K,
+                                                _stream(w.device)))
+    return out
+
+
+def gemv_block_set_config(fmt, rows_per_wave: int = 0, waves_per_group: int = 0) -> None:
+    """Rows per wavefront (1, 2, 4) and wavefronts per workgroup (4, 8) of
+    gemv_block for one format; 0, 0 restores the default (host-only)."""
+    _check("gemv_block_set_config", lib().gemv_block_set_config(_fmt(fmt), rows_per_wave,
+                                                                waves_per_group))
+
+
+def gemv_block_config(fmt) -> tuple[int, int]:
+    r, wv = ctypes.c_int(), ctypes.c_int()
+    _check("gemv_block_config", lib().gemv_block_config(_fmt(fmt), ctypes.byref(r), ctypes.byref(wv)))
+    return r.value, wv.value

@@ -1,0 +1,596 @@
+// gemv_blocks.hip -- decode GEMV and dequantiser over the block quantisation
+// formats of the cera page's decode benchmark (Q4_0, Q8_0, Q4_K, Q5_K, Q6_K),
+// for gfx950.  The formats are the published GGML block formats of those
+// names; their layouts are spelled out in q4blocks.h.
+//
+// Mapping onto CDNA4 (one activation row; a streaming dot product, no MFMA):
+//   * A lane owns a 64-element unit of a row: two blocks of Q4_0 or Q8_0, or
+//     a quarter of a 256-element K-format block.  A wavefront covers 64
+//     consecutive units (4096 elements) of R rows per pass; longer rows take
+//     several passes.  Consecutive lanes read consecutive unit bytes, so one
+//     wavefront's loads for a row cover one contiguous stretch of it.
+//   * The unit's 64 x values stay in the lane's registers for all R rows of
+//     the pass.  Every workgroup stages x once in LDS with one float4 of
+//     padding per 16, so that 16 consecutive lanes reading their units'
+//     slices hit 16 different bank groups.
+//   * Unit bytes come in with dword-aligned buffer loads.  Fields that start
+//     2 bytes past a dword boundary (the first block of a Q4_0 or Q8_0 pair,
+//     every odd Q6_K block) are shifted into place with v_alignbyte_b32;
+//     every Q6_K load stays inside its own block.
+//   * Each weight is an exact small integer -- the code minus its offset
+//     (8 for Q4_0, 32 for Q6_K, none otherwise) -- times x, so a code equal
+//     to its offset contributes exactly zero.  Sums run in fp32 per 16 or 32
+//     elements and take their block or sub-block scale once; the Q4_K/Q5_K
+//     min term is dmin * m_j times the sub-block's sum of x.
+//   * The dequantiser decodes through the same per-format code and forms
+//     each weight as fma(scale, integer, -min), one rounding of its exact
+//     value.
+#include "q4_common.h"
+#include "q4_device.h"
+#include "q4blocks.h"
+
+#include <algorithm>
+
+namespace {
+
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Buffer resource for a raw byte range: reads past `bytes` return zero.
+__device__ __forceinline__ rsrc_t raw_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+
+constexpr int kNonTemporal = 2;   // weights are read once
+
+__device__ __forceinline__ u32x4_t ld128(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal);
+}
+__device__ __forceinline__ uint32_t ld32(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kNonTemporal);
+}
+__device__ __forceinline__ uint32_t ld16(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
+__device__ __forceinline__ float f16lo(uint32_t v) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
+}
+__device__ __forceinline__ float f16hi(uint32_t v) { return f16lo(v >> 16); }
+
+// Bytes sh .. sh+3 of the 8-byte little-endian pair (lo, hi).
+__device__ __forceinline__ uint32_t realign(uint32_t lo, uint32_t hi, uint32_t sh) {
+    return __builtin_amdgcn_alignbyte(hi, lo, sh);
+}
+
+// Signed field of `bits` bits at bit `at`, as a float (exact).  The builtin
+// returns the sign-extended field in an unsigned type: convert it as int.
+__device__ __forceinline__ float sfield(uint32_t v, int at, int bits) {
+    return (float)(int)__builtin_amdgcn_sbfe(v, at, bits);
+}
+// Byte j of v as a float (v_cvt_f32_ubyte<j>).
+__device__ __forceinline__ float ubyte(uint32_t v, int j) { return (float)((v >> (8 * j)) & 0xFFu); }
+
+// ---------------------------------------------------------------------------
+// Per-format unit decoding.  For unit u of a row starting at byte `ro` of a
+// buffer resource:
+//   load(raw, rs, ro, u)    issues the unit's loads
+//   xstart(u, run)          first element of run 0 / run 1 (32 elements each)
+//                           of the lane's 64 x values
+//   affine(raw, u, a, b)    weight of lane element e = a[e/16] * v + b[e/16]
+//                           (b = -dmin * m_j, or -0 where there is no min)
+//   visit(raw, u, fn)       fn(e, v) for e = 0..63 with v the exact integer
+// ---------------------------------------------------------------------------
+
+struct FmtQ4_0 {
+    static constexpr bool kMin = false;
+    struct Raw { uint32_t v[9]; };
+    __device__ static void load(Raw &r, rsrc_t rs, uint32_t ro, int u) {
+        const uint32_t o = ro + 36u * (uint32_t)u;      // two 18-byte blocks
+        const u32x4_t a = ld128(rs, o), b = ld128(rs, o + 16);
+        r.v[0] = a.x; r.v[1] = a.y; r.v[2] = a.z; r.v[3] = a.w;
+        r.v[4] = b.x; r.v[5] = b.y; r.v[6] = b.z; r.v[7] = b.w;
+        r.v[8] = ld32(rs, o + 32);
+    }
+    __device__ static int xstart(int u, int run) { return 64 * u + 32 * run; }
+    __device__ static void affine(const Raw &r, int, float (&a)[4], float (&b)[4]) {
+        const float dA = f16lo(r.v[0]), dB = f16hi(r.v[4]);
+        a[0] = a[1] = dA;
+        a[2] = a[3] = dB;
+        b[0] = b[1] = b[2] = b[3] = -0.f;   // fma(a, v, -0) keeps the sign of a zero product
+    }
+    template <class Fn> __device__ static void visit(const Raw &r, int, Fn &&fn) {
+        // Nibble c ^ 8, sign-extended, is c - 8.
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t ta = realign(r.v[i], r.v[i + 1], 2) ^ 0x88888888u;   // block A bytes 2..17
+            const uint32_t tb = r.v[5 + i] ^ 0x88888888u;                        // block B bytes 20..35
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                fn(4 * i + j, sfield(ta, 8 * j, 4));
+                fn(16 + 4 * i + j, sfield(ta, 8 * j + 4, 4));
+                fn(32 + 4 * i + j, sfield(tb, 8 * j, 4));
+                fn(48 + 4 * i + j, sfield(tb, 8 * j + 4, 4));
+            }
+        }
+    }
+};
+
+struct FmtQ8_0 {
+    static constexpr bool kMin = false;
+    struct Raw { uint32_t v[17]; };
+    __device__ static void load(Raw &r, rsrc_t rs, uint32_t ro, int u) {
+        const uint32_t o = ro + 68u * (uint32_t)u;      // two 34-byte blocks
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x4_t t = ld128(rs, o + 16 * i);
+            r.v[4 * i] = t.x; r.v[4 * i + 1] = t.y; r.v[4 * i + 2] = t.z; r.v[4 * i + 3] = t.w;
+        }
+        r.v[16] = ld32(rs, o + 64);
+    }
+    __device__ static int xstart(int u, int run) { return 64 * u + 32 * run; }
+    __device__ static void affine(const Raw &r, int, float (&a)[4], float (&b)[4]) {
+        const float dA = f16lo(r.v[0]), dB = f16hi(r.v[8]);
+        a[0] = a[1] = dA;
+        a[2] = a[3] = dB;
+        b[0] = b[1] = b[2] = b[3] = -0.f;   // fma(a, v, -0) keeps the sign of a zero product
+    }
+    template <class Fn> __device__ static void visit(const Raw &r, int, Fn &&fn) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t qa = realign(r.v[i], r.v[i + 1], 2);   // block A bytes 2..33
+            const uint32_t qb = r.v[9 + i];                       // block B bytes 36..67
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                fn(4 * i + j, sfield(qa, 8 * j, 8));
+                fn(32 + 4 * i + j, sfield(qb, 8 * j, 8));
+            }
+        }
+    }
+};
+
+// 6-bit scale and min of sub-block j from the 12 packed bytes, held in
+// header dwords 1..3 (bytes 4..15 of a Q4_K / Q5_K block).
+__device__ __forceinline__ void k_scale_min(uint32_t h1, uint32_t h2, uint32_t h3, int j,
+                                            float &s, float &m) {
+    const uint32_t sh = (uint32_t)(j & 3) * 8u;
+    const uint32_t b1 = (h1 >> sh) & 0xFFu, b2 = (h2 >> sh) & 0xFFu, b3 = (h3 >> sh) & 0xFFu;
+    uint32_t si, mi;
+    if (j < 4) {
+        si = b1 & 63u;
+        mi = b2 & 63u;
+    } else {
+        si = (b3 & 15u) | ((b1 >> 6) << 4);
+        mi = (b3 >> 4) | ((b2 >> 6) << 4);
+    }
+    s = (float)si;
+    m = (float)mi;
+}
+
+// Lane's quarter of a K-format block: sub-blocks 2p (low nibbles, lane
+// elements 0..31) and 2p + 1 (high nibbles, lane elements 32..63).
+__device__ __forceinline__ void k_affine(const uint32_t *hd, int u, float (&a)[4], float (&b)[4]) {
+    const int p = u & 3;
+    const float d = f16lo(hd[0]), dmin = f16hi(hd[0]);
+    float s0, m0, s1, m1;
+    k_scale_min(hd[1], hd[2], hd[3], 2 * p, s0, m0);
+    k_scale_min(hd[1], hd[2], hd[3], 2 * p + 1, s1, m1);
+    a[0] = a[1] = d * s0;          // exact: 11 + 6 significant bits
+    a[2] = a[3] = d * s1;
+    b[0] = b[1] = -(dmin * m0);
+    b[2] = b[3] = -(dmin * m1);
+}
+
+struct FmtQ4_K {
+    static constexpr bool kMin = true;
+    struct Raw { uint32_t v[12]; };
+    __device__ static void load(Raw &r, rsrc_t rs, uint32_t ro, int u) {
+        const uint32_t ob = ro + 144u * (uint32_t)(u >> 2);
+        const uint32_t oq = ob + 16u + 32u * (uint32_t)(u & 3);
+        const u32x4_t h = ld128(rs, ob), c0 = ld128(rs, oq), c1 = ld128(rs, oq + 16);
+        r.v[0] = h.x; r.v[1] = h.y; r.v[2] = h.z; r.v[3] = h.w;
+        r.v[4] = c0.x; r.v[5] = c0.y; r.v[6] = c0.z; r.v[7] = c0.w;
+        r.v[8] = c1.x; r.v[9] = c1.y; r.v[10] = c1.z; r.v[11] = c1.w;
+    }
+    __device__ static int xstart(int u, int run) { return 64 * u + 32 * run; }
+    __device__ static void affine(const Raw &r, int u, float (&a)[4], float (&b)[4]) {
+        k_affine(r.v, u, a, b);
+    }
+    template <class Fn> __device__ static void visit(const Raw &r, int, Fn &&fn) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t lo = r.v[4 + i] & 0x0F0F0F0Fu;
+            const uint32_t hi = (r.v[4 + i] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                fn(4 * i + j, ubyte(lo, j));
+                fn(32 + 4 * i + j, ubyte(hi, j));
+            }
+        }
+    }
+};
+
+struct FmtQ5_K {
+    static constexpr bool kMin = true;
+    struct Raw { uint32_t v[20]; };
+    __device__ static void load(Raw &r, rsrc_t rs, uint32_t ro, int u) {
+        const uint32_t ob = ro + 176u * (uint32_t)(u >> 2);
+        const uint32_t oq = ob + 48u + 32u * (uint32_t)(u & 3);
+        const u32x4_t h = ld128(rs, ob), e0 = ld128(rs, ob + 16), e1 = ld128(rs, ob + 32);
+        const u32x4_t c0 = ld128(rs, oq), c1 = ld128(rs, oq + 16);
+        r.v[0] = h.x; r.v[1] = h.y; r.v[2] = h.z; r.v[3] = h.w;
+        r.v[4] = e0.x; r.v[5] = e0.y; r.v[6] = e0.z; r.v[7] = e0.w;
+        r.v[8] = e1.x; r.v[9] = e1.y; r.v[10] = e1.z; r.v[11] = e1.w;
+        r.v[12] = c0.x; r.v[13] = c0.y; r.v[14] = c0.z; r.v[15] = c0.w;
+        r.v[16] = c1.x; r.v[17] = c1.y; r.v[18] = c1.z; r.v[19] = c1.w;
+    }
+    __device__ static int xstart(int u, int run) { return 64 * u + 32 * run; }
+    __device__ static void affine(const Raw &r, int u, float (&a)[4], float (&b)[4]) {
+        k_affine(r.v, u, a, b);
+    }
+    template <class Fn> __device__ static void visit(const Raw &r, int u, Fn &&fn) {
+        const uint32_t p2 = 2u * (uint32_t)(u & 3);     // fifth bit of sub-block 2p, 2p + 1
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t q = r.v[12 + i], qh = r.v[4 + i];
+            const uint32_t lo = (q & 0x0F0F0F0Fu) | (((qh >> p2) & 0x01010101u) << 4);
+            const uint32_t hi = ((q >> 4) & 0x0F0F0F0Fu) | (((qh >> (p2 + 1)) & 0x01010101u) << 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                fn(4 * i + j, ubyte(lo, j));
+                fn(32 + 4 * i + j, ubyte(hi, j));
+            }
+        }
+    }
+};
+
+// Q6_K: unit u is block b = u / 4, half hf = (u / 2) % 2, side s = u % 2.
+// The lane takes the 32 ql bytes 64 hf + 32 s .. +31 with both nibbles:
+// low nibbles are elements 128 hf + 32 s + l (quarter s), high nibbles
+// elements 128 hf + 64 + 32 s + l (quarter s + 2), and the 32 qh bytes of
+// its half.  Blocks are 210 bytes, so a block may start 2 bytes past a
+// dword boundary; its ql and qh runs are read as 9 aligned dwords each and
+// shifted into place, its scales and d with 16-bit loads.
+struct FmtQ6_K {
+    static constexpr bool kMin = false;
+    struct Raw { uint32_t l[9], h[9], sa, sb, d, sh; };
+    __device__ static void load(Raw &r, rsrc_t rs, uint32_t ro, int u) {
+        const uint32_t hf = (uint32_t)(u >> 1) & 1u, s = (uint32_t)u & 1u;
+        const uint32_t ob = ro + 210u * (uint32_t)(u >> 2);
+        const uint32_t o1 = ob + 64u * hf + 32u * s, o2 = ob + 128u + 32u * hf;
+        const uint32_t a1 = o1 & ~3u, a2 = o2 & ~3u;   // o1, o2 differ by a multiple of 4
+        r.sh = o1 & 3u;
+        const u32x4_t l0 = ld128(rs, a1), l1 = ld128(rs, a1 + 16);
+        const u32x4_t h0 = ld128(rs, a2), h1 = ld128(rs, a2 + 16);
+        r.l[0] = l0.x; r.l[1] = l0.y; r.l[2] = l0.z; r.l[3] = l0.w;
+        r.l[4] = l1.x; r.l[5] = l1.y; r.l[6] = l1.z; r.l[7] = l1.w;
+        r.l[8] = ld32(rs, a1 + 32);
+        r.h[0] = h0.x; r.h[1] = h0.y; r.h[2] = h0.z; r.h[3] = h0.w;
+        r.h[4] = h1.x; r.h[5] = h1.y; r.h[6] = h1.z; r.h[7] = h1.w;
+        r.h[8] = ld32(rs, a2 + 32);
+        r.sa = ld16(rs, ob + 192u + 8u * hf + 2u * s);   // scales of quarter s, both 16-element halves
+        r.sb = ld16(rs, ob + 196u + 8u * hf + 2u * s);   // scales of quarter s + 2
+        r.d = ld16(rs, ob + 208u);
+    }
+    __device__ static int xstart(int u, int run) {
+        return 256 * (u >> 2) + 128 * ((u >> 1) & 1) + 32 * (u & 1) + 64 * run;
+    }
+    __device__ static void affine(const Raw &r, int, float (&a)[4], float (&b)[4]) {
+        const float d = f16lo(r.d);
+        a[0] = d * sfield(r.sa, 0, 8);     // exact: 11 + 8 significant bits
+        a[1] = d * sfield(r.sa, 8, 8);
+        a[2] = d * sfield(r.sb, 0, 8);
+        a[3] = d * sfield(r.sb, 8, 8);
+        b[0] = b[1] = b[2] = b[3] = -0.f;   // fma(a, v, -0) keeps the sign of a zero product
+    }
+    template <class Fn> __device__ static void visit(const Raw &r, int u, Fn &&fn) {
+        const uint32_t s2 = 2u * ((uint32_t)u & 1u);
+        // A 6-bit code c ^ 32, sign-extended, is c - 32.
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t ql = realign(r.l[i], r.l[i + 1], r.sh);
+            const uint32_t qh = realign(r.h[i], r.h[i + 1], r.sh);
+            const uint32_t ca = ((ql & 0x0F0F0F0Fu) | (((qh >> s2) & 0x03030303u) << 4)) ^ 0x20202020u;
+            const uint32_t cb = (((ql >> 4) & 0x0F0F0F0Fu) | (((qh >> (s2 + 4)) & 0x03030303u) << 4)) ^
+                                0x20202020u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                fn(4 * i + j, sfield(ca, 8 * j, 6));
+                fn(32 + 4 * i + j, sfield(cb, 8 * j, 6));
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// GEMV kernel.  R rows per wavefront, W wavefronts per workgroup.
+// ---------------------------------------------------------------------------
+
+// LDS slot of x's float4 number f: one float4 of padding after every 16.
+__device__ __forceinline__ int xslot(int f) { return f + (f >> 4); }
+
+template <class T, int R, int W>
+__global__ __launch_bounds__(W * 64) void gemv_blk_kernel(const float *__restrict__ x,
+                                                          const uint8_t *__restrict__ w,
+                                                          float *__restrict__ y, int N, int K,
+                                                          uint32_t RB) {
+    extern __shared__ float blds[];
+    f32x4_t *xs = reinterpret_cast<f32x4_t *>(blds);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int U = K >> 6;                 // units per row
+    const int nx4 = K >> 2;
+    const int row0 = (blockIdx.x * W + wave) * R;    // may be >= N
+    const int rbase = min(row0, N - 1);
+
+    // Resource based 16-byte aligned at (or just before) the wavefront's
+    // first row; rows past N re-read row N - 1 and are not stored.
+    const uint64_t byte0 = (uint64_t)rbase * RB;
+    const uint32_t delta = (uint32_t)(byte0 & 15u);
+    const uint64_t span = (uint64_t)(N - rbase) * RB + delta;
+    const rsrc_t wr = raw_rsrc(w + (byte0 - delta), (uint32_t)std::min<uint64_t>(span, 0xFFFFFFFFull));
+    uint32_t ro[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) ro[r] = delta + (uint32_t)(min(row0 + r, N - 1) - rbase) * RB;
+
+    // x: the first 4096 elements go to registers ahead of the weight loads
+    // (loads retire in issue order), the rest after them.
+    const f32x4_t *x4 = reinterpret_cast<const f32x4_t *>(x);
+    constexpr int XB = 1024 / (W * 64);
+    f32x4_t xr[XB];
+#pragma unroll
+    for (int t = 0; t < XB; ++t) {
+        const int i = t * W * 64 + tid;
+        xr[t] = i < nx4 ? x4[i] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    typename T::Raw raw[R];
+    {
+        const int uc = min(lane, U - 1);
+#pragma unroll
+        for (int r = 0; r < R; ++r) T::load(raw[r], wr, ro[r], uc);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < XB; ++t) {
+        const int i = t * W * 64 + tid;
+        if (i < nx4) xs[xslot(i)] = xr[t];
+    }
+    for (int i = XB * W * 64 + tid; i < nx4; i += W * 64) xs[xslot(i)] = x4[i];
+    __syncthreads();
+
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+    const int P = (U + 63) >> 6;
+    for (int pass = 0; pass < P; ++pass) {
+        const int u = pass * 64 + lane;
+        const int uc = min(u, U - 1);
+        if (pass > 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) T::load(raw[r], wr, ro[r], uc);
+        }
+        float xv[64];
+#pragma unroll
+        for (int run = 0; run < 2; ++run) {
+            const int f = T::xstart(uc, run) >> 2;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const f32x4_t v = xs[xslot(f + i)];
+                xv[32 * run + 4 * i] = v.x;
+                xv[32 * run + 4 * i + 1] = v.y;
+                xv[32 * run + 4 * i + 2] = v.z;
+                xv[32 * run + 4 * i + 3] = v.w;
+            }
+        }
+        float sx[4];
+        if constexpr (T::kMin) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                float t = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) t += xv[16 * k + i];
+                sx[k] = t;
+            }
+        }
+        if (u < U) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                float a[4], b[4];
+                T::affine(raw[r], uc, a, b);
+                float dk[4] = {0.f, 0.f, 0.f, 0.f};
+                T::visit(raw[r], uc, [&](int e, float v) { dk[e >> 4] = __builtin_fmaf(v, xv[e], dk[e >> 4]); });
+                float c = acc[r];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    c = __builtin_fmaf(a[k], dk[k], c);
+                    if constexpr (T::kMin) c = __builtin_fmaf(b[k], sx[k], c);
+                }
+                acc[r] = c;
+            }
+        }
+    }
+
+    constexpr int NQ = (R + 3) / 4;
+    float out[NQ];
+    q4::wave_reduce_rows<R>(acc, out);
+    const int h = lane >> 4;
+    const bool writer = (lane & 15) == 0 && (R >= 4 || (h & (R == 2 ? 1 : 3)) == 0);
+    if (writer) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int row = row0 + q4::reduced_row<R>(q, h);
+            if (row < N) y[row] = out[q];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Dequantiser: one thread per unit, 256 consecutive units per workgroup.
+// ---------------------------------------------------------------------------
+
+constexpr int kDqBlock = 256;
+
+template <class T>
+__global__ __launch_bounds__(kDqBlock) void dequant_blk_kernel(const uint8_t *__restrict__ w,
+                                                               float *__restrict__ out, int N, int K,
+                                                               uint32_t RB) {
+    const int64_t U = K >> 6;
+    const int64_t t0 = (int64_t)blockIdx.x * kDqBlock;
+    const int64_t t = t0 + threadIdx.x;
+    const int64_t n0 = t0 / U;
+    const int64_t nl = std::min<int64_t>((t0 + kDqBlock - 1) / U, N - 1);
+    const uint64_t byte0 = (uint64_t)n0 * RB;
+    const uint32_t delta = (uint32_t)(byte0 & 15u);
+    const uint64_t span = (uint64_t)(nl - n0 + 1) * RB + delta;
+    const rsrc_t wr = raw_rsrc(w + (byte0 - delta), (uint32_t)std::min<uint64_t>(span, 0xFFFFFFFFull));
+    if (t >= (int64_t)N * U) return;
+    const int64_t n = t / U;
+    const int u = (int)(t - n * U);
+    typename T::Raw raw;
+    T::load(raw, wr, delta + (uint32_t)(n - n0) * RB, u);
+    float a[4], b[4];
+    T::affine(raw, u, a, b);
+    float v[64];
+    T::visit(raw, u, [&](int e, float c) { v[e] = __builtin_fmaf(a[e >> 4], c, b[e >> 4]); });
+#pragma unroll
+    for (int run = 0; run < 2; ++run) {
+        f32x4_t *dst = reinterpret_cast<f32x4_t *>(out + n * K + T::xstart(u, run));
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            dst[i] = f32x4_t{v[32 * run + 4 * i], v[32 * run + 4 * i + 1], v[32 * run + 4 * i + 2],
+                             v[32 * run + 4 * i + 3]};
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+
+constexpr int kMaxK = 32768;
+
+struct Geo { int elems, bytes; };
+
+bool geometry_of(int f, Geo &g) {
+    switch (f) {
+    case BLK_Q4_0: g = {32, 18}; return true;
+    case BLK_Q8_0: g = {32, 34}; return true;
+    case BLK_Q4_K: g = {256, 144}; return true;
+    case BLK_Q5_K: g = {256, 176}; return true;
+    case BLK_Q6_K: g = {256, 210}; return true;
+    default: return false;
+    }
+}
+
+struct Cfg { int R, W; };
+// Default rows per wavefront and wavefronts per workgroup, per format.
+constexpr Cfg kDefault[6] = {{0, 0}, {4, 4}, {2, 4}, {4, 4}, {2, 4}, {2, 4}};
+Cfg g_cfg[6] = {{0, 0}, {4, 4}, {2, 4}, {4, 4}, {2, 4}, {2, 4}};
+
+bool cfg_ok(int R, int W) { return (R == 1 || R == 2 || R == 4) && (W == 4 || W == 8); }
+
+template <class T, int R, int W>
+void launch_w(const float *x, const uint8_t *w, float *y, int N, int K, uint32_t RB, hipStream_t st) {
+    const int grid = (N + R * W - 1) / (R * W);
+    const size_t lds = (size_t)(K / 4 + K / 64) * 16;
+    hipLaunchKernelGGL((gemv_blk_kernel<T, R, W>), dim3(grid), dim3(W * 64), lds, st, x, w, y, N, K, RB);
+}
+
+template <class T>
+void launch_fmt(Cfg c, const float *x, const uint8_t *w, float *y, int N, int K, uint32_t RB,
+                hipStream_t st) {
+    if (c.W == 8) {
+        if (c.R == 1) launch_w<T, 1, 8>(x, w, y, N, K, RB, st);
+        else if (c.R == 2) launch_w<T, 2, 8>(x, w, y, N, K, RB, st);
+        else launch_w<T, 4, 8>(x, w, y, N, K, RB, st);
+    } else {
+        if (c.R == 1) launch_w<T, 1, 4>(x, w, y, N, K, RB, st);
+        else if (c.R == 2) launch_w<T, 2, 4>(x, w, y, N, K, RB, st);
+        else launch_w<T, 4, 4>(x, w, y, N, K, RB, st);
+    }
+}
+
+template <class T>
+void launch_dq(const uint8_t *w, float *out, int N, int K, uint32_t RB, hipStream_t st) {
+    const int64_t units = (int64_t)N * (K >> 6);
+    const int grid = (int)((units + kDqBlock - 1) / kDqBlock);
+    hipLaunchKernelGGL((dequant_blk_kernel<T>), dim3(grid), dim3(kDqBlock), 0, st, w, out, N, K, RB);
+}
+
+int check_k(int K) { return (K >= 256 && K <= kMaxK && K % 256 == 0) ? Q4_OK : Q4_EINVAL; }
+
+}  // namespace
+
+extern "C" int block_geometry(int format, int *elems, int *bytes) {
+    if (!elems || !bytes) return Q4_ENULL;
+    Geo g;
+    if (!geometry_of(format, g)) return Q4_EINVAL;
+    *elems = g.elems;
+    *bytes = g.bytes;
+    return Q4_OK;
+}
+
+extern "C" int gemv_block(int format, const float *x, const uint8_t *w, float *y, int M, int N,
+                          int K, void *stream) {
+    Geo g;
+    if (!geometry_of(format, g)) return Q4_EINVAL;
+    if (M != 1 || N < 0 || check_k(K) != Q4_OK) return Q4_EINVAL;
+    if (N == 0) return Q4_OK;
+    if (!x || !w || !y) return Q4_ENULL;
+    if (!q4::aligned(x, 16) || !q4::aligned(w, 16) || !q4::aligned(y, 4)) return Q4_EALIGN;
+    if (int st = q4::check_device(); st != Q4_OK) return st;
+    const uint32_t RB = (uint32_t)(K / g.elems * g.bytes);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const Cfg c = g_cfg[format];
+    switch (format) {
+    case BLK_Q4_0: launch_fmt<FmtQ4_0>(c, x, w, y, N, K, RB, st); break;
+    case BLK_Q8_0: launch_fmt<FmtQ8_0>(c, x, w, y, N, K, RB, st); break;
+    case BLK_Q4_K: launch_fmt<FmtQ4_K>(c, x, w, y, N, K, RB, st); break;
+    case BLK_Q5_K: launch_fmt<FmtQ5_K>(c, x, w, y, N, K, RB, st); break;
+    default: launch_fmt<FmtQ6_K>(c, x, w, y, N, K, RB, st); break;
+    }
+    return q4::launch_status();
+}
+
+extern "C" int dequant_block(int format, const uint8_t *w, float *w_out, int N, int K, void *stream) {
+    Geo g;
+    if (!geometry_of(format, g)) return Q4_EINVAL;
+    if (N < 0 || check_k(K) != Q4_OK) return Q4_EINVAL;
+    if (N == 0) return Q4_OK;
+    if (!w || !w_out) return Q4_ENULL;
+    if (!q4::aligned(w, 16) || !q4::aligned(w_out, 16)) return Q4_EALIGN;
+    if (int st = q4::check_device(); st != Q4_OK) return st;
+    const uint32_t RB = (uint32_t)(K / g.elems * g.bytes);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    switch (format) {
+    case BLK_Q4_0: launch_dq<FmtQ4_0>(w, w_out, N, K, RB, st); break;
+    case BLK_Q8_0: launch_dq<FmtQ8_0>(w, w_out, N, K, RB, st); break;
+    case BLK_Q4_K: launch_dq<FmtQ4_K>(w, w_out, N, K, RB, st); break;
+    case BLK_Q5_K: launch_dq<FmtQ5_K>(w, w_out, N, K, RB, st); break;
+    default: launch_dq<FmtQ6_K>(w, w_out, N, K, RB, st); break;
+    }
+    return q4::launch_status();
+}
+
+extern "C" int gemv_block_set_config(int format, int rows_per_wave, int waves_per_group) {
+    Geo g;
+    if (!geometry_of(format, g)) return Q4_EINVAL;
+    if (rows_per_wave == 0 && waves_per_group == 0) {
+        g_cfg[format] = kDefault[format];
+        return Q4_OK;
+    }
+    if (!cfg_ok(rows_per_wave, waves_per_group)) return Q4_EINVAL;
+    g_cfg[format] = {rows_per_wave, waves_per_group};
+    return Q4_OK;
+}
+
+extern "C" int gemv_block_config(int format, int *rows_per_wave, int *waves_per_group) {
+    if (!rows_per_wave || !waves_per_group) return Q4_ENULL;
+    Geo g;
+    if (!geometry_of(format, g)) return Q4_EINVAL;
+    *rows_per_wave = g_cfg[format].R;
+    *waves_per_group = g_cfg[format].W;
+    return Q4_OK;
+}

@@ -1,5 +1,5 @@
 """C-ABI checks that need no GPU: the library loads, exports every function
-include/q4gemv.h declares, and rejects bad arguments before touching the
+include/q4gemv.h and include/q4blocks.h declare, and rejects bad arguments before touching the
 device.  Calls here either fail validation or stop at the device check; none
 launches a kernel."""
 
@@ -11,7 +11,7 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "q4gemv.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("q4gemv.h", "q4blocks.h")]
 
 import memory_bandwidth_amd as q4  # noqa: E402
 import workloads  # noqa: E402
@@ -26,9 +26,11 @@ def L():
 
 
 def header_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"^(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    names = []
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names += re.findall(r"^(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return names
 
 
 def test_header_declares_expected_functions():
