@@ -17,8 +17,13 @@ HBM read peak).  Each cell is a two-point difference, per_iter =
 "noise" unless t(2n) >= 1.2 t(n); n is swept; the first round is discarded;
 medians of >= 3 runs are reported with min and p10-p90.
 
+Also in the default line ("block_formats", skipped with --no-blocks):
+gemv_block on the Q4_0, Q8_0, Q4_K, Q5_K and Q6_K block formats of the cera
+page at the same 4096 x 14336 stream shape and at the page's four decode
+shapes, each cycling >= 1 GiB of distinct matrices.
+
 Other modes:
-  --full            every workload (all five configurations), JSONL table
+  --blocks-only     only the block-format cells
   --pmc-workload    a short fixed sequence of dispatches for rocprofv3 --pmc
   --summarize DIR   turn rocprofv3 CSV output in DIR into a profiles/ summary
 The CPU oracle is timed on a bounded sample of the same workload
@@ -391,10 +396,97 @@ def run_default(args):
         "two_point": result or None,
         "cache_class": "hbm-streaming",
     }
+    if not args.no_blocks:
+        line["block_formats"] = run_block_formats(torch, q4, dev)
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+# ---------------------------------------------------------------- block formats
+
+BLOCK_STREAM_BYTES = 1 << 30    # distinct matrices cycled per shape: at least this many bytes ...
+BLOCK_MAX_MATRICES = 64         # ... and at most this many matrices
+
+
+def block_shapes():
+    return [(wl.STREAM_SHAPE.N, wl.STREAM_SHAPE.K, "stream")] + list(wl.BLOCK_SHAPES)
+
+
+def run_block_formats(torch, q4, dev, reps_target_s: float = 0.02, only=None) -> dict:
+    """gemv_block on every format at the stream shape and the cera page's four
+    decode shapes.  Matrix 0 of each cell comes from the seeded generator;
+    the other distinct matrices (enough to cycle >= 1 GiB, at most 64) are
+    seeded random bytes drawn on the device with every binary16 scale field
+    set to 2^-7.  Each cell is gated against gemv_f32 on the dequantised
+    matrix 0, then timed by two-point differences of graph replays (median
+    of three), per launch."""
+    out = {}
+    seed = wl.config_seed(5)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    for fmt, (code, e, bb, offs) in wl.BLOCK_FORMATS.items():
+        cells = {}
+        for N, K, label in block_shapes():
+            if only and label not in only:
+                continue
+            rb = wl.block_row_bytes(fmt, K)
+            nbytes = N * rb
+            n_mats = max(2, min(BLOCK_MAX_MATRICES, -(-BLOCK_STREAM_BYTES // nbytes)))
+            x = torch.from_numpy(wl.make_x(seed, 1, K)).to(dev)
+            m0 = torch.from_numpy(wl.make_block_weights(seed, fmt, N, K)).to(dev)
+            mats = [m0]
+            for _ in range(n_mats - 1):
+                m = torch.randint(0, 256, m0.shape, dtype=torch.uint8, device=dev, generator=gen)
+                v = m.view(N, K // e, bb)
+                for o in offs:
+                    v[:, :, o] = 0x00
+                    v[:, :, o + 1] = 0x20
+                mats.append(m)
+            ys = [torch.empty((1, N), dtype=torch.float32, device=dev) for _ in mats]
+            w = q4.dequant_block(fmt, m0, K)
+            yb = q4.gemv_block(fmt, x, m0)
+            yf = q4.gemv_f32(x, w)
+            bound = q4.gemv_f32(x.abs(), w.abs())
+            err = (yb.double() - yf.double()).abs()
+            tol = 2 * (1e-4 * bound.double() + 1e-6)
+            if not bool((err <= tol).all()):
+                raise SystemExit(f"block parity gate failed: {fmt} {label}: worst err/tol "
+                                 f"{float((err / tol).max()):.3g}")
+            del w, yf, bound
+
+            def one_pass():
+                for mm, y in zip(mats, ys):
+                    q4.gemv_block(fmt, x, mm, out=y)
+
+            G = Graph(one_pass, torch)
+            G.time(2)
+            t1 = G.time(1)
+            reps = max(1, int(reps_target_s / max(t1, 1e-6)))
+            per = []
+            for _ in range(3):
+                a, b = G.time(reps), G.time(2 * reps)
+                per.append((b - a) / (reps * n_mats))
+            t = statistics.median(per)
+            gbs = nbytes / t / 1e9
+            cells[label] = {"N": N, "K": K, "bytes_per_call": nbytes, "matrices": n_mats,
+                            "us_per_launch": round(t * 1e6, 3), "GBps": round(gbs, 1),
+                            "frac_of_spec": round(gbs / SPEC_PEAK_GBS, 4),
+                            "geometry": list(q4.gemv_block_config(fmt))}
+            log(f"block {fmt} {label:12s} N={N} K={K}: {t * 1e6:7.3f} us/launch, {gbs:7.1f} GB/s")
+            del mats, ys, G
+            torch.cuda.empty_cache()
+        out[fmt] = cells
+    return out
+
+
+def run_blocks_only(args):
+    import torch
+    import memory_bandwidth_amd as q4
+    only = set(args.block_shapes.split(",")) if args.block_shapes else None
+    res = run_block_formats(torch, q4, torch.device("cuda:0"), only=only)
+    print(json.dumps({"block_formats": res, "unit": "GB/s", "peak": SPEC_PEAK_GBS}), flush=True)
 
 
 # ---------------------------------------------------------------- --pmc-workload
@@ -433,8 +525,9 @@ def _rows(pattern):
 def _kernel_short(name: str) -> str:
 
     m = re.search(r"(gemv_q4(?:_int)?_kernel<[^>]*>|gemv_f32_kernel<[^>]*>|read_reduce_kernel|"
-                  r"write_fill_kernel|dequant_q4_kernel|at::native::\w+|__amd_rocclr_\w+)", name)
-    return m.group(1) if m else name.split("(")[0][:60]
+                  r"write_fill_kernel|dequant_q4_kernel|gemv_blk_kernel<[^>]*>|"
+                  r"dequant_blk_kernel<[^>]*>|at::native::\w+|__amd_rocclr_\w+)", name)
+    return m.group(1).replace("(anonymous namespace)::", "") if m else name.split("(")[0][:60]
 
 
 def summarize_stats(d: str, name: str, command: str) -> str:
@@ -453,6 +546,17 @@ def summarize_stats(d: str, name: str, command: str) -> str:
         b = wl.q4_weight_bytes(wl.STREAM_SHAPE.N, wl.STREAM_SHAPE.K, wl.STREAM_SHAPE.g)
         lines += ["", f"gemv_q4 average kernel duration {avg * 1e6:.3f} us -> "
                       f"{b / avg / 1e9:.1f} GB/s of algorithmic bytes ({b} B per launch)."]
+    blk = [r for r in stats if "gemv_blk_kernel" in r["Name"]]
+    if blk:
+        s = wl.STREAM_SHAPE
+        lines += ["", f"gemv_block at the stream shape (N={s.N}, K={s.K}; each kernel above ran "
+                      "only that shape):"]
+        for r in blk:
+            fmt = re.search(r"FmtQ(\w+?),", r["Name"]).group(1).lower()
+            b = wl.block_row_bytes("q" + fmt, s.K) * s.N
+            avg = float(r["AverageNs"]) * 1e-9
+            lines.append(f"- q{fmt}: average {avg * 1e6:.3f} us -> {b / avg / 1e9:.1f} GB/s "
+                         f"({b} B per launch)")
     out = os.path.join(PROFILES, name + ".md")
     open(out, "w").write("\n".join(lines) + "\n")
     return out
@@ -526,6 +630,10 @@ def main(argv=None):
     ap.add_argument("--quick", action="store_true", help="skip the two-point sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-blocks", action="store_true", help="skip the block-format cells")
+    ap.add_argument("--blocks-only", action="store_true", help="only the block-format cells")
+    ap.add_argument("--block-shapes", default="",
+                    help="with --blocks-only: comma list of shape labels (stream, 'lm head', ...)")
     ap.add_argument("--pmc-workload", action="store_true")
     ap.add_argument("--summarize", metavar="DIR", help="rocprofv3 CSV dir (stats, or FETCH_SIZE pmc)")
     ap.add_argument("--summarize-write", metavar="DIR", help="WRITE_SIZE pmc dir (with --summarize)")
@@ -543,6 +651,8 @@ def main(argv=None):
         return 2
     if args.pmc_workload:
         return run_pmc_workload(args)
+    if args.blocks_only:
+        return run_blocks_only(args)
     return run_default(args)
 
 

@@ -73,14 +73,19 @@ int gemv_block(int format, const float *x, const uint8_t *w, float *y, int M, in
  * nothing launched. */
 int dequant_block(int format, const uint8_t *w, float *w_out, int N, int K, void *stream);
 
-/* Launch geometry of gemv_block for one format: rows per wavefront (1, 2 or
- * 4) and wavefronts per workgroup (4 or 8); 0, 0 restores the default.
- * Process-wide, not thread-safe against concurrent gemv_block calls.
- * Q4_EINVAL for an unknown format or an unsupported combination. */
-int gemv_block_set_config(int format, int rows_per_wave, int waves_per_group);
+/* Launch geometry of gemv_block for one format: row slots per lane (1, 2 or
+ * 4), wavefronts per workgroup (4 or 8) and workgroups per compute unit
+ * (0..64; 0 = one workgroup per row block, otherwise the grid is at most
+ * that many per CU and each workgroup loops over row blocks).  A set
+ * geometry applies to every shape; 0, 0, 0 restores the default, a
+ * per-format geometry for shapes of at least 512 row blocks and 1 row slot
+ * with 4 wavefronts below that.  Process-wide, not thread-safe against concurrent
+ * gemv_block calls.  Q4_EINVAL for an unknown format or an unsupported
+ * combination. */
+int gemv_block_set_config(int format, int rows_per_lane, int waves_per_group, int groups_per_cu);
 
-/* The rows per wavefront and wavefronts per workgroup gemv_block uses now. */
-int gemv_block_config(int format, int *rows_per_wave, int *waves_per_group);
+/* The geometry gemv_block uses now for `format`. */
+int gemv_block_config(int format, int *rows_per_lane, int *waves_per_group, int *groups_per_cu);
 
 #ifdef __cplusplus
 }

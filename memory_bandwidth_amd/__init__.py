@@ -72,8 +72,8 @@ def lib() -> ctypes.CDLL:
     L.block_geometry.argtypes = [I, IP, IP]
     L.gemv_block.argtypes = [I, P, P, P, I, I, I, P]
     L.dequant_block.argtypes = [I, P, P, I, I, P]
-    L.gemv_block_set_config.argtypes = [I, I, I]
-    L.gemv_block_config.argtypes = [I, IP, IP]
+    L.gemv_block_set_config.argtypes = [I, I, I, I]
+    L.gemv_block_config.argtypes = [I, IP, IP, IP]
     L.q4_strerror.argtypes = [I]
     L.q4_strerror.restype = ctypes.c_char_p
     L.q4_abi_version.argtypes = []
@@ -310,14 +310,16 @@ def dequant_block(fmt, w: torch.Tensor, K: int) -> torch.Tensor:
     return out
 
 
-def gemv_block_set_config(fmt, rows_per_wave: int = 0, waves_per_group: int = 0) -> None:
-    """Rows per wavefront (1, 2, 4) and wavefronts per workgroup (4, 8) of
-    gemv_block for one format; 0, 0 restores the default (host-only)."""
-    _check("gemv_block_set_config", lib().gemv_block_set_config(_fmt(fmt), rows_per_wave,
-                                                                waves_per_group))
+def gemv_block_set_config(fmt, rows_per_lane: int = 0, waves_per_group: int = 0,
+                          groups_per_cu: int = 0) -> None:
+    """Row slots per lane (1, 2, 4), wavefronts per workgroup (4, 8) and
+    workgroups per CU (0 = one per row block) of gemv_block for one format;
+    all zero restores the default (host-only)."""
+    _check("gemv_block_set_config", lib().gemv_block_set_config(_fmt(fmt), rows_per_lane,
+                                                                waves_per_group, groups_per_cu))
 
 
-def gemv_block_config(fmt) -> tuple[int, int]:
-    r, wv = ctypes.c_int(), ctypes.c_int()
-    _check("gemv_block_config", lib().gemv_block_config(_fmt(fmt), ctypes.byref(r), ctypes.byref(wv)))
-    return r.value, wv.value
+def gemv_block_config(fmt) -> tuple[int, int, int]:
+    v = [ctypes.c_int() for _ in range(3)]
+    _check("gemv_block_config", lib().gemv_block_config(_fmt(fmt), *[ctypes.byref(t) for t in v]))
+    return tuple(t.value for t in v)

@@ -5,14 +5,15 @@
 //
 // Mapping onto CDNA4 (one activation row; a streaming dot product, no MFMA):
 //   * A lane owns a 64-element unit of a row: two blocks of Q4_0 or Q8_0, or
-//     a quarter of a 256-element K-format block.  A wavefront covers 64
-//     consecutive units (4096 elements) of R rows per pass; longer rows take
-//     several passes.  Consecutive lanes read consecutive unit bytes, so one
-//     wavefront's loads for a row cover one contiguous stretch of it.
-//   * The unit's 64 x values stay in the lane's registers for all R rows of
-//     the pass.  Every workgroup stages x once in LDS with one float4 of
-//     padding per 16, so that 16 consecutive lanes reading their units'
-//     slices hit 16 different bank groups.
+//     a quarter of a 256-element K-format block.  64, 32 or 16 lanes share a
+//     row, so one load instruction covers one, two or four rows, and
+//     consecutive lanes read consecutive unit bytes of their row.  Rows with
+//     more units than their lanes take several passes.
+//   * Workgroups loop over blocks of rows; each stages x once in LDS, with
+//     one float4 of padding per 16 so that 16 consecutive lanes reading their
+//     units' slices hit 16 different bank groups, and a lane keeps its
+//     unit's 64 x values in registers while they stay the same.  The loads
+//     of the next block are issued before the arithmetic of the current one.
 //   * Unit bytes come in with dword-aligned buffer loads.  Fields that start
 //     2 bytes past a dword boundary (the first block of a Q4_0 or Q8_0 pair,
 //     every odd Q6_K block) are shifted into place with v_alignbyte_b32;
@@ -42,13 +43,16 @@ __device__ __forceinline__ rsrc_t raw_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
 }
 
-constexpr int kNonTemporal = 2;   // weights are read once
-
+// Default cache policy: a lane's unit is not a whole cache line, so one load
+// instruction touches each line of its stretch only in part and the unit's
+// other loads find the line in cache.  (Loads marked non-temporal, the
+// weights being read once, were 7-40% slower: the lines left the cache
+// before the other loads of the stretch reached them.)
 __device__ __forceinline__ u32x4_t ld128(rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 __device__ __forceinline__ uint32_t ld32(rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kNonTemporal);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 __device__ __forceinline__ uint32_t ld16(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
@@ -84,6 +88,7 @@ __device__ __forceinline__ float ubyte(uint32_t v, int j) { return (float)((v >>
 // ---------------------------------------------------------------------------
 
 struct FmtQ4_0 {
+    static constexpr int kMaxR = 4;   // row slots per lane without spilling
     static constexpr bool kMin = false;
     struct Raw { uint32_t v[9]; };
     __device__ static void load(Raw &r, rsrc_t rs, uint32_t ro, int u) {
@@ -118,6 +123,7 @@ struct FmtQ4_0 {
 };
 
 struct FmtQ8_0 {
+    static constexpr int kMaxR = 4;   // row slots per lane without spilling
     static constexpr bool kMin = false;
     struct Raw { uint32_t v[17]; };
     __device__ static void load(Raw &r, rsrc_t rs, uint32_t ro, int u) {
@@ -183,6 +189,7 @@ __device__ __forceinline__ void k_affine(const uint32_t *hd, int u, float (&a)[4
 }
 
 struct FmtQ4_K {
+    static constexpr int kMaxR = 4;   // row slots per lane without spilling
     static constexpr bool kMin = true;
     struct Raw { uint32_t v[12]; };
     __device__ static void load(Raw &r, rsrc_t rs, uint32_t ro, int u) {
@@ -212,6 +219,7 @@ struct FmtQ4_K {
 };
 
 struct FmtQ5_K {
+    static constexpr int kMaxR = 2;   // row slots per lane without spilling
     static constexpr bool kMin = true;
     struct Raw { uint32_t v[20]; };
     __device__ static void load(Raw &r, rsrc_t rs, uint32_t ro, int u) {
@@ -253,6 +261,7 @@ struct FmtQ5_K {
 // dword boundary; its ql and qh runs are read as 9 aligned dwords each and
 // shifted into place, its scales and d with 16-bit loads.
 struct FmtQ6_K {
+    static constexpr int kMaxR = 2;   // row slots per lane without spilling
     static constexpr bool kMin = false;
     struct Raw { uint32_t l[9], h[9], sa, sb, d, sh; };
     __device__ static void load(Raw &r, rsrc_t rs, uint32_t ro, int u) {
@@ -304,40 +313,64 @@ struct FmtQ6_K {
 };
 
 // ---------------------------------------------------------------------------
-// GEMV kernel.  R rows per wavefront, W wavefronts per workgroup.
+// GEMV kernel.
+//
+// LPR lanes share a row: a row's units are spread over LPR lanes (64, or 32
+// and 16 for rows of at most 32 or 16 units, so that one load instruction
+// covers RG = 64 / LPR rows).  A lane has R row slots, a wavefront RPW =
+// R * RG rows and a workgroup of W wavefronts a block of W * RPW rows.
+// Workgroups stride over the row blocks, staging x in LDS once; a block with
+// more units than LPR takes several passes, each an item of the workgroup's
+// loop.  The loads of the next item are issued before the arithmetic of the
+// current one.
 // ---------------------------------------------------------------------------
 
 // LDS slot of x's float4 number f: one float4 of padding after every 16.
 __device__ __forceinline__ int xslot(int f) { return f + (f >> 4); }
 
-template <class T, int R, int W>
+template <class T, int R, int W, int LPR>
 __global__ __launch_bounds__(W * 64) void gemv_blk_kernel(const float *__restrict__ x,
                                                           const uint8_t *__restrict__ w,
                                                           float *__restrict__ y, int N, int K,
                                                           uint32_t RB) {
+    constexpr int RG = 64 / LPR;
+    constexpr int RPW = R * RG;
+    constexpr int RPB = RPW * W;
     extern __shared__ float blds[];
     f32x4_t *xs = reinterpret_cast<f32x4_t *>(blds);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int U = K >> 6;                 // units per row
-    const int nx4 = K >> 2;
-    const int row0 = (blockIdx.x * W + wave) * R;    // may be >= N
-    const int rbase = min(row0, N - 1);
+    const int g = LPR == 64 ? 0 : lane / LPR;      // row of the lane within a load instruction
+    const int ul = LPR == 64 ? lane : lane % LPR;  // unit of the lane within a pass
+    const int U = K >> 6;                          // units per row
+    const int P = (U + LPR - 1) / LPR;             // passes per row block
+    const int nblk = (N + RPB - 1) / RPB;
+    const int nitems = (nblk - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x * P;
 
-    // Resource based 16-byte aligned at (or just before) the wavefront's
-    // first row; rows past N re-read row N - 1 and are not stored.
-    const uint64_t byte0 = (uint64_t)rbase * RB;
-    const uint32_t delta = (uint32_t)(byte0 & 15u);
-    const uint64_t span = (uint64_t)(N - rbase) * RB + delta;
-    const rsrc_t wr = raw_rsrc(w + (byte0 - delta), (uint32_t)std::min<uint64_t>(span, 0xFFFFFFFFull));
-    uint32_t ro[R];
+    // Issues the loads of item `it` (row block, pass) into raw.  Rows past N
+    // re-read row N - 1 and units past U re-read unit U - 1; neither is used.
+    auto load_item = [&](typename T::Raw (&raw)[R], int it) {
+        const int blk = (int)blockIdx.x + it / P * (int)gridDim.x;
+        const int pass = it % P;
+        const int rb0 = blk * RPB + wave * RPW;
+        const int rbase = min(rb0, N - 1);
+        const uint64_t byte0 = (uint64_t)rbase * RB;
+        const uint32_t delta = (uint32_t)(byte0 & 15u);
+        const uint64_t span = (uint64_t)(N - rbase) * RB + delta;
+        const rsrc_t rs = raw_rsrc(w + (byte0 - delta), (uint32_t)std::min<uint64_t>(span, 0xFFFFFFFFull));
+        const int uc = min(pass * LPR + ul, U - 1);
 #pragma unroll
-    for (int r = 0; r < R; ++r) ro[r] = delta + (uint32_t)(min(row0 + r, N - 1) - rbase) * RB;
+        for (int r = 0; r < R; ++r) {
+            const uint32_t ro = delta + (uint32_t)(min(rb0 + r * RG + g, N - 1) - rbase) * RB;
+            T::load(raw[r], rs, ro, uc);
+        }
+    };
 
-    // x: the first 4096 elements go to registers ahead of the weight loads
-    // (loads retire in issue order), the rest after them.
+    // x: the first 4096 elements go to registers ahead of the first item's
+    // loads (loads retire in issue order), the rest after them.
     const f32x4_t *x4 = reinterpret_cast<const f32x4_t *>(x);
+    const int nx4 = K >> 2;
     constexpr int XB = 1024 / (W * 64);
     f32x4_t xr[XB];
 #pragma unroll
@@ -346,12 +379,8 @@ __global__ __launch_bounds__(W * 64) void gemv_blk_kernel(const float *__restric
         xr[t] = i < nx4 ? x4[i] : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     __builtin_amdgcn_sched_barrier(0);
-    typename T::Raw raw[R];
-    {
-        const int uc = min(lane, U - 1);
-#pragma unroll
-        for (int r = 0; r < R; ++r) T::load(raw[r], wr, ro[r], uc);
-    }
+    typename T::Raw ra[R], rb[R];
+    load_item(ra, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < XB; ++t) {
@@ -361,38 +390,41 @@ __global__ __launch_bounds__(W * 64) void gemv_blk_kernel(const float *__restric
     for (int i = XB * W * 64 + tid; i < nx4; i += W * 64) xs[xslot(i)] = x4[i];
     __syncthreads();
 
+    float xv[64], sx[4];
+    int xpass = -1;
     float acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = 0.f;
-    const int P = (U + 63) >> 6;
-    for (int pass = 0; pass < P; ++pass) {
-        const int u = pass * 64 + lane;
+
+    // Arithmetic of item `it` on raw; after a block's last pass, the row sums
+    // are reduced across the LPR lanes of each row and stored.
+    auto process = [&](const typename T::Raw (&raw)[R], int it) {
+        const int blk = (int)blockIdx.x + it / P * (int)gridDim.x;
+        const int pass = it % P;
+        const int u = pass * LPR + ul;
         const int uc = min(u, U - 1);
-        if (pass > 0) {
+        if (pass != xpass) {
+            xpass = pass;
 #pragma unroll
-            for (int r = 0; r < R; ++r) T::load(raw[r], wr, ro[r], uc);
-        }
-        float xv[64];
+            for (int run = 0; run < 2; ++run) {
+                const int f = T::xstart(uc, run) >> 2;
 #pragma unroll
-        for (int run = 0; run < 2; ++run) {
-            const int f = T::xstart(uc, run) >> 2;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const f32x4_t v = xs[xslot(f + i)];
-                xv[32 * run + 4 * i] = v.x;
-                xv[32 * run + 4 * i + 1] = v.y;
-                xv[32 * run + 4 * i + 2] = v.z;
-                xv[32 * run + 4 * i + 3] = v.w;
+                for (int i = 0; i < 8; ++i) {
+                    const f32x4_t v = xs[xslot(f + i)];
+                    xv[32 * run + 4 * i] = v.x;
+                    xv[32 * run + 4 * i + 1] = v.y;
+                    xv[32 * run + 4 * i + 2] = v.z;
+                    xv[32 * run + 4 * i + 3] = v.w;
+                }
             }
-        }
-        float sx[4];
-        if constexpr (T::kMin) {
+            if constexpr (T::kMin) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                float t = 0.f;
+                for (int k = 0; k < 4; ++k) {
+                    float t = 0.f;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) t += xv[16 * k + i];
-                sx[k] = t;
+                    for (int i = 0; i < 16; ++i) t += xv[16 * k + i];
+                    sx[k] = t;
+                }
             }
         }
         if (u < U) {
@@ -411,19 +443,39 @@ __global__ __launch_bounds__(W * 64) void gemv_blk_kernel(const float *__restric
                 acc[r] = c;
             }
         }
-    }
-
-    constexpr int NQ = (R + 3) / 4;
-    float out[NQ];
-    q4::wave_reduce_rows<R>(acc, out);
-    const int h = lane >> 4;
-    const bool writer = (lane & 15) == 0 && (R >= 4 || (h & (R == 2 ? 1 : 3)) == 0);
-    if (writer) {
+        if (pass == P - 1) {
+            const int rb0 = blk * RPB + wave * RPW;
+            if constexpr (LPR == 64) {
+                constexpr int NQ = (R + 3) / 4;
+                float out[NQ];
+                q4::wave_reduce_rows<R>(acc, out);
+                const int h = lane >> 4;
+                if ((lane & 15) == 0 && (R >= 4 || (h & (R == 2 ? 1 : 3)) == 0)) {
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            const int row = row0 + q4::reduced_row<R>(q, h);
-            if (row < N) y[row] = out[q];
+                    for (int q = 0; q < NQ; ++q) {
+                        const int row = rb0 + q4::reduced_row<R>(q, h);
+                        if (row < N) y[row] = out[q];
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const float s = q4::group_sum<LPR>(acc[r]);
+                    const int row = rb0 + r * RG + g;
+                    if (ul == 0 && row < N) y[row] = s;
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r] = 0.f;
         }
+    };
+
+    for (int it = 0; it < nitems; it += 2) {
+        if (it + 1 < nitems) load_item(rb, it + 1);
+        process(ra, it);
+        if (it + 1 >= nitems) break;
+        if (it + 2 < nitems) load_item(ra, it + 2);
+        process(rb, it + 1);
     }
 }
 
@@ -484,31 +536,76 @@ bool geometry_of(int f, Geo &g) {
     }
 }
 
-struct Cfg { int R, W; };
-// Default rows per wavefront and wavefronts per workgroup, per format.
-constexpr Cfg kDefault[6] = {{0, 0}, {4, 4}, {2, 4}, {4, 4}, {2, 4}, {2, 4}};
-Cfg g_cfg[6] = {{0, 0}, {4, 4}, {2, 4}, {4, 4}, {2, 4}, {2, 4}};
+// Launch geometry of one format: rows per lane slot count R, wavefronts
+// per workgroup W, and workgroups per CU G (the grid is at most G * CUs
+// workgroups; 0 = one workgroup per row block).
+// Defaults (measured on the 4096 -> 14336 stream and 1024 -> 65536 shapes)
+// apply to shapes of at least 2 * CUs row blocks; smaller ones, latency-
+// bound, take one row slot and 4 wavefronts, the most workgroups.  A
+// configuration set through gemv_block_set_config applies to every shape.
+struct Cfg { int R, W, G; bool forced; };
+constexpr int kCUs = 256;
+constexpr Cfg kDefault[6] = {{0, 0, 0, false}, {1, 8, 2, false}, {1, 4, 2, false},
+                             {2, 4, 4, false}, {2, 4, 2, false}, {1, 4, 2, false}};
+constexpr Cfg kSmall = {1, 4, 0, false};
+Cfg g_cfg[6] = {kDefault[0], kDefault[1], kDefault[2], kDefault[3], kDefault[4], kDefault[5]};
 
-bool cfg_ok(int R, int W) { return (R == 1 || R == 2 || R == 4) && (W == 4 || W == 8); }
+// Lanes per row: the fewest of 64, 32, 16 that hold a row's units.
+int lanes_per_row(int K);
+
+Cfg config_for(int format, int N, int K) {
+    const Cfg c = g_cfg[format];
+    if (c.forced) return c;
+    const int rpb = c.R * (64 / lanes_per_row(K)) * c.W;
+    return (N + rpb - 1) / rpb < 2 * kCUs ? kSmall : c;
+}
+
+bool cfg_ok(int format, int R, int W, int G) {
+    const int max_r = (format == BLK_Q5_K || format == BLK_Q6_K) ? 2 : 4;
+    return (R == 1 || R == 2 || R == 4) && R <= max_r && (W == 4 || W == 8) && G >= 0 && G <= 64;
+}
+
+// Lanes per row: the fewest of 64, 32, 16 that hold a row's units.
+int lanes_per_row(int K) {
+    const int U = K >> 6;
+    return U > 32 ? 64 : (U > 16 ? 32 : 16);
+}
+
+template <class T, int R, int W, int LPR>
+void launch_l(Cfg c, const float *x, const uint8_t *w, float *y, int N, int K, uint32_t RB,
+              hipStream_t st) {
+    constexpr int RPB = R * (64 / LPR) * W;
+    const int nblk = (N + RPB - 1) / RPB;
+    const int grid = c.G > 0 ? std::min(nblk, c.G * kCUs) : nblk;
+    const size_t lds = (size_t)(K / 4 + K / 64) * 16;
+    hipLaunchKernelGGL((gemv_blk_kernel<T, R, W, LPR>), dim3(grid), dim3(W * 64), lds, st, x, w, y, N, K,
+                       RB);
+}
 
 template <class T, int R, int W>
-void launch_w(const float *x, const uint8_t *w, float *y, int N, int K, uint32_t RB, hipStream_t st) {
-    const int grid = (N + R * W - 1) / (R * W);
-    const size_t lds = (size_t)(K / 4 + K / 64) * 16;
-    hipLaunchKernelGGL((gemv_blk_kernel<T, R, W>), dim3(grid), dim3(W * 64), lds, st, x, w, y, N, K, RB);
+void launch_w(Cfg c, const float *x, const uint8_t *w, float *y, int N, int K, uint32_t RB,
+              hipStream_t st) {
+    switch (lanes_per_row(K)) {
+    case 16: launch_l<T, R, W, 16>(c, x, w, y, N, K, RB, st); break;
+    case 32: launch_l<T, R, W, 32>(c, x, w, y, N, K, RB, st); break;
+    default: launch_l<T, R, W, 64>(c, x, w, y, N, K, RB, st); break;
+    }
 }
 
 template <class T>
 void launch_fmt(Cfg c, const float *x, const uint8_t *w, float *y, int N, int K, uint32_t RB,
                 hipStream_t st) {
-    if (c.W == 8) {
-        if (c.R == 1) launch_w<T, 1, 8>(x, w, y, N, K, RB, st);
-        else if (c.R == 2) launch_w<T, 2, 8>(x, w, y, N, K, RB, st);
-        else launch_w<T, 4, 8>(x, w, y, N, K, RB, st);
+    if (c.R == 4) {
+        if constexpr (T::kMaxR >= 4) {
+            if (c.W == 8) launch_w<T, 4, 8>(c, x, w, y, N, K, RB, st);
+            else launch_w<T, 4, 4>(c, x, w, y, N, K, RB, st);
+        }
+    } else if (c.W == 8) {
+        if (c.R == 1) launch_w<T, 1, 8>(c, x, w, y, N, K, RB, st);
+        else launch_w<T, 2, 8>(c, x, w, y, N, K, RB, st);
     } else {
-        if (c.R == 1) launch_w<T, 1, 4>(x, w, y, N, K, RB, st);
-        else if (c.R == 2) launch_w<T, 2, 4>(x, w, y, N, K, RB, st);
-        else launch_w<T, 4, 4>(x, w, y, N, K, RB, st);
+        if (c.R == 1) launch_w<T, 1, 4>(c, x, w, y, N, K, RB, st);
+        else launch_w<T, 2, 4>(c, x, w, y, N, K, RB, st);
     }
 }
 
@@ -543,7 +640,7 @@ extern "C" int gemv_block(int format, const float *x, const uint8_t *w, float *y
     if (int st = q4::check_device(); st != Q4_OK) return st;
     const uint32_t RB = (uint32_t)(K / g.elems * g.bytes);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const Cfg c = g_cfg[format];
+    const Cfg c = config_for(format, N, K);
     switch (format) {
     case BLK_Q4_0: launch_fmt<FmtQ4_0>(c, x, w, y, N, K, RB, st); break;
     case BLK_Q8_0: launch_fmt<FmtQ8_0>(c, x, w, y, N, K, RB, st); break;
@@ -574,23 +671,26 @@ extern "C" int dequant_block(int format, const uint8_t *w, float *w_out, int N, 
     return q4::launch_status();
 }
 
-extern "C" int gemv_block_set_config(int format, int rows_per_wave, int waves_per_group) {
+extern "C" int gemv_block_set_config(int format, int rows_per_lane, int waves_per_group,
+                                     int groups_per_cu) {
     Geo g;
     if (!geometry_of(format, g)) return Q4_EINVAL;
-    if (rows_per_wave == 0 && waves_per_group == 0) {
+    if (rows_per_lane == 0 && waves_per_group == 0 && groups_per_cu == 0) {
         g_cfg[format] = kDefault[format];
         return Q4_OK;
     }
-    if (!cfg_ok(rows_per_wave, waves_per_group)) return Q4_EINVAL;
-    g_cfg[format] = {rows_per_wave, waves_per_group};
+    if (!cfg_ok(format, rows_per_lane, waves_per_group, groups_per_cu)) return Q4_EINVAL;
+    g_cfg[format] = {rows_per_lane, waves_per_group, groups_per_cu, true};
     return Q4_OK;
 }
 
-extern "C" int gemv_block_config(int format, int *rows_per_wave, int *waves_per_group) {
-    if (!rows_per_wave || !waves_per_group) return Q4_ENULL;
+extern "C" int gemv_block_config(int format, int *rows_per_lane, int *waves_per_group,
+                                 int *groups_per_cu) {
+    if (!rows_per_lane || !waves_per_group || !groups_per_cu) return Q4_ENULL;
     Geo g;
     if (!geometry_of(format, g)) return Q4_EINVAL;
-    *rows_per_wave = g_cfg[format].R;
+    *rows_per_lane = g_cfg[format].R;
     *waves_per_group = g_cfg[format].W;
+    *groups_per_cu = g_cfg[format].G;
     return Q4_OK;
 }

@@ -71,19 +71,34 @@ def test_gemv_small_shapes(fmt, N, K):
 
 @pytest.mark.parametrize("fmt", FMTS)
 def test_every_config(fmt):
-    """Every (rows per wavefront, wavefronts per workgroup) the library runs."""
-    N, K = 45, 4352
-    w = wl.make_block_weights(44, fmt, N, K)
-    x = wl.make_x(45, 1, K)
-    y_ref, b = blocks.gemv(code(fmt), x, w)
+    """Every (row slots, wavefronts per workgroup) the library runs, with one
+    workgroup per row block and with at most one per CU looping over row
+    blocks, at 64, 32 and 16 lanes per row (K = 4352 in two passes, 2048,
+    1024) and at 65536 x 1024 on sampled rows, where every configuration
+    loops."""
+    cases = []
+    for i, (N, K) in enumerate([(1100, 4352), (1500, 2048), (1030, 1024)]):
+        w = wl.make_block_weights(44, fmt, N, K, index=i)
+        x = wl.make_x(45, 1, K, index=i)
+        cases.append((x, w, None, *blocks.gemv(code(fmt), x, w)))
+    w = wl.make_block_weights(44, fmt, 65536, 1024, index=9)
+    x = wl.make_x(45, 1, 1024, index=9)
+    rows = np.unique(np.r_[0:70, 65536 - 70:65536,
+                           np.random.default_rng(56).choice(65536, 64, replace=False)]).astype(np.int64)
+    cases.append((x, w, rows, *blocks.gemv(code(fmt), x, w, rows)))
     try:
-        for R in (1, 2, 4):
+        for R in ((1, 2) if fmt in ("q5_k", "q6_k") else (1, 2, 4)):
             for W in (4, 8):
-                q4.gemv_block_set_config(fmt, R, W)
-                assert q4.gemv_block_config(fmt) == (R, W)
-                assert_within(run(fmt, x, w), y_ref, b, f"{fmt} R={R} W={W}")
+                for G in (0, 1):
+                    q4.gemv_block_set_config(fmt, R, W, G)
+                    assert q4.gemv_block_config(fmt) == (R, W, G)
+                    for x, w, rows, y_ref, b in cases:
+                        y = run(fmt, x, w)
+                        if rows is not None:
+                            y = y[:, rows]
+                        assert_within(y, y_ref, b, f"{fmt} R={R} W={W} G={G} N={w.shape[0]}")
     finally:
-        q4.gemv_block_set_config(fmt, 0, 0)
+        q4.gemv_block_set_config(fmt, 0, 0, 0)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
