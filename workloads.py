@@ -194,6 +194,28 @@ def make_block_weights(seed: int, fmt: str, N: int, K: int, s_lo: float = 0.002,
     return w.reshape(N, rb)
 
 
+# The 2-bit corpus scan of the Refractometer page: 65,536 vectors x 8
+# queries.  D is not on the page; 768 is the EmbeddingGemma embedding width.
+SCAN_VECTORS, SCAN_QUERIES, SCAN_DIM = 65536, 8, 768
+_STREAM_SCAN_C, _STREAM_SCAN_Q, _STREAM_SCAN_L = 41, 42, 43
+
+
+def make_scan_codes(seed: int, V: int, D: int, index: int = 0) -> np.ndarray:
+    """codes uint32 [V, D/16]: every 2-bit code uniform over 0..3."""
+    if D % 16:
+        raise ValueError("D must be a multiple of 16")
+    return _rng(seed, _STREAM_SCAN_C, index).integers(0, 2**32, size=(V, D // 16), dtype=np.uint32)
+
+
+def make_scan_lut(seed: int, Q: int, D: int, index: int = 0) -> np.ndarray:
+    """lut float32 [Q, D, 4]: entry (q, d, c) = query[q, d] * level[d, c], the
+    table an asymmetric-distance scan builds from each query (query ~ N(0, 1))
+    and a per-dimension 2-bit codebook (four sorted levels, N(0, 1) draws)."""
+    query = _rng(seed, _STREAM_SCAN_Q, index).standard_normal((Q, D))
+    level = np.sort(_rng(seed, _STREAM_SCAN_L, index).standard_normal((D, 4)), axis=1)
+    return (query[:, :, None] * level[None, :, :]).astype(np.float32)
+
+
 def make_probe_buffer(n_floats: int, seed: int = 0x5EED0004) -> np.ndarray:
     """A float32 buffer for the read probe, values uniform in [0, 1)."""
     return _rng(seed, 21, 0).random(n_floats, dtype=np.float32)
