@@ -17,13 +17,15 @@ HBM read peak).  Each cell is a two-point difference, per_iter =
 "noise" unless t(2n) >= 1.2 t(n); n is swept; the first round is discarded;
 medians of >= 3 runs are reported with min and p10-p90.
 
-Also in the default line ("block_formats", skipped with --no-blocks):
-gemv_block on the Q4_0, Q8_0, Q4_K, Q5_K and Q6_K block formats of the cera
-page at the same 4096 x 14336 stream shape and at the page's four decode
-shapes, each cycling >= 1 GiB of distinct matrices.
+Also in the default line ("block_formats" and "scan2", skipped with
+--no-blocks): gemv_block on the Q4_0, Q8_0, Q4_K, Q5_K and Q6_K block formats
+of the cera page at the same 4096 x 14336 stream shape and at the page's four
+decode shapes, each cycling >= 1 GiB of distinct matrices; and the 2-bit
+corpus scan of the Refractometer page, 65,536 vectors x 8 queries, D = 768,
+cycling 64 distinct corpora.
 
 Other modes:
-  --blocks-only     only the block-format cells
+  --blocks-only     only the block-format and scan cells (--block-shapes to pick)
   --pmc-workload    a short fixed sequence of dispatches for rocprofv3 --pmc
   --summarize DIR   turn rocprofv3 CSV output in DIR into a profiles/ summary
 The CPU oracle is timed on a bounded sample of the same workload
@@ -398,6 +400,7 @@ def run_default(args):
     }
     if not args.no_blocks:
         line["block_formats"] = run_block_formats(torch, q4, dev)
+        line["scan2"] = run_scan(torch, q4, dev)
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
@@ -481,12 +484,76 @@ def run_block_formats(torch, q4, dev, reps_target_s: float = 0.02, only=None) ->
     return out
 
 
+def run_scan(torch, q4, dev, reps_target_s: float = 0.02) -> dict:
+    """scan2 on the Refractometer page's workload, 65,536 vectors x 8 queries
+    (D = 768), cycling 64 distinct corpora (805 MB > L2 + MALL): corpus 0
+    from the seeded generator, the rest seeded device random words.  Gated
+    on 4096 vectors of corpus 0 against the same scores from gemv_f32 (the
+    lookup as a GEMV: score[v] = lut[Q, 4D] . onehot(codes[v])), then timed by two-point
+    differences of graph replays, per scan."""
+    V, Q, D = wl.SCAN_VECTORS, wl.SCAN_QUERIES, wl.SCAN_DIM
+    seed = wl.config_seed(6)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    n_corpora = 64
+    c0 = torch.from_numpy(wl.make_scan_codes(seed, V, D).view("int32")).to(dev)
+    corpora = [c0] + [torch.randint(-2**31, 2**31 - 1, c0.shape, dtype=torch.int32, device=dev,
+                                    generator=gen) for _ in range(n_corpora - 1)]
+    lut = torch.from_numpy(wl.make_scan_lut(seed, Q, D)).to(dev)
+    outs = [torch.empty((V, Q), dtype=torch.float32, device=dev) for _ in corpora]
+    # gate: one-hot expansion of 4096 vectors, scored by the fp32 GEMV
+    n = 4096
+    sh = torch.arange(16, device=dev, dtype=torch.int64) * 2
+    codes = ((c0[:n].to(torch.int64) & 0xFFFFFFFF).unsqueeze(-1) >> sh) & 3          # [n, D/16, 16]
+    onehot = torch.nn.functional.one_hot(codes.reshape(n, D), 4).to(torch.float32).reshape(n, 4 * D)
+    table = lut.reshape(Q, 4 * D).contiguous()
+    ref = q4.gemv_f32(table, onehot).t()               # the table as the 8 activation rows
+    bound = q4.gemv_f32(table.abs(), onehot).t()
+    got = q4.scan2(c0, lut)[:n]
+    err = (got.double() - ref.double()).abs()
+    tol = 2 * (1e-4 * bound.double() + 1e-6)
+    if not bool((err <= tol).all()):
+        raise SystemExit(f"scan parity gate failed: worst err/tol {float((err / tol).max()):.3g}")
+    del onehot, codes
+
+    def one_pass():
+        for c, o in zip(corpora, outs):
+            q4.scan2(c, lut, out=o)
+
+    G = Graph(one_pass, torch)
+    G.time(2)
+    t1 = G.time(1)
+    reps = max(1, int(reps_target_s / max(t1, 1e-6)))
+    per = []
+    for _ in range(3):
+        a, b = G.time(reps), G.time(2 * reps)
+        per.append((b - a) / (reps * n_corpora))
+    t = statistics.median(per)
+    nbytes = V * D // 4
+    lds_bytes = V * D * 16 * ((Q + 3) // 4)        # table bytes read from LDS per scan
+    log(f"scan2 {V} x {Q} D={D}: {t * 1e6:.3f} us/scan, {nbytes / t / 1e9:.1f} GB/s of codes, "
+        f"{lds_bytes / t / 1e12:.1f} TB/s of LDS table reads")
+    res = {"V": V, "Q": Q, "D": D, "bytes_per_call": nbytes, "corpora": n_corpora,
+           "us_per_scan": round(t * 1e6, 3), "GBps": round(nbytes / t / 1e9, 1),
+           "frac_of_spec": round(nbytes / t / 1e9 / SPEC_PEAK_GBS, 4),
+           "lds_table_TBps": round(lds_bytes / t / 1e12, 2),
+           "lookups_per_s": round(V * D * Q / t, 1), "config": list(q4.scan2_config())}
+    del corpora, outs, G
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_blocks_only(args):
     import torch
     import memory_bandwidth_amd as q4
     only = set(args.block_shapes.split(",")) if args.block_shapes else None
-    res = run_block_formats(torch, q4, torch.device("cuda:0"), only=only)
-    print(json.dumps({"block_formats": res, "unit": "GB/s", "peak": SPEC_PEAK_GBS}), flush=True)
+    dev = torch.device("cuda:0")
+    out = {"unit": "GB/s", "peak": SPEC_PEAK_GBS}
+    if not only or only != {"scan"}:
+        out["block_formats"] = run_block_formats(torch, q4, dev, only=only)
+    if not only or "scan" in only:
+        out["scan2"] = run_scan(torch, q4, dev)
+    print(json.dumps(out), flush=True)
 
 
 # ---------------------------------------------------------------- --pmc-workload
@@ -526,7 +593,7 @@ def _kernel_short(name: str) -> str:
 
     m = re.search(r"(gemv_q4(?:_int)?_kernel<[^>]*>|gemv_f32_kernel<[^>]*>|read_reduce_kernel|"
                   r"write_fill_kernel|dequant_q4_kernel|gemv_blk_kernel<[^>]*>|"
-                  r"dequant_blk_kernel<[^>]*>|at::native::\w+|__amd_rocclr_\w+)", name)
+                  r"dequant_blk_kernel<[^>]*>|scan2_kernel<[^>]*>|at::native::\w+|__amd_rocclr_\w+)", name)
     return m.group(1).replace("(anonymous namespace)::", "") if m else name.split("(")[0][:60]
 
 
@@ -546,6 +613,14 @@ def summarize_stats(d: str, name: str, command: str) -> str:
         b = wl.q4_weight_bytes(wl.STREAM_SHAPE.N, wl.STREAM_SHAPE.K, wl.STREAM_SHAPE.g)
         lines += ["", f"gemv_q4 average kernel duration {avg * 1e6:.3f} us -> "
                       f"{b / avg / 1e9:.1f} GB/s of algorithmic bytes ({b} B per launch)."]
+    sc = [r for r in stats if "scan2_kernel" in r["Name"]]
+    if sc:
+        V, D = wl.SCAN_VECTORS, wl.SCAN_DIM
+        avg = float(sc[0]["AverageNs"]) * 1e-9
+        lines += ["", f"scan2 ({V} vectors x {wl.SCAN_QUERIES} queries, D = {D}): average "
+                      f"{avg * 1e6:.3f} us -> {V * D / 4 / avg / 1e9:.1f} GB/s of codes "
+                      f"({V * D // 4} B per scan), {V * D * 32 / avg / 1e12:.1f} TB/s of LDS "
+                      "table reads (32 B per vector and dimension)."]
     blk = [r for r in stats if "gemv_blk_kernel" in r["Name"]]
     if blk:
         s = wl.STREAM_SHAPE
@@ -633,7 +708,7 @@ def main(argv=None):
     ap.add_argument("--no-blocks", action="store_true", help="skip the block-format cells")
     ap.add_argument("--blocks-only", action="store_true", help="only the block-format cells")
     ap.add_argument("--block-shapes", default="",
-                    help="with --blocks-only: comma list of shape labels (stream, 'lm head', ...)")
+                    help="with --blocks-only: comma list of shape labels (stream, 'lm head', ..., scan)")
     ap.add_argument("--pmc-workload", action="store_true")
     ap.add_argument("--summarize", metavar="DIR", help="rocprofv3 CSV dir (stats, or FETCH_SIZE pmc)")
     ap.add_argument("--summarize-write", metavar="DIR", help="WRITE_SIZE pmc dir (with --summarize)")

@@ -24,13 +24,13 @@ LIB_PATH = os.path.join(_HERE, "libq4gemv.so")
 
 Q4_OK, Q4_EINVAL, Q4_ENULL, Q4_EALIGN, Q4_EDEVICE, Q4_ELAUNCH = 0, -1, -2, -3, -4, -5
 
-# Exported C symbols, in the order include/q4gemv.h and include/q4blocks.h
-# declare them.
+# Exported C symbols, in the order include/q4gemv.h, include/q4blocks.h and
+# include/q4scan.h declare them.
 EXPORTS = ("gemv_q4", "gemv_q4_swiglu", "gemv_f32", "dequant_q4", "read_reduce", "write_fill",
            "gemv_q4_geometry", "gemv_q4_path", "q4_strerror", "q4_abi_version",
            "gemv_q4_set_geometry", "gemv_q4_clear_geometry",
            "block_geometry", "gemv_block", "dequant_block", "gemv_block_set_config",
-           "gemv_block_config")
+           "gemv_block_config", "scan2", "scan2_set_config", "scan2_config")
 
 # Block formats of include/q4blocks.h.
 BLK_Q4_0, BLK_Q8_0, BLK_Q4_K, BLK_Q5_K, BLK_Q6_K = 1, 2, 3, 4, 5
@@ -74,13 +74,17 @@ def lib() -> ctypes.CDLL:
     L.dequant_block.argtypes = [I, P, P, I, I, P]
     L.gemv_block_set_config.argtypes = [I, I, I, I]
     L.gemv_block_config.argtypes = [I, IP, IP, IP]
+    L.scan2.argtypes = [P, P, P, I, I, I, P]
+    L.scan2_set_config.argtypes = [I, I, I, I]
+    L.scan2_config.argtypes = [IP, IP, IP, IP]
     L.q4_strerror.argtypes = [I]
     L.q4_strerror.restype = ctypes.c_char_p
     L.q4_abi_version.argtypes = []
     for f in ("gemv_q4", "gemv_q4_swiglu", "gemv_f32", "dequant_q4", "read_reduce", "write_fill",
               "gemv_q4_geometry", "gemv_q4_path", "q4_abi_version",
               "gemv_q4_set_geometry", "gemv_q4_clear_geometry", "block_geometry", "gemv_block",
-              "dequant_block", "gemv_block_set_config", "gemv_block_config"):
+              "dequant_block", "gemv_block_set_config", "gemv_block_config", "scan2",
+              "scan2_set_config", "scan2_config"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -322,4 +326,36 @@ def gemv_block_set_config(fmt, rows_per_lane: int = 0, waves_per_group: int = 0,
 def gemv_block_config(fmt) -> tuple[int, int, int]:
     v = [ctypes.c_int() for _ in range(3)]
     _check("gemv_block_config", lib().gemv_block_config(_fmt(fmt), *[ctypes.byref(t) for t in v]))
+    return tuple(t.value for t in v)
+
+
+# ---------------------------------------------------------------- 2-bit scan
+
+def scan2(codes: torch.Tensor, lut: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """scores[V, Q] = sum_d lut[q, d, code(v, d)] for codes uint32 (or int32)
+    [V, D/16] and lut float32 [Q, D, 4]."""
+    _need(codes, "codes", (torch.int32, torch.uint32) if hasattr(torch, "uint32") else (torch.int32,))
+    dev = codes.device
+    _need(lut, "lut", (torch.float32,), dev)
+    if codes.dim() != 2 or lut.dim() != 3 or lut.shape[2] != 4 or lut.shape[1] != 16 * codes.shape[1]:
+        raise ValueError(f"codes must be [V, D/16] and lut [Q, D, 4]: got {tuple(codes.shape)}, "
+                         f"{tuple(lut.shape)}")
+    V, Q, D = codes.shape[0], lut.shape[0], lut.shape[1]
+    out = _out(out, V, Q, dev)
+    _check("scan2", lib().scan2(_ptr(codes), _ptr(lut), _ptr(out), V, D, Q, _stream(dev)))
+    return out
+
+
+def scan2_set_config(lut_in_lds: int = 0, vectors_per_thread: int = 0,
+                     threads_per_group: int = 0, threads_per_vector: int = 0) -> None:
+    """The scan's knobs: table in LDS (1) or memory (0), vectors per thread
+    (1, 2), threads per workgroup (64, 256, 1024), threads per vector (1, 2,
+    4, 8; an upper bound); all zero restores the default (host-only)."""
+    _check("scan2_set_config", lib().scan2_set_config(lut_in_lds, vectors_per_thread,
+                                                      threads_per_group, threads_per_vector))
+
+
+def scan2_config() -> tuple[int, int, int, int]:
+    v = [ctypes.c_int() for _ in range(4)]
+    _check("scan2_config", lib().scan2_config(*[ctypes.byref(t) for t in v]))
     return tuple(t.value for t in v)

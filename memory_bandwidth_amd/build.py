@@ -18,7 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libq4gemv.so")
-SOURCES = ["api.cpp", "gemv_q4.hip", "gemv_f32.hip", "dequant_q4.hip", "probes.hip", "gemv_blocks.hip"]
+SOURCES = ["api.cpp", "gemv_q4.hip", "gemv_f32.hip", "dequant_q4.hip", "probes.hip", "gemv_blocks.hip",
+           "scan2.hip"]
 ARCH = "gfx950"
 
 # Packed-FP32 instructions stay off: the code never asks for them and the
