@@ -530,7 +530,8 @@ def run_scan(torch, q4, dev, reps_target_s: float = 0.02) -> dict:
         per.append((b - a) / (reps * n_corpora))
     t = statistics.median(per)
     nbytes = V * D // 4
-    lds_bytes = V * D * 16 * ((Q + 3) // 4)        # table bytes read from LDS per scan
+    lds_bytes = V * D * 8 * ((Q + 3) // 4)         # table bytes read from LDS per scan:
+                                                   # 16 B per pair of dimensions and query group
     log(f"scan2 {V} x {Q} D={D}: {t * 1e6:.3f} us/scan, {nbytes / t / 1e9:.1f} GB/s of codes, "
         f"{lds_bytes / t / 1e12:.1f} TB/s of LDS table reads")
     res = {"V": V, "Q": Q, "D": D, "bytes_per_call": nbytes, "corpora": n_corpora,
@@ -619,8 +620,9 @@ def summarize_stats(d: str, name: str, command: str) -> str:
         avg = float(sc[0]["AverageNs"]) * 1e-9
         lines += ["", f"scan2 ({V} vectors x {wl.SCAN_QUERIES} queries, D = {D}): average "
                       f"{avg * 1e6:.3f} us -> {V * D / 4 / avg / 1e9:.1f} GB/s of codes "
-                      f"({V * D // 4} B per scan), {V * D * 32 / avg / 1e12:.1f} TB/s of LDS "
-                      "table reads (32 B per vector and dimension)."]
+                      f"({V * D // 4} B per scan), {V * D * 16 / avg / 1e12:.1f} TB/s of LDS "
+                      "table reads (16 B per vector and pair of dimensions, for each group of "
+                      "four queries)."]
     blk = [r for r in stats if "gemv_blk_kernel" in r["Name"]]
     if blk:
         s = wl.STREAM_SHAPE

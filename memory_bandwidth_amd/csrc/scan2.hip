@@ -12,16 +12,18 @@
 //     256-CU part 65,536 vectors then fill one wavefront per SIMD, too few
 //     to hide LDS latency).  Codes come in 16-byte loads (64 dimensions),
 //     the next chunk's load issued before the current chunk's lookups.
-//   * With the table in LDS, every workgroup first stages it as
-//     [d][code][query] float4 groups (queries padded to a multiple of 4), so
-//     one ds_read_b128 returns four queries' entries for one (d, code).  The
-//     lanes of one part of the dimensions are at the same dimension and
-//     address at most four distinct 16-byte groups (broadcast reads); the
-//     parts are offset from one another by padding, so that they fall in
-//     different banks.
+//   * A workgroup serves one group of four queries.  With the table in LDS
+//     it first builds, for every pair of dimensions and each of the 16 code
+//     pairs, the float4 of its four queries' two-entry sums, so one
+//     ds_read_b128 covers two dimensions (the scan is bound by these reads:
+//     16 bytes of table per pair of dimensions and four queries, against
+//     half a byte of codes).  The parts of a vector's dimensions are offset
+//     from one another by padding, so that they fall in different banks.
 //   * With the table read from memory, each lookup is a 4-byte load that
 //     the caches serve (the page's "storage" variant).
-//   * Sums are fp32, per vector and query, in increasing d.
+//   * Sums are fp32, per vector and query, in increasing d (two dimensions
+//     at a time from the LDS table: each entry is one fp32 sum of two table
+//     values).
 #include "q4_common.h"
 #include "q4scan.h"
 
@@ -32,43 +34,52 @@ namespace {
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// Q4: groups of four queries (1 or 2).  VPT: vectors per thread.  TPV:
+// One workgroup scores its vectors against one group of four queries (the
+// query groups of the same vectors are adjacent workgroups, so the second
+// read of the codes finds them in L2).  VPT: vectors per thread.  TPV:
 // threads per vector (each takes a contiguous 1/TPV of the dimensions; their
 // partial sums meet through lane shuffles).  W: wavefronts per workgroup.
-// LDS: table staged in LDS.
+// LDS: the table staged in LDS; otherwise every lookup reads the caller's
+// table from memory.
 //
-// LDS layout: part p of the dimensions (the range one of a vector's TPV
-// threads scans) starts 256 / TPV bytes further into the bank rows than a
-// plain [d][code][query] layout would put it, so that the TPV lanes of a
-// vector, at the same position of their parts, read different banks.
-template <int Q4, int VPT, int TPV, int W, bool LDS>
+// LDS table: per pair of dimensions (2p, 2p + 1) and per 4-bit code pair
+// c0 + 4 c1, the float4 of the four queries' lut[q, 2p, c0] + lut[q, 2p + 1,
+// c1], so one ds_read_b128 covers two dimensions.  Part t of the pairs (the
+// range one of a vector's TPV threads scans) starts 256 / TPV bytes further
+// into the bank rows than a plain layout would put it, so that the TPV lanes
+// of a vector, at the same position of their parts, read different banks.
+template <int VPT, int TPV, int W, bool LDS>
 __global__ __launch_bounds__(W * 64) void scan2_kernel(const uint32_t *__restrict__ codes,
                                                        const float *__restrict__ lut,
                                                        float *__restrict__ scores, int V, int D,
                                                        int Q) {
     constexpr int T = W * 64;
-    constexpr int QP = 4 * Q4;
     constexpr int PAD = 16 / TPV;         // float4s of padding before each part
-    extern __shared__ f32x4_t slut[];     // [part][D/TPV][4][Q4] (+ padding) when LDS
+    extern __shared__ f32x4_t slut[];     // [pair][16] float4 (+ padding) when LDS
     const int tid = threadIdx.x;
-    const int DP = D / TPV;               // dimensions per part
+    const int NQG = (Q + 3) >> 2;         // query groups
+    const int qg = (int)blockIdx.x % NQG;
+    const int vb = (int)blockIdx.x / NQG; // vector block
+    const int q0 = 4 * qg;
+    const int NP = D >> 1;                // dimension pairs
+    const int PP = NP / TPV;              // pairs per part
     if constexpr (LDS) {
-        // One float4 of lut (the four codes of one (q, d)) per step.
-        const int n = Q * D;
+        // One (pair, query) per step: two float4 of lut (the four codes of
+        // each dimension) give that query's 16 sums.
         float *sl = reinterpret_cast<float *>(slut);
-        for (int i = tid; i < n; i += T) {
-            const int q = i / D, d = i - q * D;
-            const f32x4_t v = reinterpret_cast<const f32x4_t *>(lut)[i];
-            const int base = ((d * 4) * Q4 + (d / DP) * PAD) * 4 + q;   // float index of (d, code 0, q)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) sl[base + c * Q4 * 4] = v[c];
-        }
-        if (Q % 4) {                      // padded queries read as zero
-            for (int i = tid; i < D * 4; i += T) {
-                const int d = i >> 2, c = i & 3;
-                const int base = ((d * 4 + c) * Q4 + (d / DP) * PAD) * 4;
-                for (int q = Q; q < QP; ++q) sl[base + q] = 0.f;
+        for (int i = tid; i < NP * 4; i += T) {
+            const int pr = i >> 2, j = i & 3, q = q0 + j;
+            f32x4_t a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+            if (q < Q) {
+                const f32x4_t *l = reinterpret_cast<const f32x4_t *>(lut) + (size_t)q * D + 2 * pr;
+                a = l[0];
+                b = l[1];
             }
+            const int base = (pr * 16 + (pr / PP) * PAD) * 4 + j;
+#pragma unroll
+            for (int c1 = 0; c1 < 4; ++c1)
+#pragma unroll
+                for (int c0 = 0; c0 < 4; ++c0) sl[base + (c0 + 4 * c1) * 4] = a[c0] + b[c1];
         }
         __syncthreads();
     }
@@ -84,18 +95,18 @@ __global__ __launch_bounds__(W * 64) void scan2_kernel(const uint32_t *__restric
     const u32x4_t *src[VPT];
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-        const int v = ((int)blockIdx.x * VPT + k) * SLOTS + slot;
+        const int v = (vb * VPT + k) * SLOTS + slot;
         ok[k] = v < V;
         vk[k] = min(v, V - 1);            // past V: re-read the last vector, store nothing
         src[k] = reinterpret_cast<const u32x4_t *>(codes + (size_t)vk[k] * WPV) + part * CPP;
     }
-    float acc[VPT][QP];
+    float acc[VPT][4];
 #pragma unroll
     for (int k = 0; k < VPT; ++k)
 #pragma unroll
-        for (int q = 0; q < QP; ++q) acc[k][q] = 0.f;
+        for (int q = 0; q < 4; ++q) acc[k][q] = 0.f;
 
-    const int d0 = part * DP;
+    const int p0 = part * PP;             // first pair of this part
     const int sbase = part * PAD;         // this part's padding, in float4s
     u32x4_t cur[VPT], nxt[VPT];
 #pragma unroll
@@ -108,24 +119,24 @@ __global__ __launch_bounds__(W * 64) void scan2_kernel(const uint32_t *__restric
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int d = d0 + ch * 64 + j * 16 + i;
+            for (int n = 0; n < 8; ++n) {
+                const int pr = p0 + ch * 32 + j * 8 + n;     // dimensions 2 pr, 2 pr + 1
 #pragma unroll
                 for (int k = 0; k < VPT; ++k) {
-                    const int c = (int)((cur[k][j] >> (2 * i)) & 3u);
+                    const int c4 = (int)((cur[k][j] >> (4 * n)) & 15u);
                     if constexpr (LDS) {
-#pragma unroll
-                        for (int qq = 0; qq < Q4; ++qq) {
-                            const f32x4_t t = slut[(d * 4 + c) * Q4 + qq + sbase];
-                            acc[k][4 * qq] += t.x;
-                            acc[k][4 * qq + 1] += t.y;
-                            acc[k][4 * qq + 2] += t.z;
-                            acc[k][4 * qq + 3] += t.w;
-                        }
+                        const f32x4_t t = slut[pr * 16 + c4 + sbase];
+                        acc[k][0] += t.x;
+                        acc[k][1] += t.y;
+                        acc[k][2] += t.z;
+                        acc[k][3] += t.w;
                     } else {
+                        const int c0 = c4 & 3, c1 = c4 >> 2;
 #pragma unroll
-                        for (int q = 0; q < QP; ++q)
-                            if (q < Q) acc[k][q] += lut[((size_t)q * D + d) * 4 + c];
+                        for (int q = 0; q < 4; ++q)
+                            if (q0 + q < Q)
+                                acc[k][q] += lut[((size_t)(q0 + q) * D + 2 * pr) * 4 + c0] +
+                                             lut[((size_t)(q0 + q) * D + 2 * pr + 1) * 4 + c1];
                     }
                 }
             }
@@ -137,17 +148,17 @@ __global__ __launch_bounds__(W * 64) void scan2_kernel(const uint32_t *__restric
 #pragma unroll
     for (int k = 0; k < VPT; ++k)
 #pragma unroll
-        for (int q = 0; q < QP; ++q)
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int m = 1; m < TPV; m <<= 1) acc[k][q] += __shfl_xor(acc[k][q], m);
     if (part != 0) return;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
         if (!ok[k]) continue;
-        float *out = scores + (size_t)vk[k] * Q;
+        float *out = scores + (size_t)vk[k] * Q + q0;
 #pragma unroll
-        for (int q = 0; q < QP; ++q)
-            if (q < Q) out[q] = acc[k][q];
+        for (int q = 0; q < 4; ++q)
+            if (q0 + q < Q) out[q] = acc[k][q];
     }
 }
 
@@ -164,50 +175,51 @@ bool scan_cfg_ok(int lds, int vpt, int tpg, int tpv) {
            (tpv == 0 || tpv == 1 || tpv == 2 || tpv == 4 || tpv == 8);
 }
 
-int auto_tpv(int V, int vpt) {
+int auto_tpv(int V, int Q, int vpt) {
+    const int64_t groups = (Q + 3) / 4;
     int t = 1;
-    while (t < 8 && (int64_t)V * t / vpt < (int64_t)16 * 64 * kCUs) t <<= 1;
+    while (t < 8 && (int64_t)V * groups * t / vpt < (int64_t)16 * 64 * kCUs) t <<= 1;
     return t;
 }
 
-// LDS bytes of the staged table: D * 4 float4 groups of Q4, plus the parts'
+// LDS bytes of the staged table: D / 2 pairs of 16 float4, plus the parts'
 // padding.
-size_t lut_lds_bytes(int D, int Q4, int tpv) { return ((size_t)D * 4 * Q4 + 16) * 16; }
+size_t lut_lds_bytes(int D) { return ((size_t)D / 2 * 16 + 16) * 16; }
 
-template <int Q4, int VPT, int TPV, int W, bool LDS>
+template <int VPT, int TPV, int W, bool LDS>
 void launch_s(const uint32_t *codes, const float *lut, float *scores, int V, int D, int Q,
               hipStream_t st) {
     const int per = VPT * W * 64 / TPV;
-    const int grid = (V + per - 1) / per;
-    const size_t lds = LDS ? lut_lds_bytes(D, Q4, TPV) : 0;
-    hipLaunchKernelGGL((scan2_kernel<Q4, VPT, TPV, W, LDS>), dim3(grid), dim3(W * 64), lds, st, codes,
-                       lut, scores, V, D, Q);
+    const int grid = (V + per - 1) / per * ((Q + 3) / 4);
+    const size_t lds = LDS ? lut_lds_bytes(D) : 0;
+    hipLaunchKernelGGL((scan2_kernel<VPT, TPV, W, LDS>), dim3(grid), dim3(W * 64), lds, st, codes, lut,
+                       scores, V, D, Q);
 }
 
-template <int Q4, int VPT, int TPV, bool LDS>
+template <int VPT, int TPV, bool LDS>
 void launch_w(int tpg, const uint32_t *codes, const float *lut, float *scores, int V, int D, int Q,
               hipStream_t st) {
-    if (tpg == 64) launch_s<Q4, VPT, TPV, 1, LDS>(codes, lut, scores, V, D, Q, st);
-    else if (tpg == 1024) launch_s<Q4, VPT, TPV, 16, LDS>(codes, lut, scores, V, D, Q, st);
-    else launch_s<Q4, VPT, TPV, 4, LDS>(codes, lut, scores, V, D, Q, st);
+    if (tpg == 64) launch_s<VPT, TPV, 1, LDS>(codes, lut, scores, V, D, Q, st);
+    else if (tpg == 1024) launch_s<VPT, TPV, 16, LDS>(codes, lut, scores, V, D, Q, st);
+    else launch_s<VPT, TPV, 4, LDS>(codes, lut, scores, V, D, Q, st);
 }
 
-template <int Q4, int VPT, bool LDS>
+template <int VPT, bool LDS>
 void launch_t(const ScanCfg &c, const uint32_t *codes, const float *lut, float *scores, int V, int D,
               int Q, hipStream_t st) {
     switch (c.tpv) {
-    case 2: launch_w<Q4, VPT, 2, LDS>(c.tpg, codes, lut, scores, V, D, Q, st); break;
-    case 4: launch_w<Q4, VPT, 4, LDS>(c.tpg, codes, lut, scores, V, D, Q, st); break;
-    case 8: launch_w<Q4, VPT, 8, LDS>(c.tpg, codes, lut, scores, V, D, Q, st); break;
-    default: launch_w<Q4, VPT, 1, LDS>(c.tpg, codes, lut, scores, V, D, Q, st); break;
+    case 2: launch_w<VPT, 2, LDS>(c.tpg, codes, lut, scores, V, D, Q, st); break;
+    case 4: launch_w<VPT, 4, LDS>(c.tpg, codes, lut, scores, V, D, Q, st); break;
+    case 8: launch_w<VPT, 8, LDS>(c.tpg, codes, lut, scores, V, D, Q, st); break;
+    default: launch_w<VPT, 1, LDS>(c.tpg, codes, lut, scores, V, D, Q, st); break;
     }
 }
 
-template <int Q4, bool LDS>
+template <bool LDS>
 void launch_v(const ScanCfg &c, const uint32_t *codes, const float *lut, float *scores, int V, int D,
               int Q, hipStream_t st) {
-    if (c.vpt == 2) launch_t<Q4, 2, LDS>(c, codes, lut, scores, V, D, Q, st);
-    else launch_t<Q4, 1, LDS>(c, codes, lut, scores, V, D, Q, st);
+    if (c.vpt == 2) launch_t<2, LDS>(c, codes, lut, scores, V, D, Q, st);
+    else launch_t<1, LDS>(c, codes, lut, scores, V, D, Q, st);
 }
 
 }  // namespace
@@ -217,20 +229,15 @@ extern "C" int scan2(const uint32_t *codes, const float *lut, float *scores, int
     ScanCfg c = g_scan;
     if (Q < 1 || Q > 8 || V < 0 || D < 64 || D % 64 != 0 || D > (c.lds ? 1024 : 4096))
         return Q4_EINVAL;
-    if (c.tpv == 0) c.tpv = auto_tpv(V, c.vpt);
+    if (c.tpv == 0) c.tpv = auto_tpv(V, Q, c.vpt);
     while ((D / 64) % c.tpv != 0) c.tpv >>= 1;    // the most threads per vector that split D evenly
     if (V == 0) return Q4_OK;
     if (!codes || !lut || !scores) return Q4_ENULL;
     if (!q4::aligned(codes, 16) || !q4::aligned(lut, 16) || !q4::aligned(scores, 16)) return Q4_EALIGN;
     if (int st = q4::check_device(); st != Q4_OK) return st;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (Q <= 4) {
-        if (c.lds) launch_v<1, true>(c, codes, lut, scores, V, D, Q, st);
-        else launch_v<1, false>(c, codes, lut, scores, V, D, Q, st);
-    } else {
-        if (c.lds) launch_v<2, true>(c, codes, lut, scores, V, D, Q, st);
-        else launch_v<2, false>(c, codes, lut, scores, V, D, Q, st);
-    }
+    if (c.lds) launch_v<true>(c, codes, lut, scores, V, D, Q, st);
+    else launch_v<false>(c, codes, lut, scores, V, D, Q, st);
     return q4::launch_status();
 }
 
