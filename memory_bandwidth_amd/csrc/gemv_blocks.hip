@@ -20,7 +20,10 @@
 //     every Q6_K load stays inside its own block.
 //   * Each weight is an exact small integer -- the code minus its offset
 //     (8 for Q4_0, 32 for Q6_K, none otherwise) -- times x, so a code equal
-//     to its offset contributes exactly zero.  Sums run in fp32 per 16 or 32
+//     to its offset contributes exactly zero.  Q4_0, Q4_K and Q6_K form two
+//     such integers at once in binary16 (a code OR 0x6400 is 1024 + code,
+//     one v_pk_add_f16 removes 1024 + offset) and v_fma_mix_f32 multiplies
+//     them by fp32 x; Q8_0 and Q5_K convert with v_bfe / v_cvt.  Sums run in fp32 per 16 or 32
 //     elements and take their block or sub-block scale once; the Q4_K/Q5_K
 //     min term is dmin * m_j times the sub-block's sum of x.
 //   * The dequantiser decodes through the same per-format code and forms
@@ -76,6 +79,25 @@ __device__ __forceinline__ float sfield(uint32_t v, int at, int bits) {
 // Byte j of v as a float (v_cvt_f32_ubyte<j>).
 __device__ __forceinline__ float ubyte(uint32_t v, int j) { return (float)((v >> (8 * j)) & 0xFFu); }
 
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// (a & m) | o in one VALU op (gfx9 VOP3 takes no literal, so the compiler
+// would split it into v_and_b32 + v_or_b32).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(o));
+    return r;
+}
+__device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+
+// Binary16 decoding of small codes: a code c in bits 0..9 of a half word OR
+// 0x6400 is the binary16 value 1024 + c (1024 <= v < 2048 has unit spacing),
+// so one v_and_or_b32 unpacks two codes and one v_pk_add_f16 subtracting
+// 1024 + offset leaves the exact integers c - offset; v_fma_mix_f32 then
+// multiplies them by the fp32 x.  A code in bits 4..7 gives 1024 + 16 c, and
+// 16 (c - offset) after the subtraction, also exact.
+constexpr uint32_t kMagic = 0x64006400u;
+
 // ---------------------------------------------------------------------------
 // Per-format unit decoding.  For unit u of a row starting at byte `ro` of a
 // buffer resource:
@@ -90,6 +112,7 @@ __device__ __forceinline__ float ubyte(uint32_t v, int j) { return (float)((v >>
 struct FmtQ4_0 {
     static constexpr int kMaxR = 4;   // row slots per lane without spilling
     static constexpr bool kMin = false;
+    static constexpr bool kDot = true;
     struct Raw { uint32_t v[9]; };
     __device__ static void load(Raw &r, rsrc_t rs, uint32_t ro, int u) {
         const uint32_t o = ro + 36u * (uint32_t)u;      // two 18-byte blocks
@@ -104,6 +127,34 @@ struct FmtQ4_0 {
         a[0] = a[1] = dA;
         a[2] = a[3] = dB;
         b[0] = b[1] = b[2] = b[3] = -0.f;   // fma(a, v, -0) keeps the sign of a zero product
+    }
+    // dk[k]: sums over lane elements 16k .. 16k + 15 of (c - 8) x.
+    __device__ static void dot(const Raw &r, int, const float (&xv)[64], float (&dk)[4]) {
+        const half2_t z1 = as_h2(0x64086408u), z16 = as_h2(0x64806480u);   // 1024 + 8, 1024 + 128
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            float lo = 0.f, hi = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t w = blk == 0 ? realign(r.v[i], r.v[i + 1], 2) : r.v[5 + i];
+                const uint32_t w8 = w >> 8;
+                const half2_t d0 = as_h2(and_or(w, 0x000F000Fu, kMagic)) - z1;    // elements 4i, 4i + 2
+                const half2_t d1 = as_h2(and_or(w8, 0x000F000Fu, kMagic)) - z1;   // 4i + 1, 4i + 3
+                const half2_t d2 = as_h2(and_or(w, 0x00F000F0u, kMagic)) - z16;   // 16 x (16 + 4i, 16 + 4i + 2)
+                const half2_t d3 = as_h2(and_or(w8, 0x00F000F0u, kMagic)) - z16;  // 16 x (16 + 4i + 1, + 3)
+                const float *x = xv + 32 * blk + 4 * i;
+                lo = __builtin_fmaf((float)d0.x, x[0], lo);
+                lo = __builtin_fmaf((float)d1.x, x[1], lo);
+                lo = __builtin_fmaf((float)d0.y, x[2], lo);
+                lo = __builtin_fmaf((float)d1.y, x[3], lo);
+                hi = __builtin_fmaf((float)d2.x, x[16], hi);
+                hi = __builtin_fmaf((float)d3.x, x[17], hi);
+                hi = __builtin_fmaf((float)d2.y, x[18], hi);
+                hi = __builtin_fmaf((float)d3.y, x[19], hi);
+            }
+            dk[2 * blk] = lo;
+            dk[2 * blk + 1] = hi * 0.0625f;
+        }
     }
     template <class Fn> __device__ static void visit(const Raw &r, int, Fn &&fn) {
         // Nibble c ^ 8, sign-extended, is c - 8.
@@ -125,6 +176,7 @@ struct FmtQ4_0 {
 struct FmtQ8_0 {
     static constexpr int kMaxR = 4;   // row slots per lane without spilling
     static constexpr bool kMin = false;
+    static constexpr bool kDot = false;
     struct Raw { uint32_t v[17]; };
     __device__ static void load(Raw &r, rsrc_t rs, uint32_t ro, int u) {
         const uint32_t o = ro + 68u * (uint32_t)u;      // two 34-byte blocks
@@ -191,6 +243,7 @@ __device__ __forceinline__ void k_affine(const uint32_t *hd, int u, float (&a)[4
 struct FmtQ4_K {
     static constexpr int kMaxR = 4;   // row slots per lane without spilling
     static constexpr bool kMin = true;
+    static constexpr bool kDot = true;
     struct Raw { uint32_t v[12]; };
     __device__ static void load(Raw &r, rsrc_t rs, uint32_t ro, int u) {
         const uint32_t ob = ro + 144u * (uint32_t)(u >> 2);
@@ -203,6 +256,33 @@ struct FmtQ4_K {
     __device__ static int xstart(int u, int run) { return 64 * u + 32 * run; }
     __device__ static void affine(const Raw &r, int u, float (&a)[4], float (&b)[4]) {
         k_affine(r.v, u, a, b);
+    }
+    // dk[0], dk[1]: sub-block 2p (low nibbles), dk[2], dk[3]: sub-block 2p + 1.
+    __device__ static void dot(const Raw &r, int, const float (&xv)[64], float (&dk)[4]) {
+        const half2_t z = as_h2(kMagic);                 // 1024
+        float hi[2] = {0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < 2; ++k) dk[k] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t w = r.v[4 + i], w8 = w >> 8;
+            const half2_t d0 = as_h2(and_or(w, 0x000F000Fu, kMagic)) - z;    // elements 4i, 4i + 2
+            const half2_t d1 = as_h2(and_or(w8, 0x000F000Fu, kMagic)) - z;   // 4i + 1, 4i + 3
+            const half2_t d2 = as_h2(and_or(w, 0x00F000F0u, kMagic)) - z;    // 16 x (32 + 4i, 32 + 4i + 2)
+            const half2_t d3 = as_h2(and_or(w8, 0x00F000F0u, kMagic)) - z;   // 16 x (32 + 4i + 1, + 3)
+            const int k = i >> 2;
+            const float *xa = xv + 4 * i, *xb = xv + 32 + 4 * i;
+            dk[k] = __builtin_fmaf((float)d0.x, xa[0], dk[k]);
+            dk[k] = __builtin_fmaf((float)d1.x, xa[1], dk[k]);
+            dk[k] = __builtin_fmaf((float)d0.y, xa[2], dk[k]);
+            dk[k] = __builtin_fmaf((float)d1.y, xa[3], dk[k]);
+            hi[k] = __builtin_fmaf((float)d2.x, xb[0], hi[k]);
+            hi[k] = __builtin_fmaf((float)d3.x, xb[1], hi[k]);
+            hi[k] = __builtin_fmaf((float)d2.y, xb[2], hi[k]);
+            hi[k] = __builtin_fmaf((float)d3.y, xb[3], hi[k]);
+        }
+        dk[2] = hi[0] * 0.0625f;
+        dk[3] = hi[1] * 0.0625f;
     }
     template <class Fn> __device__ static void visit(const Raw &r, int, Fn &&fn) {
 #pragma unroll
@@ -221,6 +301,7 @@ struct FmtQ4_K {
 struct FmtQ5_K {
     static constexpr int kMaxR = 2;   // row slots per lane without spilling
     static constexpr bool kMin = true;
+    static constexpr bool kDot = false;
     struct Raw { uint32_t v[20]; };
     __device__ static void load(Raw &r, rsrc_t rs, uint32_t ro, int u) {
         const uint32_t ob = ro + 176u * (uint32_t)(u >> 2);
@@ -260,9 +341,24 @@ struct FmtQ5_K {
 // its half.  Blocks are 210 bytes, so a block may start 2 bytes past a
 // dword boundary; its ql and qh runs are read as 9 aligned dwords each and
 // shifted into place, its scales and d with 16-bit loads.
+// The 6-bit codes of one Q6_K dword: bits 0..3 of byte j of the first result
+// are the low nibble of ql byte j and bits 4, 5 the two top bits at bit s2 of
+// qh byte j (quarter s), and the same from the high nibbles and bits s2 + 4
+// for the second (quarter s + 2).  Bits 6, 7 of each byte are left over from
+// the shifted qh and must be masked by the caller; one v_bfi_b32 merges the
+// nibble with the shifted top bits, whose spill into the neighbouring byte's
+// low nibble the merge discards.
+__device__ __forceinline__ void q6_codes(uint32_t ql, uint32_t qh, uint32_t s2, uint32_t &ca,
+                                         uint32_t &cb) {
+    constexpr uint32_t m = 0x0F0F0F0Fu;
+    ca = (ql & m) | ((qh << (4u - s2)) & ~m);
+    cb = ((ql >> 4) & m) | ((qh >> s2) & ~m);
+}
+
 struct FmtQ6_K {
     static constexpr int kMaxR = 2;   // row slots per lane without spilling
     static constexpr bool kMin = false;
+    static constexpr bool kDot = true;
     struct Raw { uint32_t l[9], h[9], sa, sb, d, sh; };
     __device__ static void load(Raw &r, rsrc_t rs, uint32_t ro, int u) {
         const uint32_t hf = (uint32_t)(u >> 1) & 1u, s = (uint32_t)u & 1u;
@@ -293,6 +389,33 @@ struct FmtQ6_K {
         a[3] = d * sfield(r.sb, 8, 8);
         b[0] = b[1] = b[2] = b[3] = -0.f;   // fma(a, v, -0) keeps the sign of a zero product
     }
+    __device__ static void dot(const Raw &r, int u, const float (&xv)[64], float (&dk)[4]) {
+        const uint32_t s2 = 2u * ((uint32_t)u & 1u);
+        const half2_t z = as_h2(0x64206420u);   // 1024 + 32
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dk[k] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t ql = realign(r.l[i], r.l[i + 1], r.sh);
+            const uint32_t qh = realign(r.h[i], r.h[i + 1], r.sh);
+            uint32_t ca, cb;
+            q6_codes(ql, qh, s2, ca, cb);
+            const half2_t a0 = as_h2(and_or(ca, 0x003F003Fu, kMagic)) - z;        // elements 4i, 4i + 2
+            const half2_t a1 = as_h2(and_or(ca >> 8, 0x003F003Fu, kMagic)) - z;   // 4i + 1, 4i + 3
+            const half2_t b0 = as_h2(and_or(cb, 0x003F003Fu, kMagic)) - z;        // 32 + 4i, ...
+            const half2_t b1 = as_h2(and_or(cb >> 8, 0x003F003Fu, kMagic)) - z;
+            const int ka = i >> 2, kb = 2 + (i >> 2);
+            const float *xa = xv + 4 * i, *xb = xv + 32 + 4 * i;
+            dk[ka] = __builtin_fmaf((float)a0.x, xa[0], dk[ka]);
+            dk[ka] = __builtin_fmaf((float)a1.x, xa[1], dk[ka]);
+            dk[ka] = __builtin_fmaf((float)a0.y, xa[2], dk[ka]);
+            dk[ka] = __builtin_fmaf((float)a1.y, xa[3], dk[ka]);
+            dk[kb] = __builtin_fmaf((float)b0.x, xb[0], dk[kb]);
+            dk[kb] = __builtin_fmaf((float)b1.x, xb[1], dk[kb]);
+            dk[kb] = __builtin_fmaf((float)b0.y, xb[2], dk[kb]);
+            dk[kb] = __builtin_fmaf((float)b1.y, xb[3], dk[kb]);
+        }
+    }
     template <class Fn> __device__ static void visit(const Raw &r, int u, Fn &&fn) {
         const uint32_t s2 = 2u * ((uint32_t)u & 1u);
         // A 6-bit code c ^ 32, sign-extended, is c - 32.
@@ -300,9 +423,10 @@ struct FmtQ6_K {
         for (int i = 0; i < 8; ++i) {
             const uint32_t ql = realign(r.l[i], r.l[i + 1], r.sh);
             const uint32_t qh = realign(r.h[i], r.h[i + 1], r.sh);
-            const uint32_t ca = ((ql & 0x0F0F0F0Fu) | (((qh >> s2) & 0x03030303u) << 4)) ^ 0x20202020u;
-            const uint32_t cb = (((ql >> 4) & 0x0F0F0F0Fu) | (((qh >> (s2 + 4)) & 0x03030303u) << 4)) ^
-                                0x20202020u;
+            uint32_t ca, cb;
+            q6_codes(ql, qh, s2, ca, cb);
+            ca ^= 0x20202020u;
+            cb ^= 0x20202020u;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 fn(4 * i + j, sfield(ca, 8 * j, 6));
@@ -433,7 +557,10 @@ __global__ __launch_bounds__(W * 64) void gemv_blk_kernel(const float *__restric
                 float a[4], b[4];
                 T::affine(raw[r], uc, a, b);
                 float dk[4] = {0.f, 0.f, 0.f, 0.f};
-                T::visit(raw[r], uc, [&](int e, float v) { dk[e >> 4] = __builtin_fmaf(v, xv[e], dk[e >> 4]); });
+                if constexpr (T::kDot)
+                    T::dot(raw[r], uc, xv, dk);
+                else
+                    T::visit(raw[r], uc, [&](int e, float v) { dk[e >> 4] = __builtin_fmaf(v, xv[e], dk[e >> 4]); });
                 float c = acc[r];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
@@ -545,8 +672,8 @@ bool geometry_of(int f, Geo &g) {
 // configuration set through gemv_block_set_config applies to every shape.
 struct Cfg { int R, W, G; bool forced; };
 constexpr int kCUs = 256;
-constexpr Cfg kDefault[6] = {{0, 0, 0, false}, {1, 8, 2, false}, {1, 4, 2, false},
-                             {2, 4, 4, false}, {2, 4, 2, false}, {1, 4, 2, false}};
+constexpr Cfg kDefault[6] = {{0, 0, 0, false}, {2, 4, 0, false}, {1, 4, 2, false},
+                             {2, 4, 0, false}, {2, 4, 2, false}, {1, 4, 2, false}};
 constexpr Cfg kSmall = {1, 4, 0, false};
 Cfg g_cfg[6] = {kDefault[0], kDefault[1], kDefault[2], kDefault[3], kDefault[4], kDefault[5]};
 
