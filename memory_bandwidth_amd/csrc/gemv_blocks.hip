@@ -23,9 +23,10 @@
 //     to its offset contributes exactly zero.  Q4_0, Q4_K and Q6_K form two
 //     such integers at once in binary16 (a code OR 0x6400 is 1024 + code,
 //     one v_pk_add_f16 removes 1024 + offset) and v_fma_mix_f32 multiplies
-//     them by fp32 x; Q8_0 and Q5_K convert with v_bfe / v_cvt.  Sums run in fp32 per 16 or 32
-//     elements and take their block or sub-block scale once; the Q4_K/Q5_K
-//     min term is dmin * m_j times the sub-block's sum of x.
+//     them by fp32 x; Q8_0 and Q5_K convert with v_bfe / v_cvt.  Sums run
+//     in fp32 per 16 or 32 elements and take their block or sub-block scale
+//     once; the Q4_K/Q5_K min term is dmin * m_j times the sub-block's sum
+//     of x.
 //   * The dequantiser decodes through the same per-format code and forms
 //     each weight as fma(scale, integer, -min), one rounding of its exact
 //     value.
@@ -107,6 +108,11 @@ constexpr uint32_t kMagic = 0x64006400u;
 //   affine(raw, u, a, b)    weight of lane element e = a[e/16] * v + b[e/16]
 //                           (b = -dmin * m_j, or -0 where there is no min)
 //   visit(raw, u, fn)       fn(e, v) for e = 0..63 with v the exact integer
+//   dot(raw, u, xv, dk)     (formats with kDot) dk[k] = sum over lane
+//                           elements 16k .. 16k + 15 of v * xv[e], the same
+//                           products as visit, decoded two at a time
+// kMin: the format has a min term (b != -0).  kMaxR: the most row slots per
+// lane that compile without spilling.
 // ---------------------------------------------------------------------------
 
 struct FmtQ4_0 {
