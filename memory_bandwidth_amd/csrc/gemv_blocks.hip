@@ -214,36 +214,24 @@ struct FmtQ8_0 {
     }
 };
 
-// 6-bit scale and min of sub-block j from the 12 packed bytes, held in
-// header dwords 1..3 (bytes 4..15 of a Q4_K / Q5_K block).
-__device__ __forceinline__ void k_scale_min(uint32_t h1, uint32_t h2, uint32_t h3, int j,
-                                            float &s, float &m) {
-    const uint32_t sh = (uint32_t)(j & 3) * 8u;
-    const uint32_t b1 = (h1 >> sh) & 0xFFu, b2 = (h2 >> sh) & 0xFFu, b3 = (h3 >> sh) & 0xFFu;
-    uint32_t si, mi;
-    if (j < 4) {
-        si = b1 & 63u;
-        mi = b2 & 63u;
-    } else {
-        si = (b3 & 15u) | ((b1 >> 6) << 4);
-        mi = (b3 >> 4) | ((b2 >> 6) << 4);
-    }
-    s = (float)si;
-    m = (float)mi;
-}
-
-// Lane's quarter of a K-format block: sub-blocks 2p (low nibbles, lane
-// elements 0..31) and 2p + 1 (high nibbles, lane elements 32..63).
+// Scales and mins of the lane's pair of sub-blocks 2p, 2p + 1 (p = u % 4),
+// from header dwords 1..3 (bytes 4..15 of a Q4_K / Q5_K block: the 12 packed
+// bytes).  Sub-blocks 2p and 2p + 1 use bytes 2(p % 2) and 2(p % 2) + 1 of
+// each of those dwords, so one shift brings both into the low 16 bits:
+//   p < 2:  s = b1 & 63,                       m = b2 & 63
+//   p >= 2: s = (b3 & 15) | (b1 >> 6) << 4,    m = (b3 >> 4) | (b2 >> 6) << 4
+// and the two 6-bit fields of each pair come out in bytes 0 and 1.
 __device__ __forceinline__ void k_affine(const uint32_t *hd, int u, float (&a)[4], float (&b)[4]) {
-    const int p = u & 3;
+    const uint32_t sh = (uint32_t)(u & 1) * 16u;
+    const uint32_t b1 = hd[1] >> sh, b2 = hd[2] >> sh, b3 = hd[3] >> sh;
+    const bool low = (u & 2) == 0;
+    const uint32_t sw = low ? (b1 & 0x3F3Fu) : ((b3 & 0x0F0Fu) | ((b1 >> 2) & 0x3030u));
+    const uint32_t mw = low ? (b2 & 0x3F3Fu) : (((b3 >> 4) & 0x0F0Fu) | ((b2 >> 2) & 0x3030u));
     const float d = f16lo(hd[0]), dmin = f16hi(hd[0]);
-    float s0, m0, s1, m1;
-    k_scale_min(hd[1], hd[2], hd[3], 2 * p, s0, m0);
-    k_scale_min(hd[1], hd[2], hd[3], 2 * p + 1, s1, m1);
-    a[0] = a[1] = d * s0;          // exact: 11 + 6 significant bits
-    a[2] = a[3] = d * s1;
-    b[0] = b[1] = -(dmin * m0);
-    b[2] = b[3] = -(dmin * m1);
+    a[0] = a[1] = d * ubyte(sw, 0);          // exact: 11 + 6 significant bits
+    a[2] = a[3] = d * ubyte(sw, 1);
+    b[0] = b[1] = -(dmin * ubyte(mw, 0));
+    b[2] = b[3] = -(dmin * ubyte(mw, 1));
 }
 
 struct FmtQ4_K {
