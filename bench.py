@@ -401,6 +401,7 @@ def run_default(args):
     if not args.no_blocks:
         line["block_formats"] = run_block_formats(torch, q4, dev)
         line["scan2"] = run_scan(torch, q4, dev)
+        line["decoder_layer"] = run_decoder_layer(torch, q4, dev)
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
@@ -544,16 +545,94 @@ def run_scan(torch, q4, dev, reps_target_s: float = 0.02) -> dict:
     return res
 
 
+LAYER_COPIES = 64   # distinct decoder layers cycled (64 x 8.6 MB > L2 + MALL)
+
+
+def run_decoder_layer(torch, q4, dev, reps_target_s: float = 0.02) -> dict:
+    """One decoder layer at the gerbil page's MatMul example shapes (WGSL
+    Kernel Reference: hidden 896, FFN 4864), with q 896 and k, v 128 wide,
+    g32, as seven separate int4 GEMVs
+    against four launches: q, k and v stored as one [1152, 896] matrix (their
+    rows one after another, one GEMV), o, gate and up fused with the SwiGLU
+    combine, down.  Layer 0 comes from the seeded generator, the other
+    distinct layers are device copies of it.  The fused q/k/v output is gated
+    against gemv_f32 on the dequantised matrix; both passes are timed by
+    two-point differences of graph replays (median of three), per layer."""
+    seed = wl.config_seed(1)
+    shapes = wl.DECODER_LAYER
+    mats = [wl.make_q4_weights(seed, s.N, s.K, s.g, s.s_lo, s.s_hi, index=20 + i)
+            for i, s in enumerate(shapes)]
+    host = {"sep": mats, "qkv": wl.fuse_rows(*mats[:3])}
+    to_dev = lambda m: {k: torch.from_numpy(v).to(dev) for k, v in m.items()}
+    l0 = {"sep": [to_dev(m) for m in host["sep"]], "qkv": to_dev(host["qkv"])}
+    clone = lambda m: {k: v.clone() for k, v in m.items()}
+    layers = [l0] + [{"sep": [clone(m) for m in l0["sep"]], "qkv": clone(l0["qkv"])}
+                     for _ in range(LAYER_COPIES - 1)]
+    H, F = shapes[0].K, shapes[4].N
+    nq = shapes[0].N + shapes[1].N + shapes[2].N
+    x = torch.from_numpy(wl.make_x(seed, 1, H, index=20)).to(dev)
+    buf = lambda n: torch.empty((1, n), dtype=torch.float32, device=dev)
+    ys = [buf(s.N) for s in shapes]
+    yqkv, yo, ysw, yd = buf(nq), buf(H), buf(F), buf(H)
+    q = l0["qkv"]
+    w = q4.dequant_q4(q["wq"], q["scales"], q["zeros"], 32, want_codes=False)[0]
+    got = q4.gemv_q4(x, q["wq"], q["scales"], q["zeros"], 32)
+    err = (got.double() - q4.gemv_f32(x, w).double()).abs()
+    tol = 2 * (1e-4 * q4.gemv_f32(x.abs(), w.abs()).double() + 1e-6)
+    if not bool((err <= tol).all()):
+        raise SystemExit(f"fused q/k/v gate failed: worst err/tol {float((err / tol).max()):.3g}")
+    del w
+
+    def unfused():
+        for L in layers:
+            for i, (m, y) in enumerate(zip(L["sep"], ys)):
+                xin = ys[5] if i == 6 else x          # down reads an FFN-wide activation
+                q4.gemv_q4(xin, m["wq"], m["scales"], m["zeros"], 32, out=y)
+
+    def fused():
+        for L in layers:
+            m, (o, g, u, d) = L["qkv"], L["sep"][3:]
+            q4.gemv_q4(x, m["wq"], m["scales"], m["zeros"], 32, out=yqkv)
+            q4.gemv_q4(x, o["wq"], o["scales"], o["zeros"], 32, out=yo)
+            q4.gemv_q4_swiglu(x, (g["wq"], g["scales"], g["zeros"]),
+                              (u["wq"], u["scales"], u["zeros"]), 32, out=ysw)
+            q4.gemv_q4(ysw, d["wq"], d["scales"], d["zeros"], 32, out=yd)
+
+    nbytes = sum(wl.q4_weight_bytes(s.N, s.K, s.g) for s in shapes)
+    res = {"layer": "hidden 896, ffn 4864, q 896, k/v 128, g32", "bytes_per_layer": nbytes,
+           "layers_cycled": LAYER_COPIES}
+    for name, fn, launches in (("unfused", unfused, 7), ("fused", fused, 4)):
+        G = Graph(fn, torch)
+        G.time(2)
+        t1 = G.time(1)
+        reps = max(1, int(reps_target_s / max(t1, 1e-6)))
+        per = []
+        for _ in range(3):
+            a, b = G.time(reps), G.time(2 * reps)
+            per.append((b - a) / (reps * LAYER_COPIES))
+        t = statistics.median(per)
+        res[name] = {"launches_per_layer": launches, "us_per_layer": round(t * 1e6, 3),
+                     "GBps": round(nbytes / t / 1e9, 1)}
+        log(f"decoder layer {name:8s} ({launches} launches): {t * 1e6:7.3f} us/layer, "
+            f"{nbytes / t / 1e9:7.1f} GB/s of weights")
+        del G
+    del layers
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_blocks_only(args):
     import torch
     import memory_bandwidth_amd as q4
     only = set(args.block_shapes.split(",")) if args.block_shapes else None
     dev = torch.device("cuda:0")
     out = {"unit": "GB/s", "peak": SPEC_PEAK_GBS}
-    if not only or only != {"scan"}:
+    if not only or only - {"scan", "layer"}:
         out["block_formats"] = run_block_formats(torch, q4, dev, only=only)
     if not only or "scan" in only:
         out["scan2"] = run_scan(torch, q4, dev)
+    if not only or "layer" in only:
+        out["decoder_layer"] = run_decoder_layer(torch, q4, dev)
     print(json.dumps(out), flush=True)
 
 
@@ -710,7 +789,7 @@ def main(argv=None):
     ap.add_argument("--no-blocks", action="store_true", help="skip the block-format cells")
     ap.add_argument("--blocks-only", action="store_true", help="only the block-format cells")
     ap.add_argument("--block-shapes", default="",
-                    help="with --blocks-only: comma list of shape labels (stream, 'lm head', ..., scan)")
+                    help="with --blocks-only: comma list of shape labels (stream, 'lm head', ..., scan, layer)")
     ap.add_argument("--pmc-workload", action="store_true")
     ap.add_argument("--summarize", metavar="DIR", help="rocprofv3 CSV dir (stats, or FETCH_SIZE pmc)")
     ap.add_argument("--summarize-write", metavar="DIR", help="WRITE_SIZE pmc dir (with --summarize)")

@@ -56,6 +56,33 @@ def test_config0_single_896():
     assert_within(y, y_ref, b, s.label)
 
 
+def test_config1_fused_layer():
+    """The decoder layer in four launches: q, k and v as one matrix whose rows
+    are theirs one after another, o, the SwiGLU block of gate and up, down."""
+    mats = [wl.make_q4_weights(wl.config_seed(1), s.N, s.K, s.g, s.s_lo, s.s_hi, index=10 + i)
+            for i, s in enumerate(wl.DECODER_LAYER)]
+    x = wl.make_x(wl.config_seed(1), 1, 896, index=10)
+    qkv = wl.fuse_rows(*mats[:3])
+    assert qkv["wq"].shape == (896 + 128 + 128, 448)
+    t = dev(dict(qkv, x=x))
+    y = run_q4(t, 32)
+    y_ref, b = oracle.gemv_q4(x, qkv["wq"], qkv["scales"], qkv["zeros"], 32)
+    assert_within(y, y_ref, b, "fused qkv")
+    o = 0
+    for i in range(3):                         # each slice is that matrix's GEMV
+        m = mats[i]
+        yi, bi = oracle.gemv_q4(x, m["wq"], m["scales"], m["zeros"], 32)
+        assert_within(y[:, o:o + m["wq"].shape[0]], yi, bi, wl.DECODER_LAYER[i].label)
+        o += m["wq"].shape[0]
+    gate, up = dev(mats[4]), dev(mats[5])
+    ys = q4.gemv_q4_swiglu(t["x"], (gate["wq"], gate["scales"], gate["zeros"]),
+                           (up["wq"], up["scales"], up["zeros"]), 32)
+    torch.cuda.synchronize()
+    ys_ref, tol = oracle.swiglu(x, (mats[4]["wq"], mats[4]["scales"], mats[4]["zeros"]),
+                                (mats[5]["wq"], mats[5]["scales"], mats[5]["zeros"]), 32)
+    assert np.all(np.abs(ys.cpu().numpy().astype(np.float64) - ys_ref) <= tol)
+
+
 def test_config1_decoder_layer():
     for i, s in enumerate(wl.DECODER_LAYER):
         d = wl.make_q4_problem(wl.config_seed(1), s, index=i)

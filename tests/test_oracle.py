@@ -409,3 +409,16 @@ def test_swiglu_invariants():
     dead = (flat, d["scales"], d["zeros"])
     assert np.all(oracle.swiglu(d["x"], mat, dead, s.g)[0] == 0)
     assert np.all(oracle.swiglu(d["x"], dead, mat, s.g)[0] == 0)
+
+
+def test_fused_rows_are_the_separate_gemvs():
+    """Matrices stored one after another (workloads.fuse_rows) give, row for
+    row, the GEMVs of the separate matrices: the layout mixes nothing."""
+    mats = [workloads.make_q4_weights(22, n, 256, 32, 0.005, 0.02, index=i)
+            for i, n in enumerate((40, 8, 8))]
+    x = workloads.make_x(22, 2, 256)
+    fused = workloads.fuse_rows(*mats)
+    y, b = oracle.gemv_q4(x, fused["wq"], fused["scales"], fused["zeros"], 32)
+    parts = [oracle.gemv_q4(x, m["wq"], m["scales"], m["zeros"], 32) for m in mats]
+    assert np.array_equal(y, np.concatenate([p[0] for p in parts], axis=1))
+    assert np.array_equal(b, np.concatenate([p[1] for p in parts], axis=1))

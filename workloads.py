@@ -127,6 +127,14 @@ def make_q4_problem(seed: int, shape: Q4Shape, index: int = 0) -> dict[str, np.n
     return d
 
 
+def fuse_rows(*mats: dict) -> dict:
+    """Matrices of the same K and group size stored as one: their rows one
+    after another (codes, scales and zero points alike), so one GEMV of the
+    result computes all of them (q, k and v of a decoder layer as one
+    [N_q + N_k + N_v, K] matrix).  Layout only."""
+    return {k: np.concatenate([m[k] for m in mats], axis=0) for k in ("wq", "scales", "zeros")}
+
+
 def make_exact_problem(seed: int, M: int, N: int, K: int, g: int,
                        index: int = 0) -> dict[str, np.ndarray]:
     """Inputs on which fp32 accumulation is exact in any order.
