@@ -22,14 +22,22 @@ Also in the default line ("block_formats" and "scan2", skipped with
 of the cera page at the same 4096 x 14336 stream shape and at the page's four
 decode shapes, each cycling >= 1 GiB of distinct matrices; and the 2-bit
 corpus scan of the Refractometer page, 65,536 vectors x 8 queries, D = 768,
-cycling 64 distinct corpora.
+cycling 64 distinct corpora; and one decoder layer (hidden 896, FFN 4864) as
+seven GEMVs and as four launches, cycling 64 distinct layers.  Then
+("bandwidth_sweep", skipped with --no-sweep) the Refractometer page's
+bandwidth sweep: vec4 read-reduce and vec4 copy over buffers from 16 KiB to
+2 GiB, the best of three workgroup counts per size, cliffs marked by the
+page's 80% rule, and from them the cache class of the stream's working set;
+and the fixed cost of one launch in a graph ("launch_gap_us").
 
 Other modes:
-  --blocks-only     only the block-format and scan cells (--block-shapes to pick)
+  --blocks-only     only the block-format, scan, layer and sweep cells
+                    (--block-shapes to pick)
   --pmc-workload    a short fixed sequence of dispatches for rocprofv3 --pmc
   --summarize DIR   turn rocprofv3 CSV output in DIR into a profiles/ summary
 The CPU oracle is timed on a bounded sample of the same workload
-(cpu_baseline); it is the only use of oracle/ here.
+(cpu_baseline: rows split over up to 16 host threads, and on one thread); it
+is the only use of oracle/ here.
 """
 
 from __future__ import annotations
@@ -204,24 +212,48 @@ def gate(torch, q4, W):
     torch.cuda.synchronize()
 
 
-def cpu_baseline(budget_s: float = 12.0) -> dict:
-    """The oracle, as it stands, on a bounded sample of the stream workload."""
+CPU_THREADS_MAX = 16   # the host cores one GPU's share of the machine holds
+
+
+def _oracle_rate(budget_s: float, threads: int):
+    """GB/s of the oracle over whole stream matrices until `budget_s` of
+    oracle time: with threads > 1 each matrix's rows are split into that many
+    contiguous ranges, one oracle call per range on its own thread (the
+    oracle releases the interpreter lock while it runs)."""
+    import concurrent.futures
+    import numpy as np
     import oracle
     s = wl.STREAM_SHAPE
     seed = wl.config_seed(4)
     x = wl.make_x(seed, 1, s.K)
+    parts = np.array_split(np.arange(s.N, dtype=np.int64), threads)
     nbytes, done, t_used = 0, 0, 0.0
-    while done < wl.STREAM_MATRICES and (t_used < budget_s or done == 0):
-        d = wl.make_q4_weights(seed, s.N, s.K, s.g, s.s_lo, s.s_hi, index=done)
-        t0 = time.perf_counter()
-        oracle.gemv_q4(x, d["wq"], d["scales"], d["zeros"], s.g)
-        t_used += time.perf_counter() - t0
-        nbytes += wl.q4_weight_bytes(s.N, s.K, s.g)
-        done += 1
-    return {"value": round(nbytes / t_used / 1e9, 5), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{done} of the 32 stream matrices, full 14336x4096 GEMV each, "
-                      f"single-threaded f64 C oracle, {t_used:.1f} s",
+    with concurrent.futures.ThreadPoolExecutor(threads) as ex:
+        while done < wl.STREAM_MATRICES and (t_used < budget_s or done == 0):
+            d = wl.make_q4_weights(seed, s.N, s.K, s.g, s.s_lo, s.s_hi, index=done)
+            t0 = time.perf_counter()
+            if threads == 1:
+                oracle.gemv_q4(x, d["wq"], d["scales"], d["zeros"], s.g)
+            else:
+                list(ex.map(lambda r: oracle.gemv_q4(x, d["wq"], d["scales"], d["zeros"], s.g, rows=r),
+                            parts))
+            t_used += time.perf_counter() - t0
+            nbytes += wl.q4_weight_bytes(s.N, s.K, s.g)
+            done += 1
+    return nbytes / t_used / 1e9, done, t_used
+
+
+def cpu_baseline(budget_s: float = 12.0) -> dict:
+    """The oracle, as it stands, on a bounded sample of the stream workload:
+    on every host core of one GPU's share (at most 16 threads) and on one."""
+    threads = max(1, min(CPU_THREADS_MAX, os.cpu_count() or 1))
+    v1, n1, t1 = _oracle_rate(budget_s / 2, 1)
+    vn, nn, tn = _oracle_rate(budget_s / 2, threads) if threads > 1 else (v1, n1, t1)
+    return {"value": round(vn, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{nn} of the 32 stream matrices, full 14336x4096 GEMV each, f64 C oracle, "
+                      f"rows split over {threads} threads, {tn:.1f} s",
+            "single_core": {"value": round(v1, 5), "cores": 1,
+                            "sample": f"{n1} stream matrices on one thread, {t1:.1f} s"},
             "host_cpu": host_cpu(), "host_nproc": os.cpu_count()}
 
 
@@ -402,6 +434,17 @@ def run_default(args):
         line["block_formats"] = run_block_formats(torch, q4, dev)
         line["scan2"] = run_scan(torch, q4, dev)
         line["decoder_layer"] = run_decoder_layer(torch, q4, dev)
+    if not args.no_sweep:
+        sw = run_bandwidth_sweep(torch, q4, dev, W["probe"])
+        ws = wl.STREAM_MATRICES * bytes_per_call["gemv_q4"]
+        cl = sw["read_reduce"]["cliffs"]
+        lv = cache_level(ws, cl)
+        sw["stream_working_set_bytes"] = ws
+        line["bandwidth_sweep"] = sw
+        # past every cliff of the read sweep: the working set streams from HBM
+        line["cache_class"] = ("hbm-streaming" if cl and lv == len(cl)
+                               else f"cache-resident: below the read sweep's cliff at {cl[lv]} B")
+        line["launch_gap_us"] = round(launch_gap(torch, q4, dev) * 1e6, 3)
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
@@ -545,6 +588,105 @@ def run_scan(torch, q4, dev, reps_target_s: float = 0.02) -> dict:
     return res
 
 
+# ---------------------------------------------------------------- bandwidth sweep
+
+SWEEP_MIN = 16 << 10            # buffer sizes 16 KiB, 32 KiB, ... 2 GiB
+SWEEP_STEPS = 18
+SWEEP_GRIDS = (256, 1024, 4096)  # workgroups tried at each size; the best is kept
+SWEEP_LAUNCH_BYTES = 1 << 30     # bytes one launch walks: passes = this / size, at most 4096
+CLIFF = 0.8                      # the Refractometer page's bandwidth cliff ratio
+
+
+def find_cliffs(sizes, best, ratio: float = CLIFF):
+    """Sizes where the best bandwidth falls below `ratio` of the best at any
+    smaller size since the previous cliff (each cliff starts a new level)."""
+    cliffs, ref = [], None
+    for s, b in zip(sizes, best):
+        if ref is not None and b < ratio * ref:
+            cliffs.append(s)
+            ref = b
+        else:
+            ref = b if ref is None else max(ref, b)
+    return cliffs
+
+
+def cache_level(nbytes: int, cliffs) -> int:
+    """0 for a working set below the first cliff size, 1 below the second, ..."""
+    return sum(1 for c in cliffs if nbytes >= c)
+
+
+def run_bandwidth_sweep(torch, q4, dev, src, samples: int = 25, sample_s: float = 2e-3) -> dict:
+    """The Refractometer page's bandwidth sweep: vec4 read-reduce and vec4
+    copy over buffers from 16 KiB to 2 GiB, each configuration (workgroup
+    count) timed as `samples` samples of back-to-back launches replayed from
+    one graph lasting about `sample_s` each (median, p10, p90 per launch);
+    the best configuration per size is kept and cliffs are marked by the
+    page's 80% rule.  Each launch walks its buffer `passes` times, so that a
+    buffer fitting a cache is re-read from it and the cost of a launch is
+    spread over about 1 GiB of traffic.  Copy bandwidth counts the bytes read
+    and written.  `src` is a float32 device buffer of at least 2 GiB."""
+    sizes = [SWEEP_MIN << k for k in range(SWEEP_STEPS)]
+    dst = torch.empty(sizes[-1] // 4, dtype=torch.float32, device=dev)
+    partials = torch.empty(max(SWEEP_GRIDS), dtype=torch.float32, device=dev)
+    out = {"sizes": sizes, "grids": list(SWEEP_GRIDS), "samples": samples}
+    for kind in ("read_reduce", "copy"):
+        rows = []
+        for size in sizes:
+            n = size // 4
+            passes = max(1, min(4096, SWEEP_LAUNCH_BYTES // size))
+            moved = size * passes * (2 if kind == "copy" else 1)
+            need = -(-n // 1024)                      # workgroups of 256 lanes x 16 B
+            best = None
+            for grid in sorted({min(g, need) for g in SWEEP_GRIDS}):
+                if kind == "copy":
+                    fn = lambda: q4.copy_vec4(src[:n], dst[:n], passes=passes, n_blocks=grid)
+                else:
+                    fn = lambda: q4.read_reduce(src[:n], grid, partials=partials, passes=passes)
+                fn()
+                torch.cuda.synchronize()
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                b.record()
+                b.synchronize()
+                reps = max(1, int(sample_s / max(a.elapsed_time(b) * 1e-3, 1e-7)))
+                G = Graph(lambda: [fn() for _ in range(reps)], torch)
+                G.time(1)
+                per = sorted(G.time(1) / reps for _ in range(samples))
+                med = statistics.median(per)
+                cell = {"grid": grid, "passes": passes, "GBps_median": moved / med / 1e9,
+                        "GBps_p10": moved / per[int(0.9 * (samples - 1))] / 1e9,
+                        "GBps_p90": moved / per[int(0.1 * (samples - 1))] / 1e9}
+                if best is None or cell["GBps_median"] > best["GBps_median"]:
+                    best = cell
+                del G
+            rows.append({k: (round(v, 1) if isinstance(v, float) else v) for k, v in best.items()})
+        gbs = [r["GBps_median"] for r in rows]
+        cliffs = find_cliffs(sizes, gbs)
+        out[kind] = {"best": rows, "cliffs": cliffs}
+        log(f"sweep {kind}: " + ", ".join(f"{s >> 10}K {g:.0f}" for s, g in zip(sizes, gbs)))
+        log(f"sweep {kind}: cliffs at " + (", ".join(f"{c >> 10} KiB" for c in cliffs) or "none"))
+    del dst
+    torch.cuda.empty_cache()
+    return out
+
+
+def launch_gap(torch, q4, dev, launches: int = 256) -> float:
+    """Seconds per launch of a kernel that reads nothing and writes one
+    float (read_reduce over an empty buffer), back to back in one graph,
+    by two-point difference: the fixed cost every launch pays."""
+    empty = torch.empty(0, dtype=torch.float32, device=dev)
+    part = torch.empty(1, dtype=torch.float32, device=dev)
+    G = Graph(lambda: [q4.read_reduce(empty, 1, partials=part) for _ in range(launches)], torch)
+    G.time(2)
+    per = []
+    for _ in range(3):
+        a, b = G.time(4), G.time(8)
+        per.append((b - a) / (4 * launches))
+    return statistics.median(per)
+
+
 LAYER_COPIES = 64   # distinct decoder layers cycled (64 x 8.6 MB > L2 + MALL)
 
 
@@ -627,12 +769,17 @@ def run_blocks_only(args):
     only = set(args.block_shapes.split(",")) if args.block_shapes else None
     dev = torch.device("cuda:0")
     out = {"unit": "GB/s", "peak": SPEC_PEAK_GBS}
-    if not only or only - {"scan", "layer"}:
+    if not only or only - {"scan", "layer", "sweep"}:
         out["block_formats"] = run_block_formats(torch, q4, dev, only=only)
     if not only or "scan" in only:
         out["scan2"] = run_scan(torch, q4, dev)
     if not only or "layer" in only:
         out["decoder_layer"] = run_decoder_layer(torch, q4, dev)
+    if not only or "sweep" in only:
+        src = torch.rand(wl.PROBE_BYTES // 4, device=dev)
+        out["bandwidth_sweep"] = run_bandwidth_sweep(torch, q4, dev, src)
+        out["launch_gap_us"] = round(launch_gap(torch, q4, dev) * 1e6, 3)
+        del src
     print(json.dumps(out), flush=True)
 
 
@@ -787,9 +934,10 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-blocks", action="store_true", help="skip the block-format cells")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the 16 KiB - 2 GiB bandwidth sweep")
     ap.add_argument("--blocks-only", action="store_true", help="only the block-format cells")
     ap.add_argument("--block-shapes", default="",
-                    help="with --blocks-only: comma list of shape labels (stream, 'lm head', ..., scan, layer)")
+                    help="with --blocks-only: comma list of shape labels (stream, 'lm head', ..., scan, layer, sweep)")
     ap.add_argument("--pmc-workload", action="store_true")
     ap.add_argument("--summarize", metavar="DIR", help="rocprofv3 CSV dir (stats, or FETCH_SIZE pmc)")
     ap.add_argument("--summarize-write", metavar="DIR", help="WRITE_SIZE pmc dir (with --summarize)")

@@ -132,6 +132,24 @@ int dequant_q4(const uint8_t *wq, const uint16_t *scales, const uint8_t *zeros,
 int read_reduce(const float *buf, size_t n_floats, float *partials, int n_partials,
                 void *stream);
 
+/* read_reduce walking buf `passes` times in one launch (1 <= passes <= 4096);
+ * each partial is the sum over all passes.  A buffer that fits a cache is
+ * then re-read from it, which the bandwidth sweep uses to find the caches'
+ * knees.  read_reduce is this call with passes = 1.  Other arguments and
+ * errors as read_reduce. */
+int read_reduce_passes(const float *buf, size_t n_floats, int passes, float *partials,
+                       int n_partials, void *stream);
+
+/* Copy-bandwidth probe (Refractometer "What each sweep measures", bandwidth:
+ * vec4 copy): dst[i] = src[i] for i < n_floats with 16-byte loads and
+ * stores, the whole range copied `passes` times in one launch.
+ *   src, dst 16-byte aligned and not overlapping (Q4_EINVAL if they do);
+ *   n_floats % 4 == 0 (n_floats == 0 launches nothing); 1 <= passes <= 4096;
+ *   0 <= n_blocks <= 65536 workgroups of 256 threads (0 picks the default
+ *   grid; never more than the range needs). */
+int copy_vec4(const float *src, float *dst, size_t n_floats, int passes, int n_blocks,
+              void *stream);
+
 /* Write-bandwidth probe (webgpu-bench 0.1.0 README, write-bandwidth): stores
  * `value` to every element with 16-byte stores and no reads.
  *   buf 16-byte aligned, n_floats % 4 == 0 (n_floats == 0 launches nothing);

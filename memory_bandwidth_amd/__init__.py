@@ -26,7 +26,8 @@ Q4_OK, Q4_EINVAL, Q4_ENULL, Q4_EALIGN, Q4_EDEVICE, Q4_ELAUNCH = 0, -1, -2, -3, -
 
 # Exported C symbols, in the order include/q4gemv.h, include/q4blocks.h and
 # include/q4scan.h declare them.
-EXPORTS = ("gemv_q4", "gemv_q4_swiglu", "gemv_f32", "dequant_q4", "read_reduce", "write_fill",
+EXPORTS = ("gemv_q4", "gemv_q4_swiglu", "gemv_f32", "dequant_q4", "read_reduce",
+           "read_reduce_passes", "copy_vec4", "write_fill",
            "gemv_q4_geometry", "gemv_q4_path", "q4_strerror", "q4_abi_version",
            "gemv_q4_set_geometry", "gemv_q4_clear_geometry",
            "block_geometry", "gemv_block", "dequant_block", "gemv_block_set_config",
@@ -63,6 +64,8 @@ def lib() -> ctypes.CDLL:
     L.gemv_f32.argtypes = [P, P, P, I, I, I, P]
     L.dequant_q4.argtypes = [P, P, P, P, P, I, I, I, P]
     L.read_reduce.argtypes = [P, Z, P, I, P]
+    L.read_reduce_passes.argtypes = [P, Z, I, P, I, P]
+    L.copy_vec4.argtypes = [P, P, Z, I, I, P]
     L.write_fill.argtypes = [P, Z, ctypes.c_float, I, P]
     IP = ctypes.POINTER(ctypes.c_int)
     L.gemv_q4_geometry.argtypes = [I, I, I, I, IP, IP, IP, IP, IP, IP]
@@ -80,8 +83,8 @@ def lib() -> ctypes.CDLL:
     L.q4_strerror.argtypes = [I]
     L.q4_strerror.restype = ctypes.c_char_p
     L.q4_abi_version.argtypes = []
-    for f in ("gemv_q4", "gemv_q4_swiglu", "gemv_f32", "dequant_q4", "read_reduce", "write_fill",
-              "gemv_q4_geometry", "gemv_q4_path", "q4_abi_version",
+    for f in ("gemv_q4", "gemv_q4_swiglu", "gemv_f32", "dequant_q4", "read_reduce",
+              "read_reduce_passes", "copy_vec4", "write_fill", "gemv_q4_geometry", "gemv_q4_path", "q4_abi_version",
               "gemv_q4_set_geometry", "gemv_q4_clear_geometry", "block_geometry", "gemv_block",
               "dequant_block", "gemv_block_set_config", "gemv_block_config", "scan2",
               "scan2_set_config", "scan2_config"):
@@ -211,8 +214,10 @@ def dequant_q4(wq: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, grou
     return w, c
 
 
-def read_reduce(buf: torch.Tensor, n_partials: int, partials: torch.Tensor | None = None) -> torch.Tensor:
-    """Launches the read probe; returns the per-workgroup partial sums (add them for the total)."""
+def read_reduce(buf: torch.Tensor, n_partials: int, partials: torch.Tensor | None = None,
+                passes: int = 1) -> torch.Tensor:
+    """Launches the read probe (walking buf `passes` times); returns the
+    per-workgroup partial sums (add them for the total)."""
     _need(buf, "buf", (torch.float32,))
     dev = buf.device
     if partials is None:
@@ -221,9 +226,28 @@ def read_reduce(buf: torch.Tensor, n_partials: int, partials: torch.Tensor | Non
         _need(partials, "partials", (torch.float32,), dev)
         if partials.numel() < n_partials:
             raise ValueError("partials too small")
-    _check("read_reduce", lib().read_reduce(_ptr(buf), buf.numel(), _ptr(partials), n_partials,
-                                            _stream(dev)))
+    if passes == 1:
+        _check("read_reduce", lib().read_reduce(_ptr(buf), buf.numel(), _ptr(partials), n_partials,
+                                                _stream(dev)))
+    else:
+        _check("read_reduce_passes", lib().read_reduce_passes(
+            _ptr(buf), buf.numel(), passes, _ptr(partials), n_partials, _stream(dev)))
     return partials
+
+
+def copy_vec4(src: torch.Tensor, dst: torch.Tensor | None = None, passes: int = 1,
+              n_blocks: int = 0) -> torch.Tensor:
+    """Copies src into dst (a new tensor if None) with the copy probe."""
+    _need(src, "src", (torch.float32,))
+    if dst is None:
+        dst = torch.empty_like(src)
+    else:
+        _need(dst, "dst", (torch.float32,), src.device)
+        if dst.numel() != src.numel():
+            raise ValueError("dst and src differ in size")
+    _check("copy_vec4", lib().copy_vec4(_ptr(src), _ptr(dst), src.numel(), passes, n_blocks,
+                                        _stream(src.device)))
+    return dst
 
 
 def write_fill(buf: torch.Tensor, value: float, n_blocks: int = 0) -> torch.Tensor:

@@ -1,11 +1,16 @@
-// probes.hip -- HBM bandwidth probes for gfx950.
+// probes.hip -- bandwidth probes for gfx950.
 //
 // read_reduce streams a buffer with 16-byte loads folded by addition only
 // and writes one partial sum per workgroup (webgpu-bench 0.1.0 README,
 // read-bandwidth; Refractometer "What each sweep measures", bandwidth: vec4
-// read-reduce).  write_fill stores a constant with 16-byte stores and reads
-// nothing (webgpu-bench 0.1.0 README, write-bandwidth).  Both walk the buffer
-// grid-stride, so at every step the whole grid covers one contiguous span.
+// read-reduce).  copy_vec4 copies with 16-byte loads and stores (the same
+// Refractometer sweep: vec4 copy).  write_fill stores a constant with
+// 16-byte stores and reads nothing (webgpu-bench 0.1.0 README,
+// write-bandwidth).  All walk the buffer grid-stride, so at every step the
+// whole grid covers one contiguous span.  The read and copy probes can walk
+// the buffer several times per launch: a buffer that fits a cache is then
+// read from that cache, and the cost of the launch itself is spread over
+// the passes.
 #include "q4_common.h"
 #include "q4_device.h"
 
@@ -14,25 +19,29 @@ namespace {
 constexpr int kBlock = 256;
 constexpr int kUnroll = 8;                     // 16-byte loads in flight per lane
 constexpr int kDefaultFillBlocks = 4096;
+constexpr int kMaxPasses = 4096;
 
 __global__ __launch_bounds__(kBlock) void read_reduce_kernel(const float4 *__restrict__ buf,
-                                                             size_t n4, float *__restrict__ partials) {
+                                                             size_t n4, int passes,
+                                                             float *__restrict__ partials) {
     __shared__ float wsum[kBlock / 64];
     const size_t stride = (size_t)gridDim.x * kBlock;
-    size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x;
     float a[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) a[u] = 0.f;
-    for (; i + (kUnroll - 1) * stride < n4; i += kUnroll * stride) {
-        float4 v[kUnroll];
+    for (int p = 0; p < passes; ++p) {
+        size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x;
+        for (; i + (kUnroll - 1) * stride < n4; i += kUnroll * stride) {
+            float4 v[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) v[u] = buf[i + u * stride];
+            for (int u = 0; u < kUnroll; ++u) v[u] = buf[i + u * stride];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) a[u] += (v[u].x + v[u].y) + (v[u].z + v[u].w);
-    }
-    for (; i < n4; i += stride) {
-        const float4 v = buf[i];
-        a[0] += (v.x + v.y) + (v.z + v.w);
+            for (int u = 0; u < kUnroll; ++u) a[u] += (v[u].x + v[u].y) + (v[u].z + v[u].w);
+        }
+        for (; i < n4; i += stride) {
+            const float4 v = buf[i];
+            a[0] += (v.x + v.y) + (v.z + v.w);
+        }
     }
     float s = 0.f;
 #pragma unroll
@@ -48,6 +57,26 @@ __global__ __launch_bounds__(kBlock) void read_reduce_kernel(const float4 *__res
     }
 }
 
+// Each pass copies the whole range again; the empty asm keeps the compiler
+// from merging passes, whose stores it could otherwise prove redundant.
+__global__ __launch_bounds__(kBlock) void copy_kernel(const float4 *__restrict__ src,
+                                                      float4 *__restrict__ dst, size_t n4,
+                                                      int passes) {
+    const size_t stride = (size_t)gridDim.x * kBlock;
+    for (int p = 0; p < passes; ++p) {
+        size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x;
+        for (; i + (kUnroll - 1) * stride < n4; i += kUnroll * stride) {
+            float4 v[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) dst[i + u * stride] = v[u];
+        }
+        for (; i < n4; i += stride) dst[i] = src[i];
+        asm volatile("" ::: "memory");
+    }
+}
+
 __global__ __launch_bounds__(kBlock) void write_fill_kernel(float4 *__restrict__ buf, size_t n4,
                                                             float value) {
     const float4 v = make_float4(value, value, value, value);
@@ -57,16 +86,45 @@ __global__ __launch_bounds__(kBlock) void write_fill_kernel(float4 *__restrict__
 
 }  // namespace
 
-extern "C" int read_reduce(const float *buf, size_t n_floats, float *partials, int n_partials,
-                           void *stream) {
-    if (n_floats % 4 != 0 || n_partials < 1 || n_partials > 65536) return Q4_EINVAL;
+extern "C" int read_reduce_passes(const float *buf, size_t n_floats, int passes, float *partials,
+                                  int n_partials, void *stream) {
+    if (n_floats % 4 != 0 || n_partials < 1 || n_partials > 65536 || passes < 1 ||
+        passes > kMaxPasses)
+        return Q4_EINVAL;
     if (!partials || (n_floats && !buf)) return Q4_ENULL;
     if ((buf && !q4::aligned(buf, 16)) || !q4::aligned(partials, 4)) return Q4_EALIGN;
     const int dev = q4::check_device();
     if (dev != Q4_OK) return dev;
     hipLaunchKernelGGL(read_reduce_kernel, dim3(n_partials), dim3(kBlock), 0,
                        static_cast<hipStream_t>(stream), reinterpret_cast<const float4 *>(buf),
-                       n_floats / 4, partials);
+                       n_floats / 4, passes, partials);
+    return q4::launch_status();
+}
+
+extern "C" int read_reduce(const float *buf, size_t n_floats, float *partials, int n_partials,
+                           void *stream) {
+    return read_reduce_passes(buf, n_floats, 1, partials, n_partials, stream);
+}
+
+extern "C" int copy_vec4(const float *src, float *dst, size_t n_floats, int passes, int n_blocks,
+                         void *stream) {
+    if (n_floats % 4 != 0 || n_blocks < 0 || n_blocks > 65536 || passes < 1 || passes > kMaxPasses)
+        return Q4_EINVAL;
+    if (n_floats == 0) return Q4_OK;
+    if (!src || !dst) return Q4_ENULL;
+    if (!q4::aligned(src, 16) || !q4::aligned(dst, 16)) return Q4_EALIGN;
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+    const uintptr_t bytes = (uintptr_t)n_floats * 4u;
+    if (s0 < d0 + bytes && d0 < s0 + bytes) return Q4_EINVAL;   // the ranges overlap
+    const int dev = q4::check_device();
+    if (dev != Q4_OK) return dev;
+    const size_t n4 = n_floats / 4;
+    size_t blocks = n_blocks ? (size_t)n_blocks : (size_t)kDefaultFillBlocks;
+    const size_t need = (n4 + kBlock - 1) / kBlock;
+    if (blocks > need) blocks = need;
+    hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(kBlock), 0,
+                       static_cast<hipStream_t>(stream), reinterpret_cast<const float4 *>(src),
+                       reinterpret_cast<float4 *>(dst), n4, passes);
     return q4::launch_status();
 }
 

@@ -114,6 +114,19 @@ def test_other_entry_points_validation(L):
     assert L.write_fill(A16, 6, ctypes.c_float(1.0), 0, None) == q4.Q4_EINVAL
     assert L.write_fill(A16 + 8, 8, ctypes.c_float(1.0), 0, None) == q4.Q4_EALIGN
     assert L.write_fill(None, 0, ctypes.c_float(1.0), 0, None) == q4.Q4_OK
+    for passes in (0, -1, 4097):
+        assert L.read_reduce_passes(A16, 8, passes, A16B, 4, None) == q4.Q4_EINVAL
+        assert L.copy_vec4(A16, A16B, 8, passes, 0, None) == q4.Q4_EINVAL
+    assert L.read_reduce_passes(A16, 6, 2, A16B, 4, None) == q4.Q4_EINVAL
+    assert L.read_reduce_passes(A16 + 4, 8, 2, A16B, 4, None) == q4.Q4_EALIGN
+    assert L.copy_vec4(A16, A16B, 6, 1, 0, None) == q4.Q4_EINVAL
+    assert L.copy_vec4(A16, A16B, 8, 1, 65537, None) == q4.Q4_EINVAL
+    assert L.copy_vec4(A16, A16B, 8, 1, -1, None) == q4.Q4_EINVAL
+    assert L.copy_vec4(None, A16B, 8, 1, 0, None) == q4.Q4_ENULL
+    assert L.copy_vec4(A16, A16B + 8, 8, 1, 0, None) == q4.Q4_EALIGN
+    assert L.copy_vec4(A16, A16 + 16, 8, 1, 0, None) == q4.Q4_EINVAL     # overlapping ranges
+    assert L.copy_vec4(A16 + 16, A16, 8, 1, 0, None) == q4.Q4_EINVAL
+    assert L.copy_vec4(None, None, 0, 1, 0, None) == q4.Q4_OK
 
 
 def test_no_device_reports_edevice(L):
@@ -124,6 +137,7 @@ def test_no_device_reports_edevice(L):
     assert L.gemv_q4(A16, A16, A16, A16, A16, 1, 8, 128, 32, None) == q4.Q4_EDEVICE
     assert L.gemv_q4_swiglu(A16, A16, A16, A16, A16, A16, A16, A16, 1, 8, 128, 32, None) == q4.Q4_EDEVICE
     assert L.read_reduce(A16, 8, A16B, 4, None) == q4.Q4_EDEVICE
+    assert L.copy_vec4(A16, A16B, 8, 1, 0, None) == q4.Q4_EDEVICE
 
 
 SHAPES = ([workloads.SMALL_896, workloads.LM_HEAD, workloads.STREAM_SHAPE]

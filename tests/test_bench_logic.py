@@ -84,3 +84,13 @@ def test_multi_gpu_request_exits_with_message():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0 and "one GPU" in r.stderr
+
+
+def test_cliffs_follow_the_80_percent_rule():
+    sizes = [1, 2, 4, 8, 16, 32, 64]
+    # rises (launch-bound), plateau, first cliff at 16, a new level, second cliff at 64
+    best = [10, 50, 100, 95, 60, 58, 30]
+    assert bench.find_cliffs(sizes, best) == [16, 64]
+    assert bench.find_cliffs(sizes, [100, 81, 80.9, 80.5, 80.1, 80, 80]) == []
+    assert bench.find_cliffs(sizes, [100, 79, 79, 79, 79, 79, 79]) == [2]
+    assert [bench.cache_level(n, [16, 64]) for n in (1, 15, 16, 63, 64, 1000)] == [0, 0, 1, 1, 2, 2]

@@ -399,6 +399,25 @@ def test_read_reduce_random():
     assert abs(float(p.double().sum()) - s) <= 1e-5 * a + 1e-6
 
 
+@pytest.mark.parametrize("n,parts,passes", [(0, 3, 2), (4, 1, 3), (1 << 20, 7, 5), ((1 << 22) + 36, 2048, 16)])
+def test_read_reduce_passes_ones(n, parts, passes):
+    buf = torch.ones(n, device=DEV)
+    p = q4.read_reduce(buf, parts, passes=passes)
+    torch.cuda.synchronize()
+    assert float(p.double().sum()) == float(n * passes)
+
+
+@pytest.mark.parametrize("n,blocks,passes", [(4, 0, 1), (4096, 3, 2), ((1 << 22) + 8, 0, 1),
+                                             ((1 << 22) + 8, 65536, 3), ((1 << 20) + 4, 1, 1)])
+def test_copy_vec4(n, blocks, passes):
+    src = torch.from_numpy(wl.make_probe_buffer(n)).to(DEV)
+    buf = torch.full((n + 64,), float("nan"), device=DEV)
+    q4.copy_vec4(src, buf[:n], passes=passes, n_blocks=blocks)
+    torch.cuda.synchronize()
+    assert torch.equal(buf[:n], src)
+    assert bool(torch.isnan(buf[n:]).all())
+
+
 @pytest.mark.parametrize("n,blocks", [(4, 0), (4096, 3), ((1 << 22) + 8, 0), ((1 << 22) + 8, 65536)])
 def test_write_fill(n, blocks):
     buf = torch.full((n + 64,), float("nan"), device=DEV)
