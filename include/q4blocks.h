@@ -63,7 +63,8 @@ int block_geometry(int format, int *elems, int *bytes);
  * sub-block as dmin * m_j * sum(x).  Accuracy: |y - y_exact| <= 1e-4 * B +
  * 1e-6, with B = sum_k |x_k| * |W(n, k)|, and for Q4_K/Q5_K B = sum_k |x_k|
  * (|d s_j q| + |dmin m_j|).  A weight that decodes to Inf or NaN makes its
- * output row NaN or infinite. */
+ * output row NaN or infinite; an x that is Inf or NaN makes every output NaN
+ * or infinite. */
 int gemv_block(int format, const float *x, const uint8_t *w, float *y, int M, int N, int K,
                void *stream);
 

@@ -153,6 +153,17 @@ def test_wide_range_x(fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+def test_non_finite_x_poisons_every_row(fmt):
+    N, K = 37, 1024
+    w = wl.make_block_weights(58, fmt, N, K)
+    for bad in (np.nan, np.inf):
+        x = wl.make_x(59, 1, K)
+        x[0, 517] = bad
+        y = run(fmt, x, w)
+        assert not np.isfinite(y).any(), (fmt, bad)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_nan_scale_poisons_only_its_row(fmt):
     N, K = 9, 1024
     _, e, bb, offs = wl.BLOCK_FORMATS[fmt]
