@@ -116,21 +116,60 @@ __global__ __launch_bounds__(W * 64) void scan2_kernel(const uint32_t *__restric
 #pragma unroll
             for (int k = 0; k < VPT; ++k) nxt[k] = src[k][ch + 1];
         }
+        if constexpr (LDS) {
+            // The eight lookups of a code word are issued together, and with
+            // one vector per thread those of the next word before the sums
+            // of this one, so that 8 to 16 table reads per wavefront are in
+            // flight (read by read, LDS latency would bound the scan).
+            const f32x4_t *tb = slut + (p0 + ch * 32) * 16 + sbase;
+            auto lookups = [&](f32x4_t (&t)[VPT][8], int j) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+                for (int n = 0; n < 8; ++n)
 #pragma unroll
-            for (int n = 0; n < 8; ++n) {
-                const int pr = p0 + ch * 32 + j * 8 + n;     // dimensions 2 pr, 2 pr + 1
+                    for (int k = 0; k < VPT; ++k)
+                        t[k][n] = tb[(j * 8 + n) * 16 + (int)((cur[k][j] >> (4 * n)) & 15u)];
+            };
+            auto sums = [&](const f32x4_t (&t)[VPT][8]) {
 #pragma unroll
-                for (int k = 0; k < VPT; ++k) {
-                    const int c4 = (int)((cur[k][j] >> (4 * n)) & 15u);
-                    if constexpr (LDS) {
-                        const f32x4_t t = slut[pr * 16 + c4 + sbase];
-                        acc[k][0] += t.x;
-                        acc[k][1] += t.y;
-                        acc[k][2] += t.z;
-                        acc[k][3] += t.w;
-                    } else {
+                for (int n = 0; n < 8; ++n)
+#pragma unroll
+                    for (int k = 0; k < VPT; ++k) {
+                        acc[k][0] += t[k][n].x;
+                        acc[k][1] += t[k][n].y;
+                        acc[k][2] += t[k][n].z;
+                        acc[k][3] += t[k][n].w;
+                    }
+            };
+            f32x4_t ta[VPT][8];
+            if constexpr (VPT == 1) {
+                f32x4_t tn[VPT][8];
+                lookups(ta, 0);
+#pragma unroll
+                for (int j = 0; j < 4; j += 2) {
+                    lookups(tn, j + 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    sums(ta);
+                    if (j + 2 < 4) lookups(ta, j + 2);
+                    __builtin_amdgcn_sched_barrier(0);
+                    sums(tn);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    lookups(ta, j);
+                    __builtin_amdgcn_sched_barrier(0);
+                    sums(ta);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int n = 0; n < 8; ++n) {
+                    const int pr = p0 + ch * 32 + j * 8 + n;     // dimensions 2 pr, 2 pr + 1
+#pragma unroll
+                    for (int k = 0; k < VPT; ++k) {
+                        const int c4 = (int)((cur[k][j] >> (4 * n)) & 15u);
                         const int c0 = c4 & 3, c1 = c4 >> 2;
 #pragma unroll
                         for (int q = 0; q < 4; ++q)
