@@ -789,10 +789,15 @@ def run_blocks_only(args):
 
 # ---------------------------------------------------------------- --pmc-workload
 
+PMC_BLOCK_MATRICES = 8
+
+
 def run_pmc_workload(args):
     """A short, fixed dispatch sequence for counter collection: 64 gemv_q4 launches
     over the 32 stream matrices, 2 read_reduce and 2 write_fill over 2 GiB (the
-    calibration kernels of known size), 4 gemv_f32 launches."""
+    calibration kernels of known size), 4 gemv_f32 launches; then 16 gemv_block
+    launches per format at the stream shape over 8 distinct matrices, and 8
+    scans of distinct 65,536 x 768 corpora."""
     import torch
     import memory_bandwidth_amd as q4
     dev = torch.device("cuda:0")
@@ -806,6 +811,35 @@ def run_pmc_workload(args):
             q4.gemv_q4(W["x"], m["wq"], m["scales"], m["zeros"], s.g, out=y)
     for w, y in zip(W["wf"], W["yf"]):
         q4.gemv_f32(W["x"], w, out=y)
+    torch.cuda.synchronize()
+    del W
+    torch.cuda.empty_cache()
+    # every block format at the stream shape, 8 distinct matrices launched twice
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.config_seed(5))
+    x = torch.from_numpy(wl.make_x(wl.config_seed(5), 1, s.K)).to(dev)
+    y = torch.empty((1, s.N), dtype=torch.float32, device=dev)
+    for fmt, (code, e, bb, offs) in wl.BLOCK_FORMATS.items():
+        mats = []
+        for _ in range(PMC_BLOCK_MATRICES):
+            m = torch.randint(0, 256, (s.N, wl.block_row_bytes(fmt, s.K)), dtype=torch.uint8,
+                              device=dev, generator=gen)
+            v = m.view(s.N, s.K // e, bb)
+            for o in offs:
+                v[:, :, o] = 0x00
+                v[:, :, o + 1] = 0x20
+            mats.append(m)
+        for _ in range(2):
+            for m in mats:
+                q4.gemv_block(fmt, x, m, out=y)
+        del mats
+    # the scan over 8 distinct corpora of the Refractometer workload
+    V, Q, D = wl.SCAN_VECTORS, wl.SCAN_QUERIES, wl.SCAN_DIM
+    lut = torch.from_numpy(wl.make_scan_lut(wl.config_seed(6), Q, D)).to(dev)
+    out = torch.empty((V, Q), dtype=torch.float32, device=dev)
+    for _ in range(PMC_BLOCK_MATRICES):
+        c = torch.randint(-2**31, 2**31 - 1, (V, D // 16), dtype=torch.int32, device=dev, generator=gen)
+        q4.scan2(c, lut, out=out)
     torch.cuda.synchronize()
     log("pmc workload done")
 
@@ -913,6 +947,22 @@ def summarize_pmc(fetch_dir: str, write_dir: str, name: str, command: str) -> st
                   f"{alg} algorithmic bytes (+{4 * s.K + 4 * s.N} B of x and y): ratio "
                   f"{(fetch_b + write_b) / alg:.4f}.",
               f"Kernel source sha256[:16] {summary['kernel_source_sha256_16']}."]
+    for k, _ in sorted(mean):
+        if _ != "FETCH_SIZE":
+            continue
+        m = re.search(r"gemv_blk_kernel<FmtQ(\w+?),", k)
+        if m:
+            fmt = "q" + m.group(1).lower()
+            a = wl.block_row_bytes(fmt, s.K) * s.N
+            f = mean[(k, "FETCH_SIZE")] * 1024 * fetch_factor
+            lines.append(f"gemv_block {fmt} per launch (stream shape): {f:.0f} B fetched against "
+                         f"{a} algorithmic bytes: ratio {f / a:.4f}.")
+        elif k.startswith("scan2_kernel"):
+            a = wl.SCAN_VECTORS * wl.SCAN_DIM // 4
+            f = mean[(k, "FETCH_SIZE")] * 1024 * fetch_factor
+            lines.append(f"scan2 per launch (65,536 x 768 codes, 8 queries): {f:.0f} B fetched "
+                         f"against {a} B of codes: ratio {f / a:.4f} (each code is read by two "
+                         "workgroups, one per group of four queries).")
     out = os.path.join(PROFILES, name + ".md")
     open(out, "w").write("\n".join(lines) + "\n")
     return out
