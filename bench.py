@@ -962,7 +962,8 @@ def summarize_pmc(fetch_dir: str, write_dir: str, name: str, command: str) -> st
             f = mean[(k, "FETCH_SIZE")] * 1024 * fetch_factor
             lines.append(f"scan2 per launch (65,536 x 768 codes, 8 queries): {f:.0f} B fetched "
                          f"against {a} B of codes: ratio {f / a:.4f} (each code is read by two "
-                         "workgroups, one per group of four queries).")
+                         "workgroups, one per group of four queries, on one XCD: the second "
+                         "read is served by its L2).")
     out = os.path.join(PROFILES, name + ".md")
     open(out, "w").write("\n".join(lines) + "\n")
     return out

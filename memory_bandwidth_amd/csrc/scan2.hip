@@ -12,7 +12,8 @@
 //     256-CU part 65,536 vectors then fill one wavefront per SIMD, too few
 //     to hide LDS latency).  Codes come in 16-byte loads (64 dimensions),
 //     the next chunk's load issued before the current chunk's lookups.
-//   * A workgroup serves one group of four queries.  With the table in LDS
+//   * A workgroup serves one group of four queries; the two groups of the
+//     same vectors are placed on one XCD, sharing its L2.  With the table in LDS
 //     it first builds, for every pair of dimensions and each of the 16 code
 //     pairs, the float4 of its four queries' two-entry sums, so one
 //     ds_read_b128 covers two dimensions (the scan is bound by these reads:
@@ -35,8 +36,8 @@ typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // One workgroup scores its vectors against one group of four queries (the
-// query groups of the same vectors are adjacent workgroups, so the second
-// read of the codes finds them in L2).  VPT: vectors per thread.  TPV:
+// two query groups of the same vectors run on the same XCD, so that the
+// second read of the codes finds them in its L2).  VPT: vectors per thread.  TPV:
 // threads per vector (each takes a contiguous 1/TPV of the dimensions; their
 // partial sums meet through lane shuffles).  W: wavefronts per workgroup.
 // LDS: the table staged in LDS; otherwise every lookup reads the caller's
@@ -58,8 +59,19 @@ __global__ __launch_bounds__(W * 64) void scan2_kernel(const uint32_t *__restric
     extern __shared__ f32x4_t slut[];     // [pair][16] float4 (+ padding) when LDS
     const int tid = threadIdx.x;
     const int NQG = (Q + 3) >> 2;         // query groups
-    const int qg = (int)blockIdx.x % NQG;
-    const int vb = (int)blockIdx.x / NQG; // vector block
+    int qg = 0, vb = (int)blockIdx.x;     // query group, vector block
+    if (NQG == 2) {
+        // Workgroups are dealt to the eight XCDs in turn (workgroup b to XCD
+        // b % 8), each with its own L2.  The two query groups of a vector
+        // block take workgroups b and b + 8, on the same XCD, so that the
+        // second read of the block's codes finds them in that L2.  The grid
+        // is rounded up to a multiple of 16; workgroups past the last
+        // vector block have nothing to do.
+        const int b = (int)blockIdx.x, r = b >> 3;
+        qg = r & 1;
+        vb = (r >> 1) * 8 + (b & 7);
+        if (vb * VPT * (T / TPV) >= V) return;
+    }
     const int q0 = 4 * qg;
     const int NP = D >> 1;                // dimension pairs
     const int PP = NP / TPV;              // pairs per part
@@ -229,7 +241,8 @@ template <int VPT, int TPV, int W, bool LDS>
 void launch_s(const uint32_t *codes, const float *lut, float *scores, int V, int D, int Q,
               hipStream_t st) {
     const int per = VPT * W * 64 / TPV;
-    const int grid = (V + per - 1) / per * ((Q + 3) / 4);
+    const int nvb = (V + per - 1) / per;
+    const int grid = Q > 4 ? (2 * nvb + 15) / 16 * 16 : nvb;   // see the kernel's workgroup order
     const size_t lds = LDS ? lut_lds_bytes(D) : 0;
     hipLaunchKernelGGL((scan2_kernel<VPT, TPV, W, LDS>), dim3(grid), dim3(W * 64), lds, st, codes, lut,
                        scores, V, D, Q);
