@@ -284,6 +284,40 @@ def test_tuned_profile_is_well_formed_and_applies(clean_geometry):
             assert all(c["cliff"] == (c["frac_of_best"] < autotune.CLIFF) for c in timed)
             q4.gemv_q4_set_geometry(e["M"], e["N"], e["K"], e["group_size"], b["path"],
                                     b["waves"], b["ksplit"])
+        for e in prof.get("block_entries", []) + prof.get("scan_entries", []):
+            timed = [c for c in e["candidates"] if c["parity"]]
+            assert e["best"]["median_us"] == min(c["median_us"] for c in timed)
+            assert all(c["cliff"] == (c["frac_of_best"] < autotune.CLIFF) for c in timed)
+        try:
+            for e in prof.get("block_entries", []):
+                q4.gemv_block_set_config(e["format"], *e["best"]["config"])
+            for e in prof.get("scan_entries", []):
+                q4.scan2_set_config(*e["best"]["config"])
+        finally:
+            for fmt in q4.BLOCK_FORMATS:
+                q4.gemv_block_set_config(fmt, 0, 0, 0)
+            q4.scan2_set_config(0, 0, 0, 0)
+
+
+def test_profile_winner_rules():
+    """A block-format winner applies only when it wins at both large shapes
+    by at least 3%; the scan's only when it beats the default by 3%."""
+    from memory_bandwidth_amd import autotune
+
+    def be(fmt, shape, cfg, us, default_us):
+        return {"format": fmt, "N": shape[0], "K": shape[1],
+                "best": {"config": list(cfg), "median_us": us, "default_us": default_us}}
+
+    big, lm = autotune.BLOCK_LARGE
+    prof = {"block_entries": [be("q4_0", big, (2, 4, 1), 9.0, 10.0), be("q4_0", lm, (2, 4, 1), 9.0, 9.5),
+                              be("q8_0", big, (1, 4, 2), 9.0, 10.0), be("q8_0", lm, (2, 4, 2), 9.0, 10.0),
+                              be("q4_k", big, (1, 8, 2), 9.0, 9.1), be("q4_k", lm, (1, 8, 2), 9.0, 10.0),
+                              be("q6_k", big, (0, 0, 0), 9.0, 9.0), be("q6_k", lm, (0, 0, 0), 9.0, 9.0)],
+            "scan_entries": [{"best": {"config": [1, 1, 256, 2], "median_us": 10.0, "default_us": 10.4}}]}
+    assert autotune.block_winners(prof) == {"q4_0": (2, 4, 1)}
+    assert autotune.scan_winner(prof) == (1, 1, 256, 2)
+    prof["scan_entries"][0]["best"]["default_us"] = 10.2
+    assert autotune.scan_winner(prof) is None
 
 
 def test_block_and_scan_validation(L):
