@@ -13,7 +13,9 @@
 //     to hide LDS latency).  Codes come in 16-byte loads (64 dimensions),
 //     the next chunk's load issued before the current chunk's lookups.
 //   * A workgroup serves one group of four queries; the two groups of the
-//     same vectors are placed on one XCD, sharing its L2.  With the table in LDS
+//     same vectors are placed on one XCD, sharing its L2.  The grid holds
+//     the workgroups that fit the chip at once, each looping over vector
+//     blocks after building its table once.  With the table in LDS
 //     it first builds, for every pair of dimensions and each of the 16 code
 //     pairs, the float4 of its four queries' two-entry sums, so one
 //     ds_read_b128 covers two dimensions (the scan is bound by these reads:
@@ -58,20 +60,24 @@ __global__ __launch_bounds__(W * 64) void scan2_kernel(const uint32_t *__restric
     constexpr int PAD = 16 / TPV;         // float4s of padding before each part
     extern __shared__ f32x4_t slut[];     // [pair][16] float4 (+ padding) when LDS
     const int tid = threadIdx.x;
+    constexpr int SLOTS = T / TPV;        // vectors a workgroup scans per vector-per-thread step
     const int NQG = (Q + 3) >> 2;         // query groups
-    int qg = 0, vb = (int)blockIdx.x;     // query group, vector block
+    // Workgroups stay resident and loop over vector blocks vb0, vb0 + vstride,
+    // ..., building the table once.
+    int qg = 0, vb0 = (int)blockIdx.x, vstride = (int)gridDim.x;
     if (NQG == 2) {
         // Workgroups are dealt to the eight XCDs in turn (workgroup b to XCD
         // b % 8), each with its own L2.  The two query groups of a vector
         // block take workgroups b and b + 8, on the same XCD, so that the
         // second read of the block's codes finds them in that L2.  The grid
-        // is rounded up to a multiple of 16; workgroups past the last
-        // vector block have nothing to do.
+        // is a multiple of 16; workgroups past the last vector block have
+        // nothing to do.
         const int b = (int)blockIdx.x, r = b >> 3;
         qg = r & 1;
-        vb = (r >> 1) * 8 + (b & 7);
-        if (vb * VPT * (T / TPV) >= V) return;
+        vb0 = (r >> 1) * 8 + (b & 7);
+        vstride = (int)gridDim.x / 2;
     }
+    if ((int64_t)vb0 * VPT * SLOTS >= V) return;
     const int q0 = 4 * qg;
     const int NP = D >> 1;                // dimension pairs
     const int PP = NP / TPV;              // pairs per part
@@ -101,115 +107,117 @@ __global__ __launch_bounds__(W * 64) void scan2_kernel(const uint32_t *__restric
     const int CPP = NCH / TPV;            // chunks per part
     const int part = TPV == 1 ? 0 : tid % TPV;
     const int slot = TPV == 1 ? tid : tid / TPV;
-    constexpr int SLOTS = T / TPV;        // vectors a workgroup scans per vector-per-thread step
-    int vk[VPT];
-    bool ok[VPT];
-    const u32x4_t *src[VPT];
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-        const int v = (vb * VPT + k) * SLOTS + slot;
-        ok[k] = v < V;
-        vk[k] = min(v, V - 1);            // past V: re-read the last vector, store nothing
-        src[k] = reinterpret_cast<const u32x4_t *>(codes + (size_t)vk[k] * WPV) + part * CPP;
-    }
-    float acc[VPT][4];
-#pragma unroll
-    for (int k = 0; k < VPT; ++k)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[k][q] = 0.f;
-
     const int p0 = part * PP;             // first pair of this part
     const int sbase = part * PAD;         // this part's padding, in float4s
-    u32x4_t cur[VPT], nxt[VPT];
+    for (int vb = vb0; (int64_t)vb * VPT * SLOTS < V; vb += vstride) {
+        int vk[VPT];
+        bool ok[VPT];
+        const u32x4_t *src[VPT];
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) cur[k] = src[k][0];
-    for (int ch = 0; ch < CPP; ++ch) {
-        if (ch + 1 < CPP) {
-#pragma unroll
-            for (int k = 0; k < VPT; ++k) nxt[k] = src[k][ch + 1];
+        for (int k = 0; k < VPT; ++k) {
+            const int64_t v = ((int64_t)vb * VPT + k) * SLOTS + slot;
+            ok[k] = v < V;
+            vk[k] = (int)std::min<int64_t>(v, V - 1);   // past V: re-read the last vector, store nothing
+            src[k] = reinterpret_cast<const u32x4_t *>(codes + (size_t)vk[k] * WPV) + part * CPP;
         }
-        if constexpr (LDS) {
-            // The eight lookups of a code word are issued together, and with
-            // one vector per thread those of the next word before the sums
-            // of this one, so that 8 to 16 table reads per wavefront are in
-            // flight (read by read, LDS latency would bound the scan).
-            const f32x4_t *tb = slut + (p0 + ch * 32) * 16 + sbase;
-            auto lookups = [&](f32x4_t (&t)[VPT][8], int j) {
+        float acc[VPT][4];
 #pragma unroll
-                for (int n = 0; n < 8; ++n)
+        for (int k = 0; k < VPT; ++k)
 #pragma unroll
-                    for (int k = 0; k < VPT; ++k)
-                        t[k][n] = tb[(j * 8 + n) * 16 + (int)((cur[k][j] >> (4 * n)) & 15u)];
-            };
-            auto sums = [&](const f32x4_t (&t)[VPT][8]) {
+            for (int q = 0; q < 4; ++q) acc[k][q] = 0.f;
+
+        u32x4_t cur[VPT], nxt[VPT];
 #pragma unroll
-                for (int n = 0; n < 8; ++n)
+        for (int k = 0; k < VPT; ++k) cur[k] = src[k][0];
+        for (int ch = 0; ch < CPP; ++ch) {
+            if (ch + 1 < CPP) {
 #pragma unroll
-                    for (int k = 0; k < VPT; ++k) {
-                        acc[k][0] += t[k][n].x;
-                        acc[k][1] += t[k][n].y;
-                        acc[k][2] += t[k][n].z;
-                        acc[k][3] += t[k][n].w;
+                for (int k = 0; k < VPT; ++k) nxt[k] = src[k][ch + 1];
+            }
+            if constexpr (LDS) {
+                // The eight lookups of a code word are issued together, and with
+                // one vector per thread those of the next word before the sums
+                // of this one, so that 8 to 16 table reads per wavefront are in
+                // flight (read by read, LDS latency would bound the scan).
+                const f32x4_t *tb = slut + (p0 + ch * 32) * 16 + sbase;
+                auto lookups = [&](f32x4_t (&t)[VPT][8], int j) {
+#pragma unroll
+                    for (int n = 0; n < 8; ++n)
+#pragma unroll
+                        for (int k = 0; k < VPT; ++k)
+                            t[k][n] = tb[(j * 8 + n) * 16 + (int)((cur[k][j] >> (4 * n)) & 15u)];
+                };
+                auto sums = [&](const f32x4_t (&t)[VPT][8]) {
+#pragma unroll
+                    for (int n = 0; n < 8; ++n)
+#pragma unroll
+                        for (int k = 0; k < VPT; ++k) {
+                            acc[k][0] += t[k][n].x;
+                            acc[k][1] += t[k][n].y;
+                            acc[k][2] += t[k][n].z;
+                            acc[k][3] += t[k][n].w;
+                        }
+                };
+                f32x4_t ta[VPT][8];
+                if constexpr (VPT == 1) {
+                    f32x4_t tn[VPT][8];
+                    lookups(ta, 0);
+#pragma unroll
+                    for (int j = 0; j < 4; j += 2) {
+                        lookups(tn, j + 1);
+                        __builtin_amdgcn_sched_barrier(0);
+                        sums(ta);
+                        if (j + 2 < 4) lookups(ta, j + 2);
+                        __builtin_amdgcn_sched_barrier(0);
+                        sums(tn);
                     }
-            };
-            f32x4_t ta[VPT][8];
-            if constexpr (VPT == 1) {
-                f32x4_t tn[VPT][8];
-                lookups(ta, 0);
+                } else {
 #pragma unroll
-                for (int j = 0; j < 4; j += 2) {
-                    lookups(tn, j + 1);
-                    __builtin_amdgcn_sched_barrier(0);
-                    sums(ta);
-                    if (j + 2 < 4) lookups(ta, j + 2);
-                    __builtin_amdgcn_sched_barrier(0);
-                    sums(tn);
+                    for (int j = 0; j < 4; ++j) {
+                        lookups(ta, j);
+                        __builtin_amdgcn_sched_barrier(0);
+                        sums(ta);
+                    }
                 }
             } else {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    lookups(ta, j);
-                    __builtin_amdgcn_sched_barrier(0);
-                    sums(ta);
-                }
-            }
-        } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+                    for (int n = 0; n < 8; ++n) {
+                        const int pr = p0 + ch * 32 + j * 8 + n;     // dimensions 2 pr, 2 pr + 1
 #pragma unroll
-                for (int n = 0; n < 8; ++n) {
-                    const int pr = p0 + ch * 32 + j * 8 + n;     // dimensions 2 pr, 2 pr + 1
+                        for (int k = 0; k < VPT; ++k) {
+                            const int c4 = (int)((cur[k][j] >> (4 * n)) & 15u);
+                            const int c0 = c4 & 3, c1 = c4 >> 2;
 #pragma unroll
-                    for (int k = 0; k < VPT; ++k) {
-                        const int c4 = (int)((cur[k][j] >> (4 * n)) & 15u);
-                        const int c0 = c4 & 3, c1 = c4 >> 2;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            if (q0 + q < Q)
-                                acc[k][q] += lut[((size_t)(q0 + q) * D + 2 * pr) * 4 + c0] +
-                                             lut[((size_t)(q0 + q) * D + 2 * pr + 1) * 4 + c1];
+                            for (int q = 0; q < 4; ++q)
+                                if (q0 + q < Q)
+                                    acc[k][q] += lut[((size_t)(q0 + q) * D + 2 * pr) * 4 + c0] +
+                                                 lut[((size_t)(q0 + q) * D + 2 * pr + 1) * 4 + c1];
+                        }
                     }
                 }
             }
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) cur[k] = nxt[k];
         }
+        // Partial sums of a vector's TPV adjacent lanes meet by shuffles.
 #pragma unroll
-        for (int k = 0; k < VPT; ++k) cur[k] = nxt[k];
-    }
-    // Partial sums of a vector's TPV adjacent lanes meet by shuffles.
+        for (int k = 0; k < VPT; ++k)
 #pragma unroll
-    for (int k = 0; k < VPT; ++k)
+            for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+                for (int m = 1; m < TPV; m <<= 1) acc[k][q] += __shfl_xor(acc[k][q], m);
+        if (part == 0) {
 #pragma unroll
-            for (int m = 1; m < TPV; m <<= 1) acc[k][q] += __shfl_xor(acc[k][q], m);
-    if (part != 0) return;
+            for (int k = 0; k < VPT; ++k) {
+                if (!ok[k]) continue;
+                float *out = scores + (size_t)vk[k] * Q + q0;
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-        if (!ok[k]) continue;
-        float *out = scores + (size_t)vk[k] * Q + q0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            if (q0 + q < Q) out[q] = acc[k][q];
+                for (int q = 0; q < 4; ++q)
+                    if (q0 + q < Q) out[q] = acc[k][q];
+        }
+        }
     }
 }
 
@@ -219,6 +227,7 @@ __global__ __launch_bounds__(W * 64) void scan2_kernel(const uint32_t *__restric
 struct ScanCfg { int lds, vpt, tpg, tpv; };
 constexpr ScanCfg kScanDefault = {1, 1, 1024, 0};
 constexpr int kCUs = 256;
+constexpr int kMaxDLds = 4096;         // the largest D (the table in memory)
 ScanCfg g_scan = kScanDefault;
 
 bool scan_cfg_ok(int lds, int vpt, int tpg, int tpv) {
@@ -237,15 +246,36 @@ int auto_tpv(int V, int Q, int vpt) {
 // padding.
 size_t lut_lds_bytes(int D) { return ((size_t)D / 2 * 16 + 16) * 16; }
 
+// Workgroups of one kernel that fit a CU at once with `lds` bytes of LDS
+// each, from the occupancy calculator, cached per LDS size (D / 64 - 1).
+template <int VPT, int TPV, int W, bool LDS>
+int resident_per_cu(int D, size_t lds) {
+    static int cache[kMaxDLds / 64];
+    int &c = cache[(LDS ? D : 64) / 64 - 1];
+    if (c == 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, scan2_kernel<VPT, TPV, W, LDS>, W * 64, lds) !=
+                hipSuccess || n < 1)
+            n = 1;
+        c = n;
+    }
+    return c;
+}
+
 template <int VPT, int TPV, int W, bool LDS>
 void launch_s(const uint32_t *codes, const float *lut, float *scores, int V, int D, int Q,
               hipStream_t st) {
     const int per = VPT * W * 64 / TPV;
-    const int nvb = (V + per - 1) / per;
-    const int grid = Q > 4 ? (2 * nvb + 15) / 16 * 16 : nvb;   // see the kernel's workgroup order
+    const int64_t nvb = ((int64_t)V + per - 1) / per;
     const size_t lds = LDS ? lut_lds_bytes(D) : 0;
-    hipLaunchKernelGGL((scan2_kernel<VPT, TPV, W, LDS>), dim3(grid), dim3(W * 64), lds, st, codes, lut,
-                       scores, V, D, Q);
+    // As many workgroups as fit the chip at once (each builds the table
+    // once and loops over vector blocks), never more than there are blocks;
+    // with two query groups a multiple of 16 (see the kernel's workgroup order).
+    const int64_t cap = (int64_t)resident_per_cu<VPT, TPV, W, LDS>(D, lds) * kCUs;
+    const int64_t grid = Q > 4 ? std::min((2 * nvb + 15) / 16, std::max<int64_t>(cap / 16, 1)) * 16
+                               : std::min(nvb, cap);
+    hipLaunchKernelGGL((scan2_kernel<VPT, TPV, W, LDS>), dim3((unsigned)grid), dim3(W * 64), lds, st,
+                       codes, lut, scores, V, D, Q);
 }
 
 template <int VPT, int TPV, bool LDS>

@@ -89,6 +89,22 @@ def test_integer_table_is_exact():
     assert np.array_equal(run(codes, lut).astype(np.float64), ref)
 
 
+@pytest.mark.parametrize("V,D,Q,cfg", [(40000, 768, 8, (1, 1, 64, 1)), (40000, 768, 3, (1, 1, 64, 1)),
+                                       (150001, 128, 8, (1, 2, 256, 1)), (70000, 320, 5, (0, 1, 256, 1))])
+def test_workgroups_loop_over_vector_blocks(V, D, Q, cfg):
+    """More vector blocks than workgroups that fit the chip at once: each
+    workgroup builds its table once and scans several blocks."""
+    codes = wl.make_scan_codes(67, V, D)
+    lut = wl.make_scan_lut(67, Q, D)
+    rows = np.unique(np.r_[0:300, V - 300:V, np.random.default_rng(68).choice(V, 2000, replace=False)])
+    ref, b = scan.scan(codes, lut, rows)
+    try:
+        q4.scan2_set_config(*cfg)
+        assert_within(run(codes, lut)[rows], ref, b, f"V={V} D={D} Q={Q} cfg={cfg}")
+    finally:
+        q4.scan2_set_config(0, 0, 0, 0)
+
+
 def test_page_workload_sampled():
     V, Q, D = wl.SCAN_VECTORS, wl.SCAN_QUERIES, wl.SCAN_DIM
     codes = wl.make_scan_codes(65, V, D)
