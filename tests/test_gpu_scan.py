@@ -34,8 +34,8 @@ def assert_within(s, ref, bound, label):
                            f"{np.nanmax(err / tol):.3g}")
 
 
-@pytest.mark.parametrize("V,D,Q", [(1, 64, 1), (257, 128, 3), (1000, 768, 8), (333, 1024, 5),
-                                   (64, 192, 4), (4097, 256, 8)])
+@pytest.mark.parametrize("V,D,Q", [(1, 64, 1), (1, 64, 8), (3, 128, 6), (257, 128, 3), (1000, 768, 8),
+                                   (333, 1024, 5), (64, 192, 4), (4097, 256, 8)])
 def test_scan_small(V, D, Q):
     codes = wl.make_scan_codes(61, V, D)
     lut = wl.make_scan_lut(61, Q, D)
