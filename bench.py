@@ -22,8 +22,10 @@ Also in the default line ("block_formats" and "scan2", skipped with
 of the cera page at the same 4096 x 14336 stream shape and at the page's four
 decode shapes, each cycling >= 1 GiB of distinct matrices; and the 2-bit
 corpus scan of the Refractometer page, 65,536 vectors x 8 queries, D = 768,
-cycling 64 distinct corpora; and one decoder layer (hidden 896, FFN 4864) as
-seven GEMVs and as four launches, cycling 64 distinct layers.  Then
+cycling 64 distinct corpora; one decoder layer (hidden 896, FFN 4864) as
+seven GEMVs and as four launches, cycling 64 distinct layers; and the FFN
+pair 4096 -> 14336 -> 4096 at 1, 2, 4 and 8 activation rows against both the
+HBM and the VALU roof ("ffn_rows").  Then
 ("bandwidth_sweep", skipped with --no-sweep) the Refractometer page's
 bandwidth sweep: vec4 read-reduce and vec4 copy over buffers from 16 KiB to
 2 GiB, the best of three workgroup counts per size, cliffs marked by the
@@ -31,7 +33,7 @@ page's 80% rule, and from them the cache class of the stream's working set;
 and the fixed cost of one launch in a graph ("launch_gap_us").
 
 Other modes:
-  --blocks-only     only the block-format, scan, layer and sweep cells
+  --blocks-only     only the block-format, scan, layer, ffn and sweep cells
                     (--block-shapes to pick)
   --pmc-workload    a short fixed sequence of dispatches for rocprofv3 --pmc
   --summarize DIR   turn rocprofv3 CSV output in DIR into a profiles/ summary
@@ -438,6 +440,7 @@ def run_default(args):
         line["block_formats"] = run_block_formats(torch, q4, dev)
         line["scan2"] = run_scan(torch, q4, dev)
         line["decoder_layer"] = run_decoder_layer(torch, q4, dev)
+        line["ffn_rows"] = run_ffn_rows(torch, q4, W)
     if not args.no_sweep:
         sw = run_bandwidth_sweep(torch, q4, dev, W["probe"])
         ws = wl.STREAM_MATRICES * bytes_per_call["gemv_q4"]
@@ -590,6 +593,71 @@ def run_scan(torch, q4, dev, reps_target_s: float = 0.02) -> dict:
     del corpora, outs, G
     torch.cuda.empty_cache()
     return res
+
+
+# ---------------------------------------------------------------- several activation rows
+
+FP32_VECTOR_PEAK = 157.3e12     # MI355X fp32 vector FLOP/s, AMD published
+
+
+def run_ffn_rows(torch, q4, W, reps_target_s: float = 0.02) -> dict:
+    """The 8B-class FFN pair, 4096 -> 14336 and 14336 -> 4096 at g128, for 1,
+    2, 4 and 8 activation rows, cycling the 32 stream matrices (each viewed
+    in the shape: the same bytes, 976 MB).  Each cell is gated against
+    gemv_f32 on the dequantised matrix 0, then timed by two-point graph
+    replays (median of three), per launch, and set against both roofs: HBM
+    (weight bytes per call against 8 TB/s) and VALU (2 M N K FLOP per call
+    against the fp32 vector peak)."""
+    g = wl.STREAM_SHAPE.g
+    dev = W["x"].device
+    seed = wl.config_seed(3)
+    out = {}
+    for label, N, K in (("up 4096->14336", 14336, 4096), ("down 14336->4096", 4096, 14336)):
+        G = K // g
+        mats = [{"wq": m["wq"].view(N, K // 2), "scales": m["scales"].view(N, G),
+                 "zeros": m["zeros"].view(N, (G + 1) // 2)} for m in W["mats"]]
+        m0 = mats[0]
+        w0 = q4.dequant_q4(m0["wq"], m0["scales"], m0["zeros"], g, want_codes=False)[0]
+        nbytes = wl.q4_weight_bytes(N, K, g)
+        cells = []
+        for M in (1, 2, 4, 8):
+            x = torch.from_numpy(wl.make_x(seed, M, K)).to(dev)
+            ys = [torch.empty((M, N), dtype=torch.float32, device=dev) for _ in mats]
+            y = q4.gemv_q4(x, m0["wq"], m0["scales"], m0["zeros"], g)
+            err = (y.double() - q4.gemv_f32(x, w0).double()).abs()
+            tol = 2 * (1e-4 * q4.gemv_f32(x.abs(), w0.abs()).double() + 1e-6)
+            if not bool((err <= tol).all()):
+                raise SystemExit(f"ffn parity gate failed: {label} M={M}: worst err/tol "
+                                 f"{float((err / tol).max()):.3g}")
+
+            def one_pass():
+                for m, yy in zip(mats, ys):
+                    q4.gemv_q4(x, m["wq"], m["scales"], m["zeros"], g, out=yy)
+
+            Gr = Graph(one_pass, torch)
+            Gr.time(2)
+            t1 = Gr.time(1)
+            reps = max(1, int(reps_target_s / max(t1, 1e-6)))
+            per = []
+            for _ in range(3):
+                a, b = Gr.time(reps), Gr.time(2 * reps)
+                per.append((b - a) / (reps * len(mats)))
+            t = statistics.median(per)
+            flops = 2 * M * N * K
+            path = "integer" if q4.gemv_q4_path(M, N, K, g) == q4.Q4_PATH_INTEGER else "multiply-add"
+            cells.append({"M": M, "path": path, "us_per_launch": round(t * 1e6, 3),
+                          "GBps": round(nbytes / t / 1e9, 1),
+                          "hbm_frac": round(nbytes / t / 1e9 / SPEC_PEAK_GBS, 4),
+                          "TFLOPs": round(flops / t / 1e12, 2),
+                          "valu_frac_of_fp32_peak": round(flops / t / FP32_VECTOR_PEAK, 4)})
+            log(f"ffn {label} M={M} ({path}): {t * 1e6:7.3f} us/launch, {nbytes / t / 1e9:7.1f} GB/s, "
+                f"{flops / t / 1e12:6.2f} TFLOP/s")
+            del Gr, ys
+        out[label] = {"N": N, "K": K, "group_size": g, "bytes_per_call": nbytes,
+                      "matrices": len(mats), "cells": cells}
+        del w0
+        torch.cuda.empty_cache()
+    return out
 
 
 # ---------------------------------------------------------------- bandwidth sweep
@@ -773,12 +841,15 @@ def run_blocks_only(args):
     only = set(args.block_shapes.split(",")) if args.block_shapes else None
     dev = torch.device("cuda:0")
     out = {"unit": "GB/s", "peak": SPEC_PEAK_GBS}
-    if not only or only - {"scan", "layer", "sweep"}:
+    if not only or only - {"scan", "layer", "sweep", "ffn"}:
         out["block_formats"] = run_block_formats(torch, q4, dev, only=only)
     if not only or "scan" in only:
         out["scan2"] = run_scan(torch, q4, dev)
     if not only or "layer" in only:
         out["decoder_layer"] = run_decoder_layer(torch, q4, dev)
+    if not only or "ffn" in only:
+        out["ffn_rows"] = run_ffn_rows(torch, q4, setup_stream(torch, q4, dev))
+        torch.cuda.empty_cache()
     if not only or "sweep" in only:
         src = torch.rand(wl.PROBE_BYTES // 4, device=dev)
         out["bandwidth_sweep"] = run_bandwidth_sweep(torch, q4, dev, src)
@@ -993,7 +1064,7 @@ def main(argv=None):
     ap.add_argument("--no-sweep", action="store_true", help="skip the 16 KiB - 2 GiB bandwidth sweep")
     ap.add_argument("--blocks-only", action="store_true", help="only the block-format cells")
     ap.add_argument("--block-shapes", default="",
-                    help="with --blocks-only: comma list of shape labels (stream, 'lm head', ..., scan, layer, sweep)")
+                    help="with --blocks-only: comma list of shape labels (stream, 'lm head', ..., scan, layer, ffn, sweep)")
     ap.add_argument("--pmc-workload", action="store_true")
     ap.add_argument("--summarize", metavar="DIR", help="rocprofv3 CSV dir (stats, or FETCH_SIZE pmc)")
     ap.add_argument("--summarize-write", metavar="DIR", help="WRITE_SIZE pmc dir (with --summarize)")
