@@ -273,7 +273,7 @@ def host_cpu() -> str:
     return "unknown"
 
 
-PROBE_GRIDS = (512, 768, 1024, 1280, 1536)
+PROBE_GRIDS = (256, 384, 512, 768, 1024, 1280, 1536)
 
 
 def pick_probe_grid(torch, q4, W) -> int:
@@ -713,7 +713,7 @@ def run_bandwidth_sweep(torch, q4, dev, src, samples: int = 25, sample_s: float 
                 if kind == "copy":
                     fn = lambda: q4.copy_vec4(src[:n], dst[:n], passes=passes, n_blocks=grid)
                 else:
-                    fn = lambda: q4.read_reduce(src[:n], grid, partials=partials, passes=passes)
+                    fn = lambda: q4.read_reduce_passes(src[:n], grid, passes, partials=partials)
                 fn()
                 torch.cuda.synchronize()
                 a = torch.cuda.Event(enable_timing=True)
@@ -861,6 +861,7 @@ def run_blocks_only(args):
 # ---------------------------------------------------------------- --pmc-workload
 
 PMC_BLOCK_MATRICES = 8
+PMC_READ_KERNEL = "read_reduce_kernel<true>"   # read_reduce's (non-temporal) kernel
 
 
 def run_pmc_workload(args):
@@ -927,7 +928,7 @@ def _rows(pattern):
 
 def _kernel_short(name: str) -> str:
 
-    m = re.search(r"(gemv_q4(?:_int)?_kernel<[^>]*>|gemv_f32_kernel<[^>]*>|read_reduce_kernel|"
+    m = re.search(r"(gemv_q4(?:_int)?_kernel<[^>]*>|gemv_f32_kernel<[^>]*>|read_reduce_kernel(?:<[^>]*>)?|"
                   r"write_fill_kernel|copy_kernel|dequant_q4_kernel|gemv_blk_kernel<[^>]*>|"
                   r"dequant_blk_kernel<[^>]*>|scan2_kernel<[^>]*>|at::native::\w+|__amd_rocclr_\w+)", name)
     return m.group(1).replace("(anonymous namespace)::", "") if m else name.split("(")[0][:60]
@@ -986,7 +987,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, name: str, command: str) -> st
             if r["Counter_Name"] == ctr:
                 per.setdefault((_kernel_short(r["Kernel_Name"]), ctr), []).append(float(r["Counter_Value"]))
     mean = {k: statistics.mean(v) for k, v in per.items()}
-    fetch_factor = wl.PROBE_BYTES / (mean[("read_reduce_kernel", "FETCH_SIZE")] * 1024)
+    fetch_factor = wl.PROBE_BYTES / (mean[(PMC_READ_KERNEL, "FETCH_SIZE")] * 1024)
     write_factor = wl.PROBE_BYTES / (mean[("write_fill_kernel", "WRITE_SIZE")] * 1024)
     qk = next(k for k, _ in mean if k.startswith("gemv_q4_"))
     s = wl.STREAM_SHAPE
@@ -1005,7 +1006,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, name: str, command: str) -> st
     json.dump(summary, open(PMC_SUMMARY, "w"), indent=1)
     lines = [f"# {name}: HBM traffic from rocprofv3 counters", "", f"command: `{command}`", "",
              f"Calibration: read_reduce over {wl.PROBE_BYTES} B reads FETCH_SIZE "
-             f"{mean[('read_reduce_kernel', 'FETCH_SIZE')]:.1f} KiB -> factor {fetch_factor:.4f}; "
+             f"{mean[(PMC_READ_KERNEL, 'FETCH_SIZE')]:.1f} KiB -> factor {fetch_factor:.4f}; "
              f"write_fill over {wl.PROBE_BYTES} B reads WRITE_SIZE "
              f"{mean[('write_fill_kernel', 'WRITE_SIZE')]:.1f} KiB -> factor {write_factor:.4f}.", "",
              "| kernel | counter | dispatches | mean KiB/dispatch | scaled bytes/dispatch |",

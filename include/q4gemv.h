@@ -124,8 +124,8 @@ int dequant_q4(const uint8_t *wq, const uint16_t *scales, const uint8_t *zeros,
 
 /* Read-bandwidth probe (webgpu-bench 0.1.0 README, read-bandwidth; Refractometer
  * "What each sweep measures", bandwidth: vec4 read-reduce).  Streams buf with
- * 16-byte loads folded by addition only and writes one partial sum per
- * workgroup: exactly n_partials workgroups are launched and
+ * 16-byte non-temporal loads folded by addition only and writes one partial
+ * sum per workgroup: exactly n_partials workgroups are launched and
  * partials[0 .. n_partials) are all written.  The caller adds the partials.
  *   buf 16-byte aligned, n_floats % 4 == 0 (n_floats == 0 writes zeros);
  *   1 <= n_partials <= 65536; partials 4-byte aligned. */
@@ -135,8 +135,9 @@ int read_reduce(const float *buf, size_t n_floats, float *partials, int n_partia
 /* read_reduce walking buf `passes` times in one launch (1 <= passes <= 4096);
  * each partial is the sum over all passes.  A buffer that fits a cache is
  * then re-read from it, which the bandwidth sweep uses to find the caches'
- * knees.  read_reduce is this call with passes = 1.  Other arguments and
- * errors as read_reduce. */
+ * knees: unlike read_reduce, whose loads are marked non-temporal (the data
+ * is read once), these loads are plain.  Other arguments and errors as
+ * read_reduce. */
 int read_reduce_passes(const float *buf, size_t n_floats, int passes, float *partials,
                        int n_partials, void *stream);
 

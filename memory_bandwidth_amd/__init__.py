@@ -214,24 +214,32 @@ def dequant_q4(wq: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, grou
     return w, c
 
 
-def read_reduce(buf: torch.Tensor, n_partials: int, partials: torch.Tensor | None = None,
-                passes: int = 1) -> torch.Tensor:
-    """Launches the read probe (walking buf `passes` times); returns the
-    per-workgroup partial sums (add them for the total)."""
+def _partials(buf: torch.Tensor, n_partials: int, partials: torch.Tensor | None) -> torch.Tensor:
     _need(buf, "buf", (torch.float32,))
-    dev = buf.device
     if partials is None:
-        partials = torch.empty(n_partials, dtype=torch.float32, device=dev)
-    else:
-        _need(partials, "partials", (torch.float32,), dev)
-        if partials.numel() < n_partials:
-            raise ValueError("partials too small")
-    if passes == 1:
-        _check("read_reduce", lib().read_reduce(_ptr(buf), buf.numel(), _ptr(partials), n_partials,
-                                                _stream(dev)))
-    else:
-        _check("read_reduce_passes", lib().read_reduce_passes(
-            _ptr(buf), buf.numel(), passes, _ptr(partials), n_partials, _stream(dev)))
+        return torch.empty(n_partials, dtype=torch.float32, device=buf.device)
+    _need(partials, "partials", (torch.float32,), buf.device)
+    if partials.numel() < n_partials:
+        raise ValueError("partials too small")
+    return partials
+
+
+def read_reduce(buf: torch.Tensor, n_partials: int, partials: torch.Tensor | None = None) -> torch.Tensor:
+    """Launches the streaming read probe (non-temporal loads); returns the
+    per-workgroup partial sums (add them for the total)."""
+    partials = _partials(buf, n_partials, partials)
+    _check("read_reduce", lib().read_reduce(_ptr(buf), buf.numel(), _ptr(partials), n_partials,
+                                            _stream(buf.device)))
+    return partials
+
+
+def read_reduce_passes(buf: torch.Tensor, n_partials: int, passes: int,
+                       partials: torch.Tensor | None = None) -> torch.Tensor:
+    """The read probe walking buf `passes` times with plain loads (so that a
+    buffer that fits a cache is re-read from it); per-workgroup partial sums."""
+    partials = _partials(buf, n_partials, partials)
+    _check("read_reduce_passes", lib().read_reduce_passes(
+        _ptr(buf), buf.numel(), passes, _ptr(partials), n_partials, _stream(buf.device)))
     return partials
 
 

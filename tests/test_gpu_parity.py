@@ -402,7 +402,7 @@ def test_read_reduce_random():
 @pytest.mark.parametrize("n,parts,passes", [(0, 3, 2), (4, 1, 3), (1 << 20, 7, 5), ((1 << 22) + 36, 2048, 16)])
 def test_read_reduce_passes_ones(n, parts, passes):
     buf = torch.ones(n, device=DEV)
-    p = q4.read_reduce(buf, parts, passes=passes)
+    p = q4.read_reduce_passes(buf, parts, passes)
     torch.cuda.synchronize()
     assert float(p.double().sum()) == float(n * passes)
 
