@@ -229,10 +229,10 @@ def _oracle_rate(budget_s: float, threads: int):
     seed = wl.config_seed(4)
     x = wl.make_x(seed, 1, s.K)
     parts = np.array_split(np.arange(s.N, dtype=np.int64), threads)
-    nbytes, done, t_used = 0, 0, 0.0
+    done, t_used, times = 0, 0.0, []
     mats = []                  # generated once; past the 32nd call the stream cycles
     with concurrent.futures.ThreadPoolExecutor(threads) as ex:
-        while t_used < budget_s or done == 0:
+        while t_used < budget_s or done < 3:
             i = done % wl.STREAM_MATRICES
             if i == len(mats):
                 mats.append(wl.make_q4_weights(seed, s.N, s.K, s.g, s.s_lo, s.s_hi, index=i))
@@ -243,10 +243,11 @@ def _oracle_rate(budget_s: float, threads: int):
             else:
                 list(ex.map(lambda r: oracle.gemv_q4(x, d["wq"], d["scales"], d["zeros"], s.g, rows=r),
                             parts))
-            t_used += time.perf_counter() - t0
-            nbytes += wl.q4_weight_bytes(s.N, s.K, s.g)
+            times.append(time.perf_counter() - t0)
+            t_used += times[-1]
             done += 1
-    return nbytes / t_used / 1e9, done, t_used
+    # the median GEMV (at least three), as the GPU figures are medians
+    return wl.q4_weight_bytes(s.N, s.K, s.g) / statistics.median(times) / 1e9, done, t_used
 
 
 def cpu_baseline(budget_s: float = 12.0) -> dict:
@@ -256,10 +257,10 @@ def cpu_baseline(budget_s: float = 12.0) -> dict:
     v1, n1, t1 = _oracle_rate(budget_s / 2, 1)
     vn, nn, tn = _oracle_rate(budget_s / 2, threads) if threads > 1 else (v1, n1, t1)
     return {"value": round(vn, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{nn} GEMVs over the 32 stream matrices (cycled), full 14336x4096 each, "
-                      f"f64 C oracle, rows split over {threads} threads, {tn:.1f} s",
+            "sample": f"median of {nn} GEMVs over the 32 stream matrices (cycled), full "
+                      f"14336x4096 each, f64 C oracle, rows split over {threads} threads, {tn:.1f} s",
             "single_core": {"value": round(v1, 5), "cores": 1,
-                            "sample": f"{n1} stream-matrix GEMVs on one thread, {t1:.1f} s"},
+                            "sample": f"median of {n1} stream-matrix GEMVs on one thread, {t1:.1f} s"},
             "host_cpu": host_cpu(), "host_nproc": os.cpu_count()}
 
 
