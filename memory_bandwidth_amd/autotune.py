@@ -393,7 +393,7 @@ def block_winners(prof: dict) -> dict:
         cfgs = {tuple(e["best"]["config"]) for e in es}
         if len(cfgs) != 1 or cfgs == {(0, 0, 0)}:
             continue
-        if all(e["best"]["default_us"] >= APPLY_GAIN * e["best"]["median_us"] for e in es):
+        if all(_beats_default(e["best"]) for e in es):
             out[fmt] = cfgs.pop()
     return out
 
@@ -402,9 +402,16 @@ def scan_winner(prof: dict):
     """The scan setting apply_profile applies, or None."""
     for e in prof.get("scan_entries", []):
         b = e["best"]
-        if b["config"] != [0, 0, 0, 0] and b["default_us"] >= APPLY_GAIN * b["median_us"]:
+        if b["config"] != [0, 0, 0, 0] and _beats_default(b):
             return tuple(b["config"])
     return None
+
+
+def _beats_default(best: dict) -> bool:
+    """The winner is APPLY_GAIN faster than the default (or the default
+    failed its parity check and has no time)."""
+    d = best.get("default_us")
+    return d is None or d >= APPLY_GAIN * best["median_us"]
 
 
 def apply_profile(path: str | None = None, dev: torch.device | None = None) -> int:

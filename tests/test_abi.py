@@ -318,6 +318,8 @@ def test_profile_winner_rules():
     assert autotune.scan_winner(prof) == (1, 1, 256, 2)
     prof["scan_entries"][0]["best"]["default_us"] = 10.2
     assert autotune.scan_winner(prof) is None
+    prof["scan_entries"][0]["best"]["default_us"] = None      # the default failed parity
+    assert autotune.scan_winner(prof) == (1, 1, 256, 2)
 
 
 def test_block_and_scan_validation(L):
