@@ -46,7 +46,7 @@ def code(fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("N,K", [(1, 256), (3, 512), (7, 2816), (33, 1024), (5, 4352)])
+@pytest.mark.parametrize("N,K", [(1, 256), (3, 512), (7, 2816), (33, 1024), (5, 4352), (2, 32768)])
 def test_dequant_bit_exact(fmt, N, K):
     w = wl.make_block_weights(41, fmt, N, K)
     got = q4.dequant_block(fmt, to_dev(w), K).cpu().numpy()

@@ -147,6 +147,7 @@ RAGGED = [
     (8, 67, 2080, 32), (1, 127, 4096, 128), (6, 129, 4224, 128), (1, 1000, 896, 32),
     (7, 257, 4864, 32), (8, 67, 14336, 128), (1, 45, 14336, 128), (2, 300, 8192, 128),
     (1, 1, 16384, 128), (8, 9, 18432, 128), (1, 4097, 384, 128), (8, 1, 32, 32),
+    (8, 100, 32768, 128), (3, 70, 32768, 32), (1, 33, 32768, 128),
 ]
 
 
@@ -450,6 +451,23 @@ def test_gemv_q4_swiglu(M, N, K, g):
         y = y[:, rows]
     bad = np.abs(y - y_ref) > tol
     assert not bad.any(), f"{int(bad.sum())}/{bad.size} outputs out of tolerance"
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 4864, 896), (1, 300, 4096), (4, 129, 4096)])
+def test_gemv_q4_swiglu_nan_in_x_poisons_its_row(M, N, K):
+    g = 32 if K % 128 else 128
+    s = wl.Q4Shape(M, N, K, g, 0.002, 0.02)
+    dg = wl.make_q4_problem(310 + N, s, index=0)
+    du = wl.make_q4_problem(310 + N, s, index=1)
+    x = dg["x"].copy()
+    x[M - 1, K // 3] = np.nan
+    tg, tu = dev(dict(dg, x=x)), dev(du)
+    y = q4.gemv_q4_swiglu(tg["x"], (tg["wq"], tg["scales"], tg["zeros"]),
+                          (tu["wq"], tu["scales"], tu["zeros"]), g)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    assert np.isnan(y[M - 1]).all()
+    assert np.isfinite(y[:M - 1]).all()
 
 
 def test_gemv_q4_swiglu_zero_gate_is_exactly_zero():
