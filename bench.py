@@ -1077,7 +1077,7 @@ def main(argv=None):
         return summarize_profile(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the int4 GEMV shards by output rows; this build measures one GPU)", file=sys.stderr)
+              "(the int4 GEMV shards by output rows; the benchmark measures one GPU)", file=sys.stderr)
         return 2
     if args.steps < 1 or args.warmup < 0 or args.runs < 1:
         print("--steps must be >= 1, --warmup >= 0, --runs >= 1", file=sys.stderr)
