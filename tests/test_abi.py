@@ -361,3 +361,22 @@ def test_block_and_scan_validation(L):
     t = ctypes.c_int()
     assert L.scan2_config(ctypes.byref(r), ctypes.byref(w), ctypes.byref(g), ctypes.byref(t)) == q4.Q4_OK
     assert (r.value, w.value, g.value, t.value) == (1, 1, 1024, 0)
+
+
+def test_tuner_candidates_are_what_the_library_accepts():
+    """Host-only: the block-format candidates are exactly the settings the
+    library accepts (R = 4 only where it compiles without spilling), plus the
+    default; the scan's are the LDS-table grid plus the page's tail with the
+    table in memory and the default."""
+    from memory_bandwidth_amd import autotune
+    for fmt in q4.BLOCK_FORMATS:
+        cands = autotune.block_candidates(fmt)
+        assert cands[0] == (0, 0, 0) and len(set(cands)) == len(cands)
+        r4 = fmt not in ("q5_k", "q6_k")
+        assert len(cands) == 1 + (3 if r4 else 2) * 2 * 4
+    cs = autotune.scan_candidates()
+    assert len(cs) == 26 and cs[0] == (0, 0, 0, 0) and (0, 1, 256, 1) in cs
+    for c in cs[1:]:
+        q4.scan2_set_config(*c)
+    q4.scan2_set_config(0, 0, 0, 0)
+    assert q4.scan2_config() == (1, 1, 1024, 0)
