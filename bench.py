@@ -406,7 +406,9 @@ def run_default(args):
 
     traffic = traffic_from_profile(bytes_per_call["gemv_q4"])
     integer = q4.gemv_q4_path(1, s.N, s.K, s.g) == q4.Q4_PATH_INTEGER
-    arith = ("x per 32 values in 23-bit block fixed point, exact int32 chunk sums, fp32 accumulate"
+    arith = ("x per 32 values as integers below 2^22 plus exact fp32 residuals for values far below "
+             "the chunk's largest: exact int32 chunk sums, fp32 residual products, fp32 accumulate; "
+             "every product within 2^-14 of itself"
              if integer else "(q-z) in fp16, fp32 x, fp32 multiply-add and accumulate")
     line = {
         "metric": METRIC,

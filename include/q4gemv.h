@@ -62,20 +62,19 @@ enum q4_status {
  *     32-code chunk;
  *   - integer (M == 1: 512 < K <= 18688; 2 to 4 rows: K > 1024 while their
  *     x fits one LDS segment; 5 to 8 rows: K > 1024): every chunk of 32 values
- *     of an x row (x[m][32c .. 32c+31]) is rounded to integers X = round(x * 2^(22-e)),
- *     where 2^(e-1) <= max|x| over the chunk < 2^e, so |X| < 2^22; the sum
- *     of (q - z) * X is formed exactly in int32, converted to fp32 once per
- *     chunk and scaled by 2^(e-22) and the group scale.  q == z gives
- *     exactly 0; a chunk of x row m holding Inf or NaN makes every output
- *     of row m NaN.
- * Accuracy against the exact sum y_ref, with w = (q - z) * s:
- *   - fused multiply-add path: |y - y_ref| <= 1e-4 * sum_k |x_k w_k| + 1e-6;
- *   - integer path: the same bound plus the rounding of x, at most
- *     2^-22 * max|x over the chunk| * |w_k| for each k.  It stays inside
- *     the first bound whenever no nonzero w_k meets an x_k more than 400
- *     times smaller than its chunk's largest |x| (x ~ N(0, 1) keeps a margin
- *     of about 100); a chunk whose large values all meet w = 0 while small
- *     ones meet w != 0 can exceed it.
+ *     of an x row (x[m][32c .. 32c+31]) is written as X + r with
+ *     X = round(x * 2^sh) an integer, |X| < 2^22 (2^(22-sh-1) <= max|x| over
+ *     the chunk < 2^(22-sh)), and r the exact residual; the sum of (q - z) * X
+ *     is formed exactly in int32, and for every element whose |r| exceeds
+ *     2^-14 of |x * 2^sh| (values far below the chunk's largest) (q - z) * r
+ *     is added in fp32, so each product is carried to within 2^-14 of itself;
+ *     then one conversion per chunk, a multiply by 2^-sh and the group scale.
+ *     q == z gives exactly 0; a chunk of x row m holding Inf or NaN makes
+ *     every output of row m NaN.
+ * Accuracy, on either path, for every finite x whose products and sums stay
+ * inside the fp32 range: each output y[m, n] satisfies
+ *     |y - y_ref| <= 1e-4 * sum_k |x[m, k] w[n, k]| + 1e-6,
+ * with y_ref the exact sum and w = (q - z) * s the dequantised weight.
  *   1 <= M <= 8;  N >= 0 (N == 0 launches nothing);  group_size in {32, 128};
  *   K >= group_size and K % group_size == 0.
  *   x and wq 16-byte aligned; scales 2-byte aligned; y 4-byte aligned.

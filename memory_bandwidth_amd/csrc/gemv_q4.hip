@@ -376,28 +376,47 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     }
 }
 
-// ---------------------------------------------------------------- M = 1: exact integer dot products
+// ---------------------------------------------------------------- the integer path
 //
-// With one activation row the (q - z) * x products are formed exactly in
-// integer arithmetic, eight per instruction.  Each chunk of 32 x values is
-// written in block fixed point: with e the binary exponent of the chunk's
-// largest |x| (|x| < 2^e), X = round(x * 2^(22-e)) is an integer with
-// |X| <= 2^22 and x = X * 2^(e-22) to within half a unit of X, i.e. to
-// within 2^-23 of the chunk's largest |x|.  X is held as six signed 4-bit
-// digits, X = sum_l d_l 16^l with d_l in [-8, 7] (the nibbles of
-// (X + 0x888888) ^ 0x888888), and the digits of 8 consecutive x values are
-// transposed into one 32-bit word per digit, so that v_dot8_i32_i4 of such
-// a word against a word of 8 codes, each read as q - 8 in [-8, 7] by one XOR
-// with 0x88888888, sums the 8 products of one digit.  Then
+// The (q - z) * x products are formed in integer arithmetic, eight per
+// instruction, on x written in block fixed point.  With e the binary exponent
+// of a 32-value chunk's largest |x| (|x| < 2^e) and sh = 22 - e, each element
+// becomes X = round(x * 2^sh), |X| < 2^22, and an exact residual
+// r = x * 2^sh - X, |r| <= 1/2, so that x = (X + r) * 2^-sh exactly.
+// X is held as six signed 4-bit digits, X = sum_l d_l 16^l with d_l in
+// [-8, 7] (the nibbles of (X + 0x888888) ^ 0x888888), and the digits of 8
+// consecutive x values are transposed into one 32-bit word per digit, so that
+// v_dot8_i32_i4 of such a word against a word of 8 codes, each read as q - 8
+// in [-8, 7] by one XOR with 0x88888888, sums the 8 products of one digit.
+// Then
 //     sum_k (q_k - z) X_k = sum_l 16^l sum_k (q_k - 8) d_l[k] + (8 - z) sum_k X_k
 // holds exactly in int32 (|sum| <= 32 * 15 * 2^22 < 2^31), so q == z still
-// gives exactly 0.  One conversion to fp32 per chunk, scaled by 2^(e-22) and
-// the group scale, accumulates into the row's fp32 sum.
+// gives exactly 0.
+//
+// X alone carries x to within |r| <= 1/2 unit, which is a small fraction of
+// |x * 2^sh| only for the chunk's larger values.  An element whose residual
+// exceeds 2^-14 of |x * 2^sh| is flagged, and (q - z) * r is added for it in
+// fp32 from its exact residual, so every product (q - z) * x is carried to
+// within 2^-14 of itself whatever the spread of x inside a chunk (elements
+// more than about 2^9 below the chunk's largest take the fp32 correction).
+// One conversion to fp32 per chunk, the corrections, then a multiply by
+// 2^-sh and the group scale accumulate into the row's fp32 sum.
 
-constexpr int kIW = 28;   // LDS dwords per chunk: digit d of word w at 4d+w, then SX low/high, 2^(e-22)
+// Record of one chunk of x in LDS, kIW dwords:
+//   [4d + w]  digit plane d (0..5) of code word w (0..3)
+//   [24]      SX = sum of X, as (SX & 0xFFF) | (SX >> 12) << 16
+//   [25]      2^-sh as fp32 (NaN when the chunk holds Inf or NaN)
+//   [26]      flags: bit k set when element k takes the fp32 residual correction
+//   [27]      residual slots: bits 0-10 for elements 0-15, bits 11-21 for
+//             16-31 (kNoSlot: not stored, recomputed from x), bits 23-31 sh + 128
+// A slot holds the 16 fp32 residuals of one half chunk.
+constexpr int kIW = 28;
+constexpr uint32_t kNoSlot = 0x7FF;
 constexpr int kIntVPT = 16;                         // x values one thread converts
 constexpr int kIntTPC = 32 / kIntVPT;               // threads per chunk of x
 constexpr int kIntWaveChunks = q4::kWave / kIntTPC; // chunks of x one wavefront converts per pass
+constexpr float kRound = 12582912.0f;               // 1.5 * 2^23: adding it rounds |v| < 2^22 to an integer
+constexpr float kRhoInv = 16384.0f;                 // residuals above 2^-14 of |x * 2^sh| are flagged
 
 // 8x8 transpose of 4-bit fields: on return nibble p of a[l] is nibble l of
 // the input a[p].  Three butterfly stages: nibbles between neighbouring
@@ -423,12 +442,18 @@ __device__ __forceinline__ void transpose_nibbles(uint32_t (&a)[8]) {
     }
 }
 
-// Converts one chunk of x to its LDS record.  The chunk's 32 values are held
-// by kIntTPC consecutive lanes, kIntVPT each in order; `part` is the lane's
-// index among them.  Every lane of the wavefront must call it (the lanes of a
-// chunk exchange partial results by DPP); only lanes with `store` set write.
-__device__ __forceinline__ void store_int_chunk(const f32x4_t (&xr)[kIntVPT / 4], int part, bool store,
-                                                uint32_t *rec) {
+__device__ __forceinline__ uint32_t dpp_pair(uint32_t v) {   // the value of the lane's partner (lane ^ 1)
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+}
+
+// Converts one chunk of x to the digit planes, SX and 2^-sh of its LDS record
+// and returns sh.  The chunk's 32 values are held by kIntTPC consecutive
+// lanes, kIntVPT each in order; `part` is the lane's index among them.  Every
+// lane of the wavefront must call it (the lanes of a chunk exchange partial
+// results by DPP); only lanes with `store` set write.
+__device__ __forceinline__ int store_int_chunk(const f32x4_t (&xr)[kIntVPT / 4], int part, bool store,
+                                               uint32_t *rec) {
+    static_assert(kIntTPC == 2, "a chunk is converted by a lane pair");
     constexpr int V = kIntVPT;
     float v[V];
 #pragma unroll
@@ -439,25 +464,19 @@ __device__ __forceinline__ void store_int_chunk(const f32x4_t (&xr)[kIntVPT / 4]
     float m = 0.f;
 #pragma unroll
     for (int i = 0; i < V; ++i) m = __builtin_elementwise_maximum(m, __builtin_fabsf(v[i]));
-    // quad_perm [1,0,3,2], then [2,3,0,1]: the maximum over the chunk's lanes
-    m = __builtin_elementwise_maximum(
-        m, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, m), 0xB1, 0xF, 0xF, false)));
-    if (kIntTPC == 4)
-        m = __builtin_elementwise_maximum(
-            m, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, m), 0x4E, 0xF, 0xF, false)));
+    m = __builtin_elementwise_maximum(m, __builtin_bit_cast(float, dpp_pair(__builtin_bit_cast(uint32_t, m))));
     const int sh = 22 - __builtin_amdgcn_frexp_expf(m);   // |x| * 2^sh < 2^22 (m == 0: sh = 22)
     uint32_t dg[V];
     uint32_t sx = 0;                                       // sum of X, two's complement
 #pragma unroll
     for (int i = 0; i < V; ++i) {
         // adding 1.5 * 2^23 rounds to the nearest integer and leaves it in the low mantissa bits
-        const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_amdgcn_ldexpf(v[i], sh) + 12582912.0f);
+        const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_amdgcn_ldexpf(v[i], sh) + kRound);
         sx += b - 0x4B400000u;
         dg[i] = (b + (0x888888u - 0x4B400000u)) ^ 0x888888u;
     }
-    sx += (uint32_t)__builtin_amdgcn_mov_dpp((int)sx, 0xB1, 0xF, 0xF, false);
-    if (kIntTPC == 4) sx += (uint32_t)__builtin_amdgcn_mov_dpp((int)sx, 0x4E, 0xF, 0xF, false);
-    if (!store) return;
+    sx += dpp_pair(sx);
+    if (!store) return sh;
 #pragma unroll
     for (int w = 0; w < V / 8; ++w) {
         uint32_t a[8];
@@ -470,10 +489,114 @@ __device__ __forceinline__ void store_int_chunk(const f32x4_t (&xr)[kIntVPT / 4]
     if (part == 0) {
         // a chunk holding Inf or NaN gets a NaN scale, so its rows come out NaN
         const float scale = m <= 3.4028235e38f ? __builtin_amdgcn_ldexpf(1.0f, -sh) : m - m;
-        rec[24] = sx & 0xFFFu;
-        rec[25] = (uint32_t)((int)sx >> 12);   // arithmetic shift: SX = 4096 * high + low
-        rec[26] = __builtin_bit_cast(uint32_t, scale);
+        rec[24] = (sx & 0xFFFu) | ((uint32_t)((int)sx >> 12) << 16);   // |SX| < 2^27: the high part fits 16 bits
+        rec[25] = __builtin_bit_cast(uint32_t, scale);
     }
+    return sh;
+}
+
+// Exact residual r = v * 2^sh - round(v * 2^sh) of one x value (the same
+// operations as the conversion, so the same value wherever it is formed).
+__device__ __forceinline__ float int_residual(float v, int sh) {
+    const float vs = __builtin_amdgcn_ldexpf(v, sh);
+    return vs - ((vs + kRound) - kRound);
+}
+
+// Flags the chunk's elements whose residual exceeds 2^-14 of |x * 2^sh| and
+// stores the residuals of each half chunk holding a flag in a slot of
+// `pool`: slot `dense_slot` when it is >= 0, else the next free one of
+// `cap`, taken from the LDS counter `*next` (a half that finds the pool full
+// keeps kNoSlot, and its residuals are recomputed from x where they are
+// used).  Writes record dwords 26 and 27.  Every lane of the wavefront must
+// call it, with the arguments of store_int_chunk and its returned sh.
+__device__ __forceinline__ void store_int_residuals(const f32x4_t (&xr)[kIntVPT / 4], int sh, int part,
+                                                    bool store, uint32_t *rec, float *pool, int dense_slot,
+                                                    uint32_t *next, uint32_t cap) {
+    constexpr int V = kIntVPT;
+    float r[V];
+    uint32_t fl = 0;
+#pragma unroll
+    for (int i = V - 1; i >= 0; --i) {
+        const float v = xr[i / 4][i % 4];
+        const float vs = __builtin_amdgcn_ldexpf(v, sh);
+        r[i] = vs - ((vs + kRound) - kRound);
+        fl = (fl << 1) | (__builtin_fabsf(r[i]) * kRhoInv > __builtin_fabsf(vs) ? 1u : 0u);
+    }
+    uint32_t slot = kNoSlot;
+    if (store && fl) {
+        const uint32_t s = dense_slot >= 0 ? (uint32_t)dense_slot : __hip_atomic_fetch_add(
+            next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (s < cap) {
+            slot = s;
+            f32x4_t *dst = reinterpret_cast<f32x4_t *>(pool + (size_t)s * 16);
+#pragma unroll
+            for (int i = 0; i < V / 4; ++i) dst[i] = f32x4_t{r[4 * i], r[4 * i + 1], r[4 * i + 2], r[4 * i + 3]};
+        }
+    }
+    const uint32_t pfl = dpp_pair(fl), pslot = dpp_pair(slot);
+    if (store && part == 0) {
+        rec[26] = fl | (pfl << 16);
+        rec[27] = slot | (pslot << 11) | ((uint32_t)(sh + 128) << 23);
+    }
+}
+
+// Fields of a record's tail (dwords 24-27) as the dot-product loops use them.
+struct IntChunk {
+    int sxl, sxh;      // SX = 4096 * sxh + sxl
+    float cscale;      // 2^-sh
+    uint32_t flags, slots;
+};
+
+__device__ __forceinline__ IntChunk int_chunk_tail(const uint32_t *rec) {
+    const u32x4_t t = *reinterpret_cast<const u32x4_t *>(rec + 24);
+    IntChunk c;
+    c.sxl = (int)(t.x & 0xFFFu);
+    c.sxh = (int)t.x >> 16;
+    const uint32_t scale_bits = t.y;   // copied out before the bit cast
+    c.cscale = __builtin_bit_cast(float, scale_bits);
+    c.flags = t.z;
+    c.slots = t.w;
+    return c;
+}
+
+// Sum of (q - z) * X over one chunk for one weight row: 24 dot products of
+// the row's four code words (raw, XORed here) against the six digit planes,
+// the zero-point term (8 - z) * SX entering as (8 - z) * sxl in digit 0 and
+// (8 - z) * sxh in digit 3 (weight 16^3 = 2^12), then a Horner combine.
+__device__ __forceinline__ int int_chunk_dot(const u32x4_t &w, const u32x4_t (&D)[6], int nz, int sxl, int sxh,
+                                             uint32_t xor_mask) {
+    const uint32_t magic8 = 0x88888888u;
+    int a[6];
+    const uint32_t c0 = w.x ^ xor_mask;
+#pragma unroll
+    for (int d = 0; d < 6; ++d) {
+        if (d == 0) a[d] = __builtin_amdgcn_sdot8((int)c0, (int)D[d].x, __mul24(nz, sxl), false);
+        else if (d == 3) a[d] = __builtin_amdgcn_sdot8((int)c0, (int)D[d].x, __mul24(nz, sxh), false);
+        else asm("v_dot8_i32_i4 %0, %1, %2, 0" : "=v"(a[d]) : "v"(c0), "v"(D[d].x));
+    }
+#pragma unroll
+    for (int wd = 1; wd < 4; ++wd) {
+        const uint32_t cw = (wd == 1 ? w.y : wd == 2 ? w.z : w.w) ^ xor_mask;
+#pragma unroll
+        for (int d = 0; d < 6; ++d) {
+            const uint32_t dw = wd == 1 ? D[d].y : wd == 2 ? D[d].z : D[d].w;
+            a[d] = __builtin_amdgcn_sdot8((int)cw, (int)dw, a[d], false);
+        }
+    }
+    (void)magic8;
+    uint32_t tu = (uint32_t)a[5];
+#pragma unroll
+    for (int d = 4; d >= 0; --d) tu = (tu << 4) + (uint32_t)a[d];   // mod 2^32; the sum fits int32
+    return (int)tu;
+}
+
+// Code q (0..15) of element k (0..31) of a chunk's four code words; `xm` is
+// the XOR the words already carry (0, or 0x88888888 when they hold q - 8).
+__device__ __forceinline__ int chunk_code(const u32x4_t &w, uint32_t k, uint32_t xm) {
+    const uint32_t lo = (k & 8u) ? w.y : w.x;
+    const uint32_t hi = (k & 8u) ? w.w : w.z;
+    const uint32_t word = ((k & 16u) ? hi : lo) ^ xm;
+    return (int)__builtin_amdgcn_ubfe(word, (k & 7u) << 2, 4);
 }
 
 // W: wavefronts per workgroup.  JP: chunk positions per lane (a lane's chunks
@@ -517,7 +640,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     const int ZB = (G + 1) >> 1;
     const int RB = K >> 1;
     uint32_t *xrec = ilds;                                           // [C][kIW]
-    float *comb = reinterpret_cast<float *>(ilds + C * kIW);         // [W][R]
+    float *xres = reinterpret_cast<float *>(ilds + C * kIW);         // [C][32]: slot 2c + h, half h of chunk c
+    float *comb = xres + C * 32;                                     // [W][R]
     const int lane = tid & 63;
     constexpr int RG = 64 / LPR;               // rows one load instruction covers
     static_assert(LPR == 64 || (S == 1 && JP == 1), "short rows: no K-split, one chunk per lane");
@@ -551,7 +675,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     // stages and the kernel is latency-bound) the weights go first.  Then
     // group metadata, then the codes in the order they are consumed.
     constexpr bool kStageFirst = W >= 8;
-    if (kStageFirst && stager) store_int_chunk(xr, xpart, hc < C, xrec + hc * kIW);
+    int xsh = 0;
+    if (kStageFirst && stager) xsh = store_int_chunk(xr, xpart, hc < C, xrec + hc * kIW);
     __builtin_amdgcn_sched_barrier(0);
 
     // The SwiGLU form (SWI) runs the loads and arithmetic twice on the same
@@ -596,8 +721,13 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     }
 
     if (ph == 0) {
-        // Chunks of x past the first pass are loaded and converted here.
-        if (!kStageFirst && stager) store_int_chunk(xr, xpart, hc < C, xrec + hc * kIW);
+        // The residuals of the first pass (after this wavefront's weight
+        // loads), then the chunks of x past the first pass, loaded and
+        // converted here.  Every half chunk has its own residual slot.
+        if (stager) {
+            if (!kStageFirst) xsh = store_int_chunk(xr, xpart, hc < C, xrec + hc * kIW);
+            store_int_residuals(xr, xsh, xpart, hc < C, xrec + hc * kIW, xres, 2 * hc + xpart, nullptr, 2u * C);
+        }
         if (MULTI)
         for (int cb = kPass; cb < C; cb += kPass) {
             if (cb + wave * kIntWaveChunks >= C) break;
@@ -606,7 +736,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
             for (int i = 0; i < kIntVPT / 4; ++i)
                 xr[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                     x_r, (uint32_t)(c * 32 + xpart * kIntVPT + 4 * i) * 4u, 0, 0));
-            store_int_chunk(xr, xpart, c < C, xrec + c * kIW);
+            const int sh = store_int_chunk(xr, xpart, c < C, xrec + c * kIW);
+            store_int_residuals(xr, sh, xpart, c < C, xrec + c * kIW, xres, 2 * c + xpart, nullptr, 2u * C);
         }
         __syncthreads();
     }
@@ -621,41 +752,32 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
             u32x4_t D[6];
 #pragma unroll
             for (int d = 0; d < 6; ++d) D[d] = *reinterpret_cast<const u32x4_t *>(rec + 4 * d);
-            const u32x4_t tail = *reinterpret_cast<const u32x4_t *>(rec + 24);
-            const int sxl = (int)tail.x;
-            const int sxh = (int)tail.y;
-            const uint32_t scale_bits = tail.z;   // copied out before the bit cast
-            const float cscale = __builtin_bit_cast(float, scale_bits);
+            const IntChunk ic = int_chunk_tail(rec);
             const uint32_t zsh = (((uint32_t)c >> gshift) & 1u) << 2;
+            int nz[R];
+            float t[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                nz[r] = 8 - (int)__builtin_amdgcn_ubfe(zr[j][r], zsh, 4);
+                t[r] = 0.f;
+                if (r * RG + rgl < nrows)
+                    t[r] = (float)int_chunk_dot(w[j][r], D, nz[r], ic.sxl, ic.sxh, magic8);
+            }
+            // Flagged elements: (q - z) * r from their exact residuals.
+            for (uint32_t fm = ic.flags; fm; fm &= fm - 1) {
+                const uint32_t k = (uint32_t)__builtin_ctz(fm);
+                const uint32_t slot = (ic.slots >> (k < 16 ? 0 : 11)) & kNoSlot;
+                const float res = xres[slot * 16 + (k & 15u)];
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    if (r * RG + rgl < nrows)
+                        t[r] = __builtin_fmaf((float)(chunk_code(w[j][r], k, 0u) - 8 + nz[r]), res, t[r]);
+            }
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 if (r * RG + rgl < nrows) {
-                    // (8 - z) * SX enters as (8 - z) * SXlow in digit 0 and
-                    // (8 - z) * SXhigh in digit 3 (weight 16^3 = 2^12).
-                    const int nz = 8 - (int)__builtin_amdgcn_ubfe(zr[j][r], zsh, 4);
-                    int a[6];
-                    const uint32_t c0 = w[j][r].x ^ magic8;
-#pragma unroll
-                    for (int d = 0; d < 6; ++d) {
-                        if (d == 0) a[d] = __builtin_amdgcn_sdot8((int)c0, (int)D[d].x, __mul24(nz, sxl), false);
-                        else if (d == 3) a[d] = __builtin_amdgcn_sdot8((int)c0, (int)D[d].x, __mul24(nz, sxh), false);
-                        else asm("v_dot8_i32_i4 %0, %1, %2, 0" : "=v"(a[d]) : "v"(c0), "v"(D[d].x));
-                    }
-#pragma unroll
-                    for (int wd = 1; wd < 4; ++wd) {
-                        const uint32_t cw = (wd == 1 ? w[j][r].y : wd == 2 ? w[j][r].z : w[j][r].w) ^ magic8;
-#pragma unroll
-                        for (int d = 0; d < 6; ++d) {
-                            const uint32_t dw = wd == 1 ? D[d].y : wd == 2 ? D[d].z : D[d].w;
-                            a[d] = __builtin_amdgcn_sdot8((int)cw, (int)dw, a[d], false);
-                        }
-                    }
-                    uint32_t tu = (uint32_t)a[5];
-#pragma unroll
-                    for (int d = 4; d >= 0; --d) tu = (tu << 4) + (uint32_t)a[d];   // mod 2^32; the sum fits int32
-                    const int t = (int)tu;
                     const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sr[j][r]);
-                    acc[ph][r] = __builtin_fmaf(s, (float)t * cscale, acc[ph][r]);
+                    acc[ph][r] = __builtin_fmaf(s, t[r] * ic.cscale, acc[ph][r]);
                 }
             }
         }
@@ -720,12 +842,14 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
 // K segments of seg_chunks chunks when M rows of records would overflow the
 // LDS budget; the weights of a segment are loaded before its x is converted.
 // The S wavefronts of a row group split each segment's chunks and meet in
-// LDS at the end.
+// LDS at the end.  Residuals of flagged half chunks go to a pool of `cap`
+// slots per segment, dealt out by an LDS counter; half chunks past the pool
+// recompute theirs from x where they are used.
 template <int W, int MP, int JP, int R, int S>
 __global__ __launch_bounds__(W * 64) void gemv_q4_intm_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ wq,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
-    float *__restrict__ y, int M, int N, int K, int gshift, int rpg, int seg_chunks, int epi) {
+    float *__restrict__ y, int M, int N, int K, int gshift, int rpg, int seg_chunks, int cap, int epi) {
     static_assert(kIntTPC == 2, "two threads convert one chunk");
     extern __shared__ uint32_t ilds[];
     const int tid = threadIdx.x;
@@ -745,7 +869,9 @@ __global__ __launch_bounds__(W * 64) void gemv_q4_intm_kernel(
     const int rbase = min(gstart, N - 1);
     const uint32_t magic8 = 0x88888888u;
     uint32_t *xrec = ilds;                                                 // [M][seg][kIW]
-    float *comb = reinterpret_cast<float *>(ilds + M * seg_chunks * kIW);  // [W][R][MP]
+    float *pool = reinterpret_cast<float *>(ilds + M * seg_chunks * kIW);  // [cap][16]
+    float *comb = pool + cap * 16;                                         // [W][R][MP]
+    uint32_t *next = reinterpret_cast<uint32_t *>(comb + W * R * MP);      // next free pool slot
 
     const __amdgpu_buffer_rsrc_t x_r = raw_rsrc(x, (uint32_t)(M * K) * 4u);
     const uint32_t rows_left = (uint32_t)(N - rbase);
@@ -772,7 +898,8 @@ __global__ __launch_bounds__(W * 64) void gemv_q4_intm_kernel(
         const int nx = M * segC;                  // chunk records of this segment
 
         // x first: every pass's loads, then the conversion, then the barrier,
-        // all before any weight load is issued.
+        // all before any weight load is issued.  The pool counter is reset
+        // before the conversion (the previous segment's pool is no longer read).
         {
             f32x4_t xr[2][4];
 #pragma unroll
@@ -784,13 +911,17 @@ __global__ __launch_bounds__(W * 64) void gemv_q4_intm_kernel(
                 for (int i = 0; i < 4; ++i)
                     xr[q][i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(x_r, off + 16u * i, 0, 0));
             }
+            if (tid == 0) *next = 0u;
+            __syncthreads();
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const int pb = q * W * 32;
                 if (pb < nx) {
                     const int p = min(pb + hc, nx - 1);
                     const int m = p / segC, c = p - m * segC;
-                    store_int_chunk(xr[q], half, pb + hc < nx, xrec + (m * segC + c) * kIW);
+                    uint32_t *rec = xrec + (m * segC + c) * kIW;
+                    const int sh = store_int_chunk(xr[q], half, pb + hc < nx, rec);
+                    store_int_residuals(xr[q], sh, half, pb + hc < nx, rec, pool, -1, next, (uint32_t)cap);
                 }
             }
             for (int pb = 2 * W * 32; pb < nx; pb += W * 32) {
@@ -801,7 +932,9 @@ __global__ __launch_bounds__(W * 64) void gemv_q4_intm_kernel(
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     xq[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(x_r, off + 16u * i, 0, 0));
-                store_int_chunk(xq, half, pb + hc < nx, xrec + (m * segC + c) * kIW);
+                uint32_t *rec = xrec + (m * segC + c) * kIW;
+                const int sh = store_int_chunk(xq, half, pb + hc < nx, rec);
+                store_int_residuals(xq, sh, half, pb + hc < nx, rec, pool, -1, next, (uint32_t)cap);
             }
         }
         __syncthreads();
@@ -845,37 +978,33 @@ __global__ __launch_bounds__(W * 64) void gemv_q4_intm_kernel(
                         u32x4_t D[6];
 #pragma unroll
                         for (int d = 0; d < 6; ++d) D[d] = *reinterpret_cast<const u32x4_t *>(rec + 4 * d);
-                        const u32x4_t tail = *reinterpret_cast<const u32x4_t *>(rec + 24);
-                        const int sxl = (int)tail.x;
-                        const int sxh = (int)tail.y;
-                        const uint32_t scale_bits = tail.z;   // copied out before the bit cast
-                        const float cscale = __builtin_bit_cast(float, scale_bits);
+                        const IntChunk ic = int_chunk_tail(rec);
+                        float t[R];
 #pragma unroll
                         for (int r = 0; r < R; ++r) {
-                            if (r < nrows) {
-                                int a[6];
-                                const uint32_t c0 = w[j][r].x;
-#pragma unroll
-                                for (int d = 0; d < 6; ++d) {
-                                    if (d == 0) a[d] = __builtin_amdgcn_sdot8((int)c0, (int)D[d].x, __mul24(nz[r], sxl), false);
-                                    else if (d == 3) a[d] = __builtin_amdgcn_sdot8((int)c0, (int)D[d].x, __mul24(nz[r], sxh), false);
-                                    else asm("v_dot8_i32_i4 %0, %1, %2, 0" : "=v"(a[d]) : "v"(c0), "v"(D[d].x));
-                                }
-#pragma unroll
-                                for (int wd = 1; wd < 4; ++wd) {
-                                    const uint32_t cw = wd == 1 ? w[j][r].y : wd == 2 ? w[j][r].z : w[j][r].w;
-#pragma unroll
-                                    for (int d = 0; d < 6; ++d) {
-                                        const uint32_t dw = wd == 1 ? D[d].y : wd == 2 ? D[d].z : D[d].w;
-                                        a[d] = __builtin_amdgcn_sdot8((int)cw, (int)dw, a[d], false);
-                                    }
-                                }
-                                uint32_t tu = (uint32_t)a[5];
-#pragma unroll
-                                for (int d = 4; d >= 0; --d) tu = (tu << 4) + (uint32_t)a[d];   // mod 2^32; the sum fits int32
-                                acc[r][m] = __builtin_fmaf(s[r], (float)(int)tu * cscale, acc[r][m]);
-                            }
+                            t[r] = 0.f;
+                            if (r < nrows) t[r] = (float)int_chunk_dot(w[j][r], D, nz[r], ic.sxl, ic.sxh, 0u);
                         }
+                        // Flagged elements: (q - z) * r from their exact residuals.
+                        for (uint32_t fm = ic.flags; fm; fm &= fm - 1) {
+                            const uint32_t k = (uint32_t)__builtin_ctz(fm);
+                            const uint32_t slot = (ic.slots >> (k < 16 ? 0 : 11)) & kNoSlot;
+                            float res;
+                            if (slot != kNoSlot) {
+                                res = pool[slot * 16 + (k & 15u)];
+                            } else {
+                                const float xv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                    x_r, (uint32_t)(m * K + c * 32 + (int)k) * 4u, 0, 0));
+                                res = int_residual(xv, (int)(ic.slots >> 23) - 128);
+                            }
+#pragma unroll
+                            for (int r = 0; r < R; ++r)
+                                if (r < nrows)
+                                    t[r] = __builtin_fmaf((float)(chunk_code(w[j][r], k, magic8) - 8 + nz[r]), res, t[r]);
+                        }
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+                            if (r < nrows) acc[r][m] = __builtin_fmaf(s[r], t[r] * ic.cscale, acc[r][m]);
                     }
                 }
             }
@@ -948,12 +1077,14 @@ struct Geometry {
     int rpg;        // integer path: rows per workgroup
     int waves;      // wavefronts per workgroup
     int mp;         // integer path, M > 1: M rounded up to 2, 4 or 8
+    int pool;       // integer path, M > 1: residual slots (half chunks) per x segment
     int epi;        // launch-time: finish a SwiGLU block in the store (see store_y)
     int fma_r;      // multiply-add path: row slots per wavefront
     const Q4Matrix *swi;   // launch-time: the up matrix of a one-launch SwiGLU block
 };
 
 constexpr int kCUs = 256;   // compute units of an MI355X
+constexpr int kLdsMax = 160 * 1024;   // LDS of one CU, and the most one workgroup may use
 
 // The integer path serves one activation row when every lane owns whole
 // chunks (LPR = 64) and x fits the LDS budget in one piece.  Its K-split is
@@ -1003,8 +1134,16 @@ bool plan_integer(Geometry &p, int N, int K, const Knobs &k) {
     const int R = row_slots(1);
     const long groups = ((long)N + R - 1) / R;
     const long waves = groups * S;
-    const int W = k.waves ? k.waves : (S == 4 && waves >= 16L * kCUs ? 16 : (waves >= 8L * kCUs ? 8 : 4));
-    if (JP > 3 || W < S || (size_t)C * kIW * 4 + (size_t)W * R * 4 > (size_t)kLdsBytes) return false;
+    // Records and residual slots of the whole x; two workgroups share a CU's
+    // LDS only while they take at most half of it each.
+    const size_t xbytes = (size_t)C * (kIW * 4 + 32 * 4);
+    const bool half_cu = xbytes + (size_t)8 * R * 4 <= (size_t)kLdsMax / 2;
+    const int W = k.waves ? k.waves
+                          : ((S == 4 || (S > 1 && !half_cu)) && waves >= 16L * kCUs ? 16
+                                                                              : (waves >= 8L * kCUs ? 8 : 4));
+    if (JP > 3 || W < S || (size_t)C * kIW * 4 > (size_t)kLdsBytes ||
+        xbytes + (size_t)W * R * 4 > (size_t)kLdsMax)
+        return false;
     const int groups_per_wg = W / S;
     long grid = (groups + groups_per_wg - 1) / groups_per_wg;
     if (grid * W > (long)kCUs * 4) grid = (grid + kCUs - 1) / kCUs * kCUs;
@@ -1019,8 +1158,6 @@ bool plan_integer(Geometry &p, int N, int K, const Knobs &k) {
     p.segments = 1;
     return true;
 }
-
-constexpr int kLdsMax = 160 * 1024;   // LDS of one CU, and the most one workgroup may use
 
 // The integer path for 2 to 8 activation rows: workgroups of 8 wavefronts, 2
 // per CU (16 and 1 per CU at MP = 8, whose records need more LDS), each
@@ -1038,8 +1175,10 @@ bool plan_integer_m(Geometry &p, int M, int N, int K, const Knobs &k) {
     if (k.waves && k.waves != W) return false;
     const int wpc = MP == 8 ? 1 : 2;
     const int R = 4;
-    const int budget = kLdsMax / wpc - W * R * MP * 4;
-    int seg = std::min(C, budget / (M * kIW * 4));
+    // Per segment chunk and x row: its record and a quarter of a chunk's
+    // residuals in the pool (a pool slot holds half a chunk's); the counter.
+    const int budget = kLdsMax / wpc - W * R * MP * 4 - 16;
+    int seg = std::min(C, budget / (M * (kIW * 4 + 32)));
     if (seg < C) seg = seg / 64 * 64;
     // Segmented x costs a barrier and a pipeline drain per segment: below 5
     // rows the multiply-add path measures faster there (unless asked for).
@@ -1068,6 +1207,8 @@ bool plan_integer_m(Geometry &p, int M, int N, int K, const Knobs &k) {
     p.rows_per_wave = R;
     p.seg_chunks = seg;
     p.segments = (C + seg - 1) / seg;
+    p.pool = std::max(1, M * seg / 2);
+    if (p.pool >= (int)kNoSlot) return false;   // slot numbers are 11-bit fields
     return true;
 }
 
@@ -1160,9 +1301,12 @@ int validate(int M, int N, int K, int g) {
 // LDS bytes a launch needs: the x segment plus, with a K-split, one partial
 // sum per (wavefront, row, m).
 size_t lds_bytes(const Geometry &p) {
-    if (p.integer)
-        return (size_t)p.M * p.seg_chunks * kIW * 4 +
-               (p.S > 1 ? (size_t)p.waves * p.rows_per_wave * std::max(p.mp, 1) * 4 : 0);
+    if (p.integer && p.M > 1)   // records, residual pool, partial sums, pool counter
+        return (size_t)p.M * p.seg_chunks * kIW * 4 + (size_t)p.pool * 64 +
+               (size_t)p.waves * p.rows_per_wave * p.mp * 4 + 16;
+    if (p.integer)              // records, a residual slot per half chunk, partial sums
+        return (size_t)p.seg_chunks * (kIW * 4 + 128) +
+               (p.S > 1 ? (size_t)p.waves * p.rows_per_wave * 4 : 0);
     size_t b = (size_t)p.M * p.seg_chunks * kXStride * sizeof(float);
     if (p.S > 1) b += (size_t)kWaves * p.rows_per_wave * p.M * sizeof(float);
     return b;
@@ -1245,7 +1389,7 @@ template <int W, int MP, int JP, int S>
 void launch_intm(const Geometry &p, const float *x, const uint8_t *wq, const uint16_t *scales,
                  const uint8_t *zeros, float *y, int M, int N, int K, int gshift, hipStream_t st) {
     hipLaunchKernelGGL((gemv_q4_intm_kernel<W, MP, JP, 4, S>), dim3(p.grid), dim3(W * 64), lds_bytes(p), st,
-                       x, wq, scales, zeros, y, M, N, K, gshift, p.rpg, p.seg_chunks, p.epi);
+                       x, wq, scales, zeros, y, M, N, K, gshift, p.rpg, p.seg_chunks, p.pool, p.epi);
 }
 
 template <int W, int MP>

@@ -209,30 +209,78 @@ def test_gemv_q4_wide_dynamic_range_x(M, N, K):
     assert_within(y, y_ref, b, f"wide-range x M{M} N{N} K{K}")
 
 
-@pytest.mark.parametrize("N,K", [(129, 4096), (40, 2048)])
-def test_gemv_q4_integer_path_x_rounding_bound(N, K):
-    """The integer path's documented bound on inputs the plain bound does not
-    cover: in every 32-value chunk the one large x meets q == z, so only the
-    small x (2^14 to 2^15 times smaller) carry weight.  Each output must stay
-    within the plain bound plus 2^-22 * max|x over the chunk| * |w_k| per k."""
-    g = 128
-    assert q4.gemv_q4_path(1, N, K, g) == q4.Q4_PATH_INTEGER
-    d = wl.make_q4_problem(14, wl.Q4Shape(1, N, K, g, 0.002, 0.01))
-    rng = np.random.default_rng(14)
-    x = rng.uniform(0.5, 1.0, size=(1, K)) * rng.choice([-1.0, 1.0], size=(1, K))
-    x[:, 0::32] = 2.0 ** 14
+def _large_x_meets_zero_point(d, M, N, K, g, seed, big_exp=14, small=(0.5, 1.0)):
+    """In every 32-value chunk of every x row the first value is 2^big_exp and
+    meets q == z (so it carries no weight), while the other 31 values are
+    2^big_exp / small times smaller and meet random codes: only the small
+    values carry weight, and the plain bound is set by them alone."""
+    rng = np.random.default_rng(seed)
+    x = rng.uniform(*small, size=(M, K)) * rng.choice([-1.0, 1.0], size=(M, K))
+    x[:, 0::32] = 2.0 ** big_exp
     d["x"] = x.astype(np.float32)
     codes = np.stack([d["wq"] & 15, d["wq"] >> 4], -1).reshape(N, K)
     z = np.stack([d["zeros"] & 15, d["zeros"] >> 4], -1).reshape(N, -1)[:, :K // g]
     codes[:, 0::32] = np.repeat(z, g // 32, axis=1)
     d["wq"] = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return d
+
+
+X_RANGE = [(1, 129, 4096, 128), (1, 40, 2048, 128), (1, 300, 896, 32), (1, 77, 14336, 128),
+           (1, 5000, 1024, 32), (2, 300, 8192, 128), (4, 129, 4096, 128), (8, 67, 4096, 128),
+           (8, 40, 14336, 128), (3, 33, 1056, 32), (5, 64, 32768, 128)]
+
+
+@pytest.mark.parametrize("M,N,K,g", X_RANGE, ids=[f"M{a}N{b}K{c}g{d}" for a, b, c, d in X_RANGE])
+def test_gemv_q4_small_x_beside_large_at_plain_bound(M, N, K, g):
+    """Every chunk's large x meets q == z and only values 2^14-2^15 times
+    smaller carry weight; each output within the plain bound
+    |y - y_ref| <= 1e-4 * sum|w x| + 1e-6, on every path: one row (64 and 32
+    lanes per row, K-split), 2-8 rows (one and several x segments), the
+    multiply-add path (M = 3, K = 1056)."""
+    d = wl.make_q4_problem(14 + M, wl.Q4Shape(M, N, K, g, 0.002, 0.01))
+    d = _large_x_meets_zero_point(d, M, N, K, g, 14 + M)
     y = run_q4(dev(d), g)
     y_ref, b = oracle.gemv_q4(d["x"], d["wq"], d["scales"], d["zeros"], g)
-    w, _ = oracle.dequant(d["wq"], d["scales"], d["zeros"], K, g)
-    chunk_max = np.repeat(np.abs(d["x"].astype(np.float64)).reshape(-1, 32).max(1), 32)
-    extra = 2.0 ** -22 * (np.abs(w.astype(np.float64)) @ chunk_max)
-    err = np.abs(y[0].astype(np.float64) - y_ref[0])
-    assert np.all(err <= oracle.gemv_tolerance(b)[0] + extra), np.max(err / (oracle.gemv_tolerance(b)[0] + extra))
+    assert_within(y, y_ref, b, f"large x on q == z, M{M} N{N} K{K} path {q4.gemv_q4_path(M, N, K, g)}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 96, 4096), (4, 129, 4096), (8, 48, 4096), (8, 40, 14336), (2, 70, 8192)])
+def test_gemv_q4_every_small_x_corrected(M, N, K):
+    """Chunks whose 31 small values all take the fp32 residual correction
+    (2^20 beside values near 1): with 2 to 8 rows more half chunks hold
+    flagged values than the residual pool has slots, so the rest are
+    recomputed from x.  Plain bound."""
+    g = 128
+    d = wl.make_q4_problem(15 + M, wl.Q4Shape(M, N, K, g, 0.002, 0.01))
+    d = _large_x_meets_zero_point(d, M, N, K, g, 15 + M, big_exp=20)
+    y = run_q4(dev(d), g)
+    y_ref, b = oracle.gemv_q4(d["x"], d["wq"], d["scales"], d["zeros"], g)
+    assert_within(y, y_ref, b, f"all small x corrected, M{M} N{N} K{K}")
+
+
+@pytest.mark.parametrize("M,N,K,g", [(1, 300, 4096, 128), (1, 4864, 896, 32), (4, 129, 4096, 128),
+                                     (1, 70, 14336, 128)])
+def test_gemv_q4_swiglu_small_x_beside_large(M, N, K, g):
+    """The q == z construction through both projections of the SwiGLU block
+    (one launch at one row on the integer path, else two)."""
+    s = wl.Q4Shape(M, N, K, g, 0.002, 0.01)
+    dg = _large_x_meets_zero_point(wl.make_q4_problem(320 + N, s, index=0), M, N, K, g, 320 + N)
+    du = wl.make_q4_problem(320 + N, s, index=1)
+    du["x"] = dg["x"]
+    codes_g = np.stack([dg["wq"] & 15, dg["wq"] >> 4], -1).reshape(N, K)
+    zu = np.stack([du["zeros"] & 15, du["zeros"] >> 4], -1).reshape(N, -1)[:, :K // g]
+    cu = np.stack([du["wq"] & 15, du["wq"] >> 4], -1).reshape(N, K)
+    cu[:, 0::32] = np.repeat(zu, g // 32, axis=1)
+    du["wq"] = (cu[:, 0::2] | (cu[:, 1::2] << 4)).astype(np.uint8)
+    assert codes_g.shape == cu.shape
+    tg, tu = dev(dg), dev(du)
+    y = q4.gemv_q4_swiglu(tg["x"], (tg["wq"], tg["scales"], tg["zeros"]),
+                          (tu["wq"], tu["scales"], tu["zeros"]), g)
+    torch.cuda.synchronize()
+    y_ref, tol = oracle.swiglu(dg["x"], (dg["wq"], dg["scales"], dg["zeros"]),
+                               (du["wq"], du["scales"], du["zeros"]), g)
+    err = np.abs(y.cpu().numpy().astype(np.float64) - y_ref)
+    assert np.all(err <= tol), f"{int((err > tol).sum())} outputs out of tolerance, worst {np.max(err / tol):.3g}"
 
 
 @pytest.mark.parametrize("M,K", [(1, 4096), (1, 896), (3, 4096)])
