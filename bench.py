@@ -354,28 +354,8 @@ def run_default(args):
                       "read_reduce": wl.PROBE_BYTES,
                       "gemv_q4_swiglu": 2 * wl.q4_weight_bytes(s.N, s.K, s.g)}
 
-    # ---- the contract's timed region: W warm-up steps, then exactly K steps
-    G = graphs["gemv_q4"]
-    for _ in range(args.warmup):
-        G.g.replay()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    start.record()
-    for _ in range(args.steps):
-        G.g.replay()
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    elapsed = start.elapsed_time(end) / 1e3
-    launches = args.steps * wl.STREAM_MATRICES
-    per_launch = elapsed / launches
-    value = bytes_per_call["gemv_q4"] / per_launch / 1e9
-    log(f"timed region: {args.steps} steps, {launches} launches, {elapsed * 1e3:.3f} ms events, "
-        f"{wall * 1e3:.3f} ms wall; {per_launch * 1e6:.3f} us/launch -> {value:.1f} GB/s")
-
-    # ---- two-point / ITERS sweep / ABBA, in the same process
+    # ---- two-point / ITERS sweep / ABBA, in the same process, before the
+    # timed region (the GPU then runs the timed steps at its steady clocks)
     result = {}
     if not args.quick:
         iters = [int(v) for v in args.iters.split(",")]
@@ -400,15 +380,44 @@ def run_default(args):
                 f"(per launch {st['median'] and st['median'] * 1e6:.3f} us; p10-p90 "
                 f"{st['p10'] and st['p10'] * 1e6:.3f}-{st['p90'] and st['p90'] * 1e6:.3f}); "
                 f"noise cells {r['noise']}")
+
+    # ---- the single-launch read floor at the headline's size
+    floor = None if args.quick else run_stream_floor(torch, q4, dev)
+
+    # ---- the contract's timed region: W warm-up steps, then exactly K steps,
+    # each step one pass over the 32 matrices.  The K steps are one replay of
+    # a graph that holds them (K x 32 launches, captured beforehand), so that
+    # no host-side gap between graph launches falls inside the region.
+    steps_graph = Graph(lambda: [q4_pass() for _ in range(args.steps)], torch)
+    G = graphs["gemv_q4"]
+    for _ in range(args.warmup):
+        G.g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    start.record()
+    steps_graph.g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    elapsed = start.elapsed_time(end) / 1e3
+    del steps_graph
+    launches = args.steps * wl.STREAM_MATRICES
+    per_launch = elapsed / launches
+    value = bytes_per_call["gemv_q4"] / per_launch / 1e9
+    log(f"timed region: {args.steps} steps, {launches} launches, {elapsed * 1e3:.3f} ms events, "
+        f"{wall * 1e3:.3f} ms wall; {per_launch * 1e6:.3f} us/launch -> {value:.1f} GB/s")
+
     measured_peak = result.get("read_reduce", {}).get("GBps_median")
     if result.get("read_reduce"):
         result["read_reduce"]["workgroups"] = probe_grid
 
     traffic = traffic_from_profile(bytes_per_call["gemv_q4"])
     integer = q4.gemv_q4_path(1, s.N, s.K, s.g) == q4.Q4_PATH_INTEGER
-    arith = ("x per 32 values as integers below 2^22 plus exact fp32 residuals for values far below "
-             "the chunk's largest: exact int32 chunk sums, fp32 residual products, fp32 accumulate; "
-             "every product within 2^-14 of itself"
+    arith = ("x per 32 values as integers of at most 26 bits (seven 4-bit digit planes) plus the exact "
+             "fp32 residual of every value more than ~2^12 below the chunk's largest: exact int32 chunk "
+             "sums, fp32 residual products, fp32 accumulate; every product within 2^-14 of itself"
              if integer else "(q-z) in fp16, fp32 x, fp32 multiply-add and accumulate")
     line = {
         "metric": METRIC,
@@ -437,8 +446,16 @@ def run_default(args):
         "measured_peak_GBps": measured_peak and round(measured_peak, 1),
         "pct_of_measured_peak": measured_peak and round(100 * value / measured_peak, 2),
         "two_point": result or None,
+        "single_launch_floor_GBps": floor and floor["GBps_median"],
+        "pct_of_single_launch_floor": floor and round(100 * value / floor["GBps_median"], 2),
         "cache_class": "hbm-streaming",
     }
+    if not args.no_configs:
+        line["configs"] = run_configs(torch, q4, dev, W, result, floor,
+                                      None if args.no_cpu else args.config_cpu_seconds)
+        for c in line["configs"]["cells_cache_resident"] + line["configs"]["cells_hbm_streaming"]:
+            if measured_peak and c["GBps_median"]:
+                c["frac_of_measured_peak"] = round(c["GBps_median"] / measured_peak, 4)
     if not args.no_blocks:
         line["block_formats"] = run_block_formats(torch, q4, dev)
         line["scan2"] = run_scan(torch, q4, dev)
@@ -459,6 +476,305 @@ def run_default(args):
         log("timing the CPU oracle on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+# ---------------------------------------------------------------- the per-config table
+
+L2_BYTES = 32 << 20       # aggregate L2 (4 MB per XCD x 8): the read sweep runs at L2 speed up to here
+MALL_BYTES = 256 << 20    # the Infinity Cache: the read sweep's second cliff
+
+
+def cache_class_of(ws: int) -> str:
+    """Where a cell's cycled working set lives, from its size and the read
+    sweep's cliffs (64 MiB and 256 MiB on MI355X)."""
+    if ws <= L2_BYTES:
+        return "cache-resident (L2)"
+    if ws <= MALL_BYTES:
+        return "cache-resident (Infinity Cache)"
+    return "hbm-streaming"
+
+
+def time_pass(torch, fn, launches: int, reps_target_s: float = 0.02, runs: int = 5) -> dict:
+    """Per-launch seconds of a captured pass of `launches` launches, by the
+    two-point method over graph replays ((t(2n) - t(n)) / n, n replays of
+    about reps_target_s), `runs` kept samples after a warm-up; noise cells
+    (t(2n) < 1.2 t(n)) are dropped and counted."""
+    G = Graph(fn, torch)
+    G.time(2)
+    t1 = G.time(1)
+    reps = max(1, int(reps_target_s / max(t1, 1e-6)))
+    per, noise = [], 0
+    while len(per) < runs and noise < 2 * runs:
+        a, b = G.time(reps), G.time(2 * reps)
+        if resolvable(a, b):
+            per.append(two_point(a, b, reps) / launches)
+        else:
+            noise += 1
+    del G
+    st = summarize(per)
+    st["noise_cells"] = noise
+    return st
+
+
+def cell_record(kernel: str, st: dict, nbytes: int, ws: int, **extra) -> dict:
+    """One table cell: per-launch time (median, min, p10-p90), GB/s of the
+    algorithmic bytes and its fraction of the 8 TB/s peak, the cache class of
+    the cycled working set."""
+    med = st["median"]
+    rec = {"kernel": kernel, "bytes_per_launch": nbytes, "working_set_bytes": ws,
+           "cache_class": cache_class_of(ws),
+           "us_per_launch": {q: (round(st[q] * 1e6, 3) if st[q] else None) for q in ("median", "min", "p10", "p90")},
+           "runs": st["n"], "noise_cells": st.get("noise_cells", 0),
+           "GBps_median": round(nbytes / med / 1e9, 1) if med else None,
+           "GBps_best": round(nbytes / st["min"] / 1e9, 1) if st["min"] else None,
+           "frac_of_spec": round(nbytes / med / 1e9 / SPEC_PEAK_GBS, 4) if med else None}
+    rec.update(extra)
+    return rec
+
+
+def cpu_oracle_cell(problems, budget_s: float, threads: int) -> dict:
+    """The oracle, as it stands, on bounded samples of a config: `problems`
+    is a list of (x, weights, g, rows) and every call computes the listed
+    rows of one problem (rows split into contiguous ranges over `threads`
+    host threads); calls cycle through the problems until budget_s of oracle
+    time and at least three calls.  GB/s of the rows' int4 bytes, median call."""
+    import concurrent.futures
+    import numpy as np
+    import oracle
+    rates, t_used, calls = [], 0.0, 0
+    with concurrent.futures.ThreadPoolExecutor(threads) as ex:
+        while t_used < budget_s or calls < 3:
+            x, d, g, rows = problems[calls % len(problems)]
+            K = x.shape[1]
+            nbytes = wl.q4_weight_bytes(len(rows), K, g)
+            parts = [r for r in np.array_split(rows, threads) if r.size]
+            t0 = time.perf_counter()
+            list(ex.map(lambda r: oracle.gemv_q4(x, d["wq"], d["scales"], d["zeros"], g, rows=r), parts))
+            dt = time.perf_counter() - t0
+            rates.append(nbytes / dt / 1e9)
+            t_used += dt
+            calls += 1
+    return {"GBps": round(statistics.median(rates), 5), "threads": threads, "calls": calls,
+            "seconds": round(t_used, 2)}
+
+
+def cpu_for(problems, budget_s: float) -> dict:
+    """cpu_oracle_cell on one thread and on every host thread of one GPU's share."""
+    threads = max(1, min(CPU_THREADS_MAX, os.cpu_count() or 1))
+    out = {"kind": "oracle", "one_thread": cpu_oracle_cell(problems, budget_s / 2, 1)}
+    out["all_threads"] = cpu_oracle_cell(problems, budget_s / 2, threads) if threads > 1 else out["one_thread"]
+    out["cores"] = threads
+    return out
+
+
+def dev_mats(torch, dev, host: dict, copies: int, gen) -> list:
+    """Matrix 0 from the seeded generator and copies - 1 distinct matrices of
+    the same shape on the device: seeded random codes and zero points, every
+    scale 2^-7 (the same bytes per call; values do not change the stream)."""
+    m0 = {k: torch.from_numpy(v).to(dev) for k, v in host.items()}
+    out = [m0]
+    for _ in range(copies - 1):
+        m = {"wq": torch.randint(0, 256, m0["wq"].shape, dtype=torch.uint8, device=dev, generator=gen),
+             "scales": torch.full(m0["scales"].shape, 0x2000, dtype=torch.int16, device=dev),
+             "zeros": torch.randint(0, 256, m0["zeros"].shape, dtype=torch.uint8, device=dev, generator=gen)}
+        m["scales"] = m["scales"].view(torch.float16)
+        out.append(m)
+    return out
+
+
+def run_configs(torch, q4, dev, W, two_pt: dict, floor: dict | None, cpu_s: float) -> dict:
+    """The five workloads, each as int4 cells and dense fp32 control cells,
+    cache-resident cells (one matrix or one layer looped) apart from
+    HBM-streaming ones (distinct copies cycled past the Infinity Cache), each
+    with its two-point per-launch statistics, GB/s, fraction of the 8 TB/s
+    peak and cache class, and beside it the CPU oracle on bounded samples of
+    the same config (one thread and all threads).  configs[4]'s cells are the
+    headline's two-point cells and the single-launch read floor."""
+    import numpy as np
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.config_seed(7))
+    cells = []
+
+    def add(config, name, rec):
+        rec = dict(rec, config=config, name=name)
+        cells.append(rec)
+        log(f"config[{config}] {name:44s} {rec['kernel']:14s} {rec['us_per_launch']['median']:9.3f} us "
+            f"{rec['GBps_median']:8.1f} GB/s  {rec['cache_class']}")
+
+    def q4_pass(x, mats, ys, g, reps=1):
+        def fn():
+            for _ in range(reps):
+                for m, y in zip(mats, ys):
+                    q4.gemv_q4(x, m["wq"], m["scales"], m["zeros"], g, out=y)
+        return fn
+
+    def f32_pass(x, ws, ys, reps=1):
+        def fn():
+            for _ in range(reps):
+                for w, y in zip(ws, ys):
+                    q4.gemv_f32(x, w, out=y)
+        return fn
+
+    def dequant(m, g):
+        return q4.dequant_q4(m["wq"], m["scales"], m["zeros"], g, want_codes=False)[0]
+
+    cpu = {}
+    # ---- configs[0]: one 896 x 896 g32 GEMV
+    s = wl.SMALL_896
+    d = wl.make_q4_problem(wl.config_seed(0), s)
+    x = torch.from_numpy(d["x"]).to(dev)
+    m = {k: torch.from_numpy(v).to(dev) for k, v in d.items() if k != "x"}
+    y = [torch.empty((1, s.N), device=dev)]
+    nb = wl.q4_weight_bytes(s.N, s.K, s.g)
+    add(0, "single 896x896 g32, one matrix looped", cell_record(
+        "gemv_q4", time_pass(torch, q4_pass(x, [m], y, s.g, 64), 64), nb, nb))
+    w = dequant(m, s.g)
+    add(0, "single 896x896 fp32 control, one matrix looped", cell_record(
+        "gemv_f32", time_pass(torch, f32_pass(x, [w], y, 64), 64), 4 * s.N * s.K, 4 * s.N * s.K))
+    cpu_for_ = (lambda probs: cpu_for(probs, cpu_s)) if cpu_s else (lambda probs: None)
+    cpu[0] = cpu_for_([(d["x"], d, s.g, np.arange(s.N))])
+    del m, w
+
+    # ---- configs[1]: the seven decoder-layer GEMVs back to back
+    shapes = wl.DECODER_LAYER
+    hosts = [wl.make_q4_problem(wl.config_seed(1), sh, index=i) for i, sh in enumerate(shapes)]
+    xs = [torch.from_numpy(h["x"]).to(dev) for h in hosts]
+    layer = [{k: torch.from_numpy(v).to(dev) for k, v in h.items() if k != "x"} for h in hosts]
+    ys = [torch.empty((1, sh.N), device=dev) for sh in shapes]
+    lb = sum(wl.q4_weight_bytes(sh.N, sh.K, sh.g) for sh in shapes)
+    fb = sum(4 * sh.N * sh.K for sh in shapes)
+
+    def layer_pass(layers, f32=False, reps=1):
+        def fn():
+            for _ in range(reps):
+                for L in layers:
+                    for i, (mm, yy) in enumerate(zip(L, ys)):
+                        if f32:
+                            q4.gemv_f32(xs[i], mm, out=yy)
+                        else:
+                            q4.gemv_q4(xs[i], mm["wq"], mm["scales"], mm["zeros"], 32, out=yy)
+        return fn
+
+    st = time_pass(torch, layer_pass([layer], reps=16), 16)
+    add(1, "decoder layer, 7 GEMVs g32, one layer looped", cell_record(
+        "gemv_q4 x7", st, lb, lb, unit="per layer"))
+    copies = -(-(1 << 30) // lb)
+    many = [layer] + [[{k: v.clone() for k, v in mm.items()} for mm in layer] for _ in range(copies - 1)]
+    st = time_pass(torch, layer_pass(many), copies)
+    add(1, f"decoder layer, 7 GEMVs g32, {copies} layers cycled", cell_record(
+        "gemv_q4 x7", st, lb, lb * copies, unit="per layer"))
+    del many
+    fl = [dequant(mm, 32) for mm in layer]
+    st = time_pass(torch, layer_pass([fl], f32=True, reps=4), 4)
+    add(1, "decoder layer, 7 fp32 control GEMVs, one layer looped", cell_record(
+        "gemv_f32 x7", st, fb, fb, unit="per layer"))
+    fcopies = -(-(1 << 30) // fb)
+    fmany = [fl] + [[w.clone() for w in fl] for _ in range(fcopies - 1)]
+    st = time_pass(torch, layer_pass(fmany, f32=True), fcopies)
+    add(1, f"decoder layer, 7 fp32 control GEMVs, {fcopies} layers cycled", cell_record(
+        "gemv_f32 x7", st, fb, fb * fcopies, unit="per layer"))
+    del fmany, fl, layer
+    cpu[1] = cpu_for_([(h["x"], h, 32, np.arange(sh.N)) for h, sh in zip(hosts, shapes)])
+    torch.cuda.empty_cache()
+
+    # ---- configs[2]: the LM head 896 -> 151936 g32
+    s = wl.LM_HEAD
+    d = wl.make_q4_problem(wl.config_seed(2), s)
+    x = torch.from_numpy(d["x"]).to(dev)
+    nb = wl.q4_weight_bytes(s.N, s.K, s.g)
+    mats = dev_mats(torch, dev, {k: v for k, v in d.items() if k != "x"}, 8, gen)
+    y = [torch.empty((1, s.N), device=dev) for _ in mats]
+    add(2, "LM head 896->151936 g32, one matrix looped", cell_record(
+        "gemv_q4", time_pass(torch, q4_pass(x, mats[:1], y[:1], s.g, 8), 8), nb, nb))
+    add(2, "LM head 896->151936 g32, 8 matrices rotated", cell_record(
+        "gemv_q4", time_pass(torch, q4_pass(x, mats, y, s.g), 8), nb, 8 * nb))
+    ws = [dequant(mats[0], s.g)]
+    ws.append(ws[0].clone())
+    fbytes = 4 * s.N * s.K
+    add(2, "LM head fp32 control, 2 matrices rotated", cell_record(
+        "gemv_f32", time_pass(torch, f32_pass(x, ws, y[:2]), 2), fbytes, 2 * fbytes))
+    del mats, ws
+    rng = np.random.default_rng(2)
+    cpu[2] = cpu_for_([(d["x"], d, s.g, np.sort(rng.choice(s.N, 16384, replace=False)))])
+    torch.cuda.empty_cache()
+
+    # ---- configs[3]: the 8B-class FFN pair at M = 1, 4, 8
+    probs = []
+    for M in (1, 4, 8):
+        for i, sh in enumerate(wl.ffn_8b(M)):
+            h = wl.make_q4_problem(wl.config_seed(3), sh, index=i)
+            xx = torch.from_numpy(h["x"]).to(dev)
+            mm = {k: torch.from_numpy(v).to(dev) for k, v in h.items() if k != "x"}
+            yy = [torch.empty((M, sh.N), device=dev)]
+            nb = wl.q4_weight_bytes(sh.N, sh.K, sh.g)
+            path = "integer" if q4.gemv_q4_path(M, sh.N, sh.K, sh.g) == q4.Q4_PATH_INTEGER else "multiply-add"
+            st = time_pass(torch, q4_pass(xx, [mm], yy, sh.g, 8), 8)
+            flops = 2 * M * sh.N * sh.K
+            add(3, f"{sh.label}, one matrix looped", cell_record(
+                "gemv_q4", st, nb, nb, M=M, path=path,
+                TFLOPs=round(flops / st["median"] / 1e12, 2),
+                valu_frac_of_fp32_peak=round(flops / st["median"] / FP32_VECTOR_PEAK, 4)))
+            if M == 1:
+                w = dequant(mm, sh.g)
+                add(3, f"{sh.label} fp32 control, one matrix looped", cell_record(
+                    "gemv_f32", time_pass(torch, f32_pass(xx, [w], yy, 2), 2), 4 * sh.N * sh.K, 4 * sh.N * sh.K))
+                del w
+            probs.append((h["x"], h, sh.g, np.arange(0, sh.N, max(1, sh.N // 512))))
+            del mm
+    cpu[3] = cpu_for_(probs)
+    torch.cuda.empty_cache()
+
+    # ---- configs[4]: the headline's cells
+    s = wl.STREAM_SHAPE
+    nb = wl.q4_weight_bytes(s.N, s.K, s.g)
+    names = {"gemv_q4": ("stream 4096x14336 g128, 32 matrices cycled", nb, wl.STREAM_MATRICES * nb),
+             "gemv_f32": ("stream fp32 control, 4 matrices cycled", 4 * s.N * s.K,
+                          wl.STREAM_F32_MATRICES * 4 * s.N * s.K),
+             "gemv_q4_swiglu": ("SwiGLU block, 16 gate/up pairs cycled", 2 * nb, wl.STREAM_MATRICES * nb),
+             "read_reduce": ("read_reduce over 2 GiB (measured peak)", wl.PROBE_BYTES, wl.PROBE_BYTES)}
+    for k, (name, b, ws_) in names.items():
+        r = two_pt.get(k)
+        if not r:
+            continue
+        st = {q: (v * 1e-6 if v is not None and q != "n" else v) for q, v in r["per_launch_us"].items()}
+        add(4, name, cell_record(k, st, b, ws_))
+    if floor:
+        add(4, "read_reduce over 32 distinct 30.5 MB buffers (one launch each)",
+            cell_record("read_reduce", floor["stats"], floor["bytes_per_launch"], floor["working_set_bytes"],
+                        workgroups=floor["workgroups"]))
+    return {"cells_cache_resident": [c for c in cells if c["cache_class"] != "hbm-streaming"],
+            "cells_hbm_streaming": [c for c in cells if c["cache_class"] == "hbm-streaming"],
+            "cpu_oracle": {str(k): v for k, v in cpu.items()}}
+
+
+FLOOR_GRIDS = (256, 512, 768, 1024, 1536, 2048)
+
+
+def run_stream_floor(torch, q4, dev) -> dict:
+    """The single-launch read floor of the headline's size: read_reduce over
+    32 distinct buffers of 30,507,008 B (one stream matrix's bytes; 976 MB
+    cycled, past the Infinity Cache), one launch per buffer, non-temporal
+    loads, at the fastest of FLOOR_GRIDS workgroup counts."""
+    nbytes = wl.q4_weight_bytes(wl.STREAM_SHAPE.N, wl.STREAM_SHAPE.K, wl.STREAM_SHAPE.g)
+    nf = nbytes // 4
+    buf = torch.rand(wl.STREAM_MATRICES * nf, device=dev)
+    bufs = [buf[i * nf:(i + 1) * nf] for i in range(wl.STREAM_MATRICES)]
+    parts = torch.empty(max(FLOOR_GRIDS), device=dev)
+    best = None
+    for grid in FLOOR_GRIDS:
+        def fn(grid=grid):
+            for b in bufs:
+                q4.read_reduce(b, grid, partials=parts)
+        st = time_pass(torch, fn, len(bufs))
+        log(f"single-launch floor, {grid} workgroups: {st['median'] * 1e6:.3f} us/launch, "
+            f"{nbytes / st['median'] / 1e9:.1f} GB/s")
+        if best is None or st["median"] < best[0]["median"]:
+            best = (st, grid)
+    del buf, bufs
+    torch.cuda.empty_cache()
+    return {"stats": best[0], "workgroups": best[1], "bytes_per_launch": nbytes,
+            "working_set_bytes": wl.STREAM_MATRICES * nbytes,
+            "GBps_median": round(nbytes / best[0]["median"] / 1e9, 1)}
 
 
 # ---------------------------------------------------------------- block formats
@@ -1065,6 +1381,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-blocks", action="store_true", help="skip the block-format cells")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-config table")
+    ap.add_argument("--config-cpu-seconds", type=float, default=3.0,
+                    help="CPU oracle seconds per config of the table (half on one thread, half on all)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the 16 KiB - 2 GiB bandwidth sweep")
     ap.add_argument("--blocks-only", action="store_true", help="only the block-format cells")
     ap.add_argument("--block-shapes", default="",

@@ -60,11 +60,11 @@ enum q4_status {
  *   - fused multiply-add: (q - z) formed exactly in binary16, multiplied by
  *     the fp32 x and accumulated in fp32, the group scale applied per
  *     32-code chunk;
- *   - integer (M == 1: 512 < K <= 18688; 2 to 4 rows: K > 1024 while their
+ *   - integer (M == 1: 512 < K <= 19264; 2 to 4 rows: K > 1024 while their
  *     x fits one LDS segment; 5 to 8 rows: K > 1024): every chunk of 32 values
  *     of an x row (x[m][32c .. 32c+31]) is written as X + r with
- *     X = round(x * 2^sh) an integer, |X| < 2^22 (2^(22-sh-1) <= max|x| over
- *     the chunk < 2^(22-sh)), and r the exact residual; the sum of (q - z) * X
+ *     X = rint(x * 2^sh) an integer, |X| <= 2^26 (2^(25-sh) <= max|x| over
+ *     the chunk < 2^(26-sh)), and r the exact residual; the sum of (q - z) * X
  *     is formed exactly in int32, and for every element whose |r| exceeds
  *     2^-14 of |x * 2^sh| (values far below the chunk's largest) (q - z) * r
  *     is added in fp32, so each product is carried to within 2^-14 of itself;

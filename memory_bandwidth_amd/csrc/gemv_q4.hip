@@ -380,42 +380,46 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
 //
 // The (q - z) * x products are formed in integer arithmetic, eight per
 // instruction, on x written in block fixed point.  With e the binary exponent
-// of a 32-value chunk's largest |x| (|x| < 2^e) and sh = 22 - e, each element
-// becomes X = round(x * 2^sh), |X| < 2^22, and an exact residual
+// of a 32-value chunk's largest |x| (|x| < 2^e) and sh = 26 - e, each element
+// becomes X = rint(x * 2^sh), |X| <= 2^26, and an exact residual
 // r = x * 2^sh - X, |r| <= 1/2, so that x = (X + r) * 2^-sh exactly.
-// X is held as six signed 4-bit digits, X = sum_l d_l 16^l with d_l in
-// [-8, 7] (the nibbles of (X + 0x888888) ^ 0x888888), and the digits of 8
+// X is held as seven signed 4-bit digits, X = sum_l d_l 16^l with d_l in
+// [-8, 7] (the nibbles of (X + 0x8888888) ^ 0x8888888), and the digits of 8
 // consecutive x values are transposed into one 32-bit word per digit, so that
 // v_dot8_i32_i4 of such a word against a word of 8 codes, each read as q - 8
 // in [-8, 7] by one XOR with 0x88888888, sums the 8 products of one digit.
 // Then
 //     sum_k (q_k - z) X_k = sum_l 16^l sum_k (q_k - 8) d_l[k] + (8 - z) sum_k X_k
-// holds exactly in int32 (|sum| <= 32 * 15 * 2^22 < 2^31), so q == z still
-// gives exactly 0.
+// exactly: digits 0-3 (with (8 - z) times the low 16 bits of SX = sum X) and
+// digits 4-6 (with (8 - z) times SX >> 16) are each combined in int32, below
+// 2^24 and 2^20 in magnitude, so both convert to fp32 exactly and one fused
+// multiply-add joins them.  q == z still gives exactly 0.
 //
-// X alone carries x to within |r| <= 1/2 unit, which is a small fraction of
-// |x * 2^sh| only for the chunk's larger values.  An element whose residual
-// exceeds 2^-14 of |x * 2^sh| is flagged, and (q - z) * r is added for it in
-// fp32 from its exact residual, so every product (q - z) * x is carried to
-// within 2^-14 of itself whatever the spread of x inside a chunk (elements
-// more than about 2^9 below the chunk's largest take the fp32 correction).
-// One conversion to fp32 per chunk, the corrections, then a multiply by
-// 2^-sh and the group scale accumulate into the row's fp32 sum.
+// X alone carries x to within |r| <= 1/2 unit, a small fraction of
+// |x * 2^sh| except for values far below the chunk's largest.  An element
+// whose residual exceeds 2^-14 of |x * 2^sh| (one more than about 2^12 below
+// the chunk's largest) is flagged, and (q - z) * r is added for it in fp32
+// from its exact residual, so every product (q - z) * x is carried to within
+// 2^-14 of itself whatever the spread of x inside a chunk.  Then a multiply
+// by 2^-sh and the group scale accumulate into the row's fp32 sum.
 
 // Record of one chunk of x in LDS, kIW dwords:
-//   [4d + w]  digit plane d (0..5) of code word w (0..3)
-//   [24]      SX = sum of X, as (SX & 0xFFF) | (SX >> 12) << 16
-//   [25]      2^-sh as fp32 (NaN when the chunk holds Inf or NaN)
-//   [26]      flags: bit k set when element k takes the fp32 residual correction
-//   [27]      residual slots: bits 0-10 for elements 0-15, bits 11-21 for
+//   [4d + w]  digit plane d (0..6) of code word w (0..3)
+//   [28]      SX = sum of X (|SX| <= 2^31 - 32)
+//   [29]      2^-sh as fp32 (NaN when the chunk holds Inf or NaN)
+//   [30]      flags: bit k set when element k takes the fp32 residual correction
+//   [31]      residual slots: bits 0-10 for elements 0-15, bits 11-21 for
 //             16-31 (kNoSlot: not stored, recomputed from x), bits 23-31 sh + 128
+//   [32..35]  unused: 144 bytes, an odd number of 16-byte slots, so that the
+//             16-byte reads of consecutive lanes (consecutive chunks) fall in
+//             distinct LDS banks (a 128-byte stride measured 16% slower)
 // A slot holds the 16 fp32 residuals of one half chunk.
-constexpr int kIW = 28;
+constexpr int kPlanes = 7;
+constexpr int kIW = 36;
+constexpr int kTail = 4 * kPlanes;
 constexpr uint32_t kNoSlot = 0x7FF;
-constexpr int kIntVPT = 16;                         // x values one thread converts
-constexpr int kIntTPC = 32 / kIntVPT;               // threads per chunk of x
-constexpr int kIntWaveChunks = q4::kWave / kIntTPC; // chunks of x one wavefront converts per pass
-constexpr float kRound = 12582912.0f;               // 1.5 * 2^23: adding it rounds |v| < 2^22 to an integer
+constexpr int kIntVPT = 16;                         // x values a lane pair's lanes convert each
+constexpr int kIntTPC = 32 / kIntVPT;               // lanes per chunk of x
 constexpr float kRhoInv = 16384.0f;                 // residuals above 2^-14 of |x * 2^sh| are flagged
 
 // 8x8 transpose of 4-bit fields: on return nibble p of a[l] is nibble l of
@@ -442,19 +446,25 @@ __device__ __forceinline__ void transpose_nibbles(uint32_t (&a)[8]) {
     }
 }
 
-__device__ __forceinline__ uint32_t dpp_pair(uint32_t v) {   // the value of the lane's partner (lane ^ 1)
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+// DPP reads within a quad of lanes: the value of lane ^ 1, lane ^ 2, lane ^ 3.
+__device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+}
+__device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+}
+__device__ __forceinline__ uint32_t dpp_xor3(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x1B, 0xF, 0xF, false);   // quad_perm [3,2,1,0]
 }
 
-// Converts one chunk of x to the digit planes, SX and 2^-sh of its LDS record
-// and returns sh.  The chunk's 32 values are held by kIntTPC consecutive
-// lanes, kIntVPT each in order; `part` is the lane's index among them.  Every
-// lane of the wavefront must call it (the lanes of a chunk exchange partial
-// results by DPP); only lanes with `store` set write.
-__device__ __forceinline__ int store_int_chunk(const f32x4_t (&xr)[kIntVPT / 4], int part, bool store,
-                                               uint32_t *rec) {
-    static_assert(kIntTPC == 2, "a chunk is converted by a lane pair");
-    constexpr int V = kIntVPT;
+// Converts one chunk of x to the digit planes, SX and 2^-sh of its LDS
+// record and returns sh.  The chunk's 32 values are held by 32 / V
+// consecutive lanes (a pair or a quad), V each in order; `part` is the lane's
+// index among them.  Every lane of the wavefront must call it (the lanes of a
+// chunk exchange partial results by DPP); only lanes with `store` set write.
+template <int V>
+__device__ __forceinline__ int store_int_chunk(const f32x4_t (&xr)[V / 4], int part, bool store, uint32_t *rec) {
+    static_assert(V == 8 || V == 16, "a chunk is converted by a lane pair or a lane quad");
     float v[V];
 #pragma unroll
     for (int i = 0; i < V / 4; ++i) {
@@ -464,18 +474,20 @@ __device__ __forceinline__ int store_int_chunk(const f32x4_t (&xr)[kIntVPT / 4],
     float m = 0.f;
 #pragma unroll
     for (int i = 0; i < V; ++i) m = __builtin_elementwise_maximum(m, __builtin_fabsf(v[i]));
-    m = __builtin_elementwise_maximum(m, __builtin_bit_cast(float, dpp_pair(__builtin_bit_cast(uint32_t, m))));
-    const int sh = 22 - __builtin_amdgcn_frexp_expf(m);   // |x| * 2^sh < 2^22 (m == 0: sh = 22)
+    m = __builtin_elementwise_maximum(m, __builtin_bit_cast(float, dpp_xor1(__builtin_bit_cast(uint32_t, m))));
+    if (V == 8)
+        m = __builtin_elementwise_maximum(m, __builtin_bit_cast(float, dpp_xor2(__builtin_bit_cast(uint32_t, m))));
+    const int sh = 26 - __builtin_amdgcn_frexp_expf(m);   // |x| * 2^sh < 2^26 (m == 0: sh = 26)
     uint32_t dg[V];
     uint32_t sx = 0;                                       // sum of X, two's complement
 #pragma unroll
     for (int i = 0; i < V; ++i) {
-        // adding 1.5 * 2^23 rounds to the nearest integer and leaves it in the low mantissa bits
-        const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_amdgcn_ldexpf(v[i], sh) + kRound);
-        sx += b - 0x4B400000u;
-        dg[i] = (b + (0x888888u - 0x4B400000u)) ^ 0x888888u;
+        const uint32_t X = (uint32_t)(int)__builtin_rintf(__builtin_amdgcn_ldexpf(v[i], sh));
+        sx += X;
+        dg[i] = (X + 0x8888888u) ^ 0x8888888u;
     }
-    sx += dpp_pair(sx);
+    sx += dpp_xor1(sx);
+    if (V == 8) sx += dpp_xor2(sx);
     if (!store) return sh;
 #pragma unroll
     for (int w = 0; w < V / 8; ++w) {
@@ -484,73 +496,88 @@ __device__ __forceinline__ int store_int_chunk(const f32x4_t (&xr)[kIntVPT / 4],
         for (int p = 0; p < 8; ++p) a[p] = dg[8 * w + p];
         transpose_nibbles(a);
 #pragma unroll
-        for (int d = 0; d < 6; ++d) rec[4 * d + (V / 8) * part + w] = a[d];
+        for (int d = 0; d < kPlanes; ++d) rec[4 * d + (V / 8) * part + w] = a[d];
     }
     if (part == 0) {
         // a chunk holding Inf or NaN gets a NaN scale, so its rows come out NaN
         const float scale = m <= 3.4028235e38f ? __builtin_amdgcn_ldexpf(1.0f, -sh) : m - m;
-        rec[24] = (sx & 0xFFFu) | ((uint32_t)((int)sx >> 12) << 16);   // |SX| < 2^27: the high part fits 16 bits
-        rec[25] = __builtin_bit_cast(uint32_t, scale);
+        rec[kTail] = sx;
+        rec[kTail + 1] = __builtin_bit_cast(uint32_t, scale);
     }
     return sh;
 }
 
-// Exact residual r = v * 2^sh - round(v * 2^sh) of one x value (the same
-// operations as the conversion, so the same value wherever it is formed).
-__device__ __forceinline__ float int_residual(float v, int sh) {
-    const float vs = __builtin_amdgcn_ldexpf(v, sh);
-    return vs - ((vs + kRound) - kRound);
-}
-
 // Flags the chunk's elements whose residual exceeds 2^-14 of |x * 2^sh| and
 // stores the residuals of each half chunk holding a flag in a slot of
-// `pool`: slot `dense_slot` when it is >= 0, else the next free one of
-// `cap`, taken from the LDS counter `*next` (a half that finds the pool full
-// keeps kNoSlot, and its residuals are recomputed from x where they are
-// used).  Writes record dwords 26 and 27.  Every lane of the wavefront must
-// call it, with the arguments of store_int_chunk and its returned sh.
-__device__ __forceinline__ void store_int_residuals(const f32x4_t (&xr)[kIntVPT / 4], int sh, int part,
-                                                    bool store, uint32_t *rec, float *pool, int dense_slot,
-                                                    uint32_t *next, uint32_t cap) {
-    constexpr int V = kIntVPT;
+// `pool`: slot `dense_slot` (the half's own, for a lane quad: its lanes
+// write 8 residuals each) when it is >= 0, else, for a lane pair, the next
+// free one of `cap`, taken from the LDS counter `*next` (a half that finds
+// the pool full keeps kNoSlot, and its residuals are recomputed from x where
+// they are used).  Writes the record's flags and slots.  Every lane of the
+// wavefront must call it, with the arguments of store_int_chunk and the sh
+// it returned.
+template <int V>
+__device__ __forceinline__ void store_int_flags(const f32x4_t (&xr)[V / 4], int sh, int part, bool store,
+                                                uint32_t *rec, float *pool, int dense_slot, uint32_t *next,
+                                                uint32_t cap) {
     float r[V];
     uint32_t fl = 0;
 #pragma unroll
     for (int i = V - 1; i >= 0; --i) {
-        const float v = xr[i / 4][i % 4];
-        const float vs = __builtin_amdgcn_ldexpf(v, sh);
-        r[i] = vs - ((vs + kRound) - kRound);
+        const float vs = __builtin_amdgcn_ldexpf(xr[i / 4][i % 4], sh);
+        r[i] = vs - __builtin_rintf(vs);                   // exact
         fl = (fl << 1) | (__builtin_fabsf(r[i]) * kRhoInv > __builtin_fabsf(vs) ? 1u : 0u);
     }
-    uint32_t slot = kNoSlot;
-    if (store && fl) {
-        const uint32_t s = dense_slot >= 0 ? (uint32_t)dense_slot : __hip_atomic_fetch_add(
-            next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        if (s < cap) {
-            slot = s;
-            f32x4_t *dst = reinterpret_cast<f32x4_t *>(pool + (size_t)s * 16);
+    if constexpr (V == 16) {
+        uint32_t slot = kNoSlot;
+        if (store && fl) {
+            const uint32_t s = dense_slot >= 0 ? (uint32_t)dense_slot : __hip_atomic_fetch_add(
+                next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (s < cap) {
+                slot = s;
+                f32x4_t *dst = reinterpret_cast<f32x4_t *>(pool + (size_t)s * 16);
 #pragma unroll
-            for (int i = 0; i < V / 4; ++i) dst[i] = f32x4_t{r[4 * i], r[4 * i + 1], r[4 * i + 2], r[4 * i + 3]};
+                for (int i = 0; i < V / 4; ++i) dst[i] = f32x4_t{r[4 * i], r[4 * i + 1], r[4 * i + 2], r[4 * i + 3]};
+            }
         }
-    }
-    const uint32_t pfl = dpp_pair(fl), pslot = dpp_pair(slot);
-    if (store && part == 0) {
-        rec[26] = fl | (pfl << 16);
-        rec[27] = slot | (pslot << 11) | ((uint32_t)(sh + 128) << 23);
+        const uint32_t pfl = dpp_xor1(fl), pslot = dpp_xor1(slot);
+        if (store && part == 0) {
+            rec[kTail + 2] = fl | (pfl << 16);
+            rec[kTail + 3] = slot | (pslot << 11) | ((uint32_t)(sh + 128) << 23);
+        }
+    } else {
+        // lane quad, dense slots only: lanes 2h and 2h + 1 hold half h
+        const uint32_t f1 = dpp_xor1(fl), f2 = dpp_xor2(fl), f3 = dpp_xor3(fl);
+        if (store && fl) {
+            f32x4_t *dst = reinterpret_cast<f32x4_t *>(pool + (size_t)dense_slot * 16 + (part & 1) * 8);
+            dst[0] = f32x4_t{r[0], r[1], r[2], r[3]};
+            dst[1] = f32x4_t{r[4], r[5], r[6], r[7]};
+        }
+        if (store && part == 0) {
+            rec[kTail + 2] = fl | (f1 << 8) | (f2 << 16) | (f3 << 24);
+            rec[kTail + 3] = (uint32_t)dense_slot | ((uint32_t)(dense_slot + 1) << 11) | ((uint32_t)(sh + 128) << 23);
+        }
     }
 }
 
-// Fields of a record's tail (dwords 24-27) as the dot-product loops use them.
+// Exact residual r = v * 2^sh - rint(v * 2^sh) of one x value (the same
+// operations as the conversion, so the same value wherever it is formed).
+__device__ __forceinline__ float int_residual(float v, int sh) {
+    const float vs = __builtin_amdgcn_ldexpf(v, sh);
+    return vs - __builtin_rintf(vs);
+}
+
+// Fields of a record's tail as the dot-product loops use them.
 struct IntChunk {
-    int sxl, sxh;      // SX = 4096 * sxh + sxl
+    int sxl, sxh;      // SX = 65536 * sxh + sxl, 0 <= sxl < 65536
     float cscale;      // 2^-sh
     uint32_t flags, slots;
 };
 
 __device__ __forceinline__ IntChunk int_chunk_tail(const uint32_t *rec) {
-    const u32x4_t t = *reinterpret_cast<const u32x4_t *>(rec + 24);
+    const u32x4_t t = *reinterpret_cast<const u32x4_t *>(rec + kTail);
     IntChunk c;
-    c.sxl = (int)(t.x & 0xFFFu);
+    c.sxl = (int)(t.x & 0xFFFFu);
     c.sxh = (int)t.x >> 16;
     const uint32_t scale_bits = t.y;   // copied out before the bit cast
     c.cscale = __builtin_bit_cast(float, scale_bits);
@@ -559,35 +586,34 @@ __device__ __forceinline__ IntChunk int_chunk_tail(const uint32_t *rec) {
     return c;
 }
 
-// Sum of (q - z) * X over one chunk for one weight row: 24 dot products of
-// the row's four code words (raw, XORed here) against the six digit planes,
-// the zero-point term (8 - z) * SX entering as (8 - z) * sxl in digit 0 and
-// (8 - z) * sxh in digit 3 (weight 16^3 = 2^12), then a Horner combine.
-__device__ __forceinline__ int int_chunk_dot(const u32x4_t &w, const u32x4_t (&D)[6], int nz, int sxl, int sxh,
-                                             uint32_t xor_mask) {
-    const uint32_t magic8 = 0x88888888u;
-    int a[6];
+// Sum of (q - z) * X over one chunk for one weight row, as fp32: 28 dot
+// products of the row's four code words (XORed here with `xor_mask` to hold
+// q - 8) against the seven digit planes, the zero-point term (8 - z) * SX
+// entering as (8 - z) * sxl in digit 0 and (8 - z) * sxh in digit 4
+// (weight 16^4 = 2^16); digits 0-3 and 4-6 each combined exactly in int32,
+// then one fused multiply-add.
+__device__ __forceinline__ float int_chunk_dot(const u32x4_t &w, const u32x4_t (&D)[kPlanes], int nz, int sxl,
+                                               int sxh, uint32_t xor_mask) {
+    int a[kPlanes];
     const uint32_t c0 = w.x ^ xor_mask;
 #pragma unroll
-    for (int d = 0; d < 6; ++d) {
+    for (int d = 0; d < kPlanes; ++d) {
         if (d == 0) a[d] = __builtin_amdgcn_sdot8((int)c0, (int)D[d].x, __mul24(nz, sxl), false);
-        else if (d == 3) a[d] = __builtin_amdgcn_sdot8((int)c0, (int)D[d].x, __mul24(nz, sxh), false);
+        else if (d == 4) a[d] = __builtin_amdgcn_sdot8((int)c0, (int)D[d].x, __mul24(nz, sxh), false);
         else asm("v_dot8_i32_i4 %0, %1, %2, 0" : "=v"(a[d]) : "v"(c0), "v"(D[d].x));
     }
 #pragma unroll
     for (int wd = 1; wd < 4; ++wd) {
         const uint32_t cw = (wd == 1 ? w.y : wd == 2 ? w.z : w.w) ^ xor_mask;
 #pragma unroll
-        for (int d = 0; d < 6; ++d) {
+        for (int d = 0; d < kPlanes; ++d) {
             const uint32_t dw = wd == 1 ? D[d].y : wd == 2 ? D[d].z : D[d].w;
             a[d] = __builtin_amdgcn_sdot8((int)cw, (int)dw, a[d], false);
         }
     }
-    (void)magic8;
-    uint32_t tu = (uint32_t)a[5];
-#pragma unroll
-    for (int d = 4; d >= 0; --d) tu = (tu << 4) + (uint32_t)a[d];   // mod 2^32; the sum fits int32
-    return (int)tu;
+    const int lo = a[0] + 16 * (a[1] + 16 * (a[2] + 16 * a[3]));   // |lo| < 2^24
+    const int hi = a[4] + 16 * (a[5] + 16 * a[6]);                 // |hi| < 2^20
+    return __builtin_fmaf(65536.0f, (float)hi, (float)lo);
 }
 
 // Code q (0..15) of element k (0..31) of a chunk's four code words; `xm` is
@@ -606,7 +632,13 @@ __device__ __forceinline__ int chunk_code(const u32x4_t &w, uint32_t k, uint32_t
 // more chunks than one pass of the workgroup converts.  S and MULTI are
 // template parameters so that the common case (S = 1, one pass) carries no
 // division and no unused path.
-template <int W, int LPR, int JP, int R, int S, bool MULTI, bool SWI = false>
+// x values each converting lane takes in the one-row kernel: 16 (lane pairs
+// per chunk) or 8 (lane quads, one code word's values per lane, every
+// wavefront converting after issuing its weight loads: 8.25 against 7.82 us
+// per 4096 -> 14336 launch, 10.98 against 10.05 at 14336 -> 4096).
+constexpr int kM1XV = 16;
+
+template <int W, int LPR, int JP, int R, int S, bool MULTI, bool SWI = false, int XV = kM1XV>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) void gemv_q4_int_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ wq,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
@@ -618,21 +650,24 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     const int tid = threadIdx.x;
     // x first, before any address arithmetic: a CU returns loads in the
     // order they were issued, so x issued later would wait behind weight
-    // loads.  Lane pair (2i, 2i+1) loads chunk i, 16 values each; reads past K
-    // return 0.  Wavefronts whose chunks all lie past the end of x (the
-    // non-stagers) skip the conversion.
-    constexpr int kPass = W * kIntWaveChunks;          // chunks converted per workgroup pass
+    // loads.  The 32 / XV lanes from 32i / XV on load chunk i, XV values
+    // each; reads past K return 0.  Wavefronts whose chunks all lie past the
+    // end of x (the non-stagers) skip the conversion.
+    constexpr int XT = 32 / XV;                        // lanes per chunk of x
+    constexpr int XWC = 64 / XT;                       // chunks one wavefront converts per pass
+    constexpr int kPass = W * XWC;                     // chunks converted per workgroup pass
     const int C = K >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool stager = wave * kIntWaveChunks < C;
-    const int hc = tid / kIntTPC, xpart = tid % kIntTPC;
+    const bool stager = wave * XWC < C;
+    const int hc = tid / XT, xpart = tid % XT;
+    const int xslot = XV == 16 ? xpart : xpart >> 1;   // half chunk of the lane's values
     const __amdgpu_buffer_rsrc_t x_r = raw_rsrc(x, (uint32_t)K * 4u);
-    f32x4_t xr[kIntVPT / 4];
+    f32x4_t xr[XV / 4];
     if (stager) {
 #pragma unroll
-        for (int i = 0; i < kIntVPT / 4; ++i)
+        for (int i = 0; i < XV / 4; ++i)
             xr[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                x_r, (uint32_t)(hc * 32 + xpart * kIntVPT + 4 * i) * 4u, 0, 0));
+                x_r, (uint32_t)(hc * 32 + xpart * XV + 4 * i) * 4u, 0, 0));
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -674,9 +709,9 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     // keep the stream busy.  With 4 (small shapes, where every wavefront
     // stages and the kernel is latency-bound) the weights go first.  Then
     // group metadata, then the codes in the order they are consumed.
-    constexpr bool kStageFirst = W >= 8;
+    constexpr bool kStageFirst = W >= 8 && XV == 16;
     int xsh = 0;
-    if (kStageFirst && stager) xsh = store_int_chunk(xr, xpart, hc < C, xrec + hc * kIW);
+    if (kStageFirst && stager) xsh = store_int_chunk<XV>(xr, xpart, hc < C, xrec + hc * kIW);
     __builtin_amdgcn_sched_barrier(0);
 
     // The SwiGLU form (SWI) runs the loads and arithmetic twice on the same
@@ -721,23 +756,23 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     }
 
     if (ph == 0) {
-        // The residuals of the first pass (after this wavefront's weight
-        // loads), then the chunks of x past the first pass, loaded and
+        // The flags and residuals of the first pass (after this wavefront's
+        // weight loads), then the chunks of x past the first pass, loaded and
         // converted here.  Every half chunk has its own residual slot.
         if (stager) {
-            if (!kStageFirst) xsh = store_int_chunk(xr, xpart, hc < C, xrec + hc * kIW);
-            store_int_residuals(xr, xsh, xpart, hc < C, xrec + hc * kIW, xres, 2 * hc + xpart, nullptr, 2u * C);
+            if (!kStageFirst) xsh = store_int_chunk<XV>(xr, xpart, hc < C, xrec + hc * kIW);
+            store_int_flags<XV>(xr, xsh, xpart, hc < C, xrec + hc * kIW, xres, 2 * hc + xslot, nullptr, 2u * C);
         }
         if (MULTI)
         for (int cb = kPass; cb < C; cb += kPass) {
-            if (cb + wave * kIntWaveChunks >= C) break;
+            if (cb + wave * XWC >= C) break;
             const int c = cb + hc;
 #pragma unroll
-            for (int i = 0; i < kIntVPT / 4; ++i)
+            for (int i = 0; i < XV / 4; ++i)
                 xr[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                    x_r, (uint32_t)(c * 32 + xpart * kIntVPT + 4 * i) * 4u, 0, 0));
-            const int sh = store_int_chunk(xr, xpart, c < C, xrec + c * kIW);
-            store_int_residuals(xr, sh, xpart, c < C, xrec + c * kIW, xres, 2 * c + xpart, nullptr, 2u * C);
+                    x_r, (uint32_t)(c * 32 + xpart * XV + 4 * i) * 4u, 0, 0));
+            const int sh = store_int_chunk<XV>(xr, xpart, c < C, xrec + c * kIW);
+            store_int_flags<XV>(xr, sh, xpart, c < C, xrec + c * kIW, xres, 2 * c + xslot, nullptr, 2u * C);
         }
         __syncthreads();
     }
@@ -749,9 +784,9 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
         const int c = lo + li + LPR * j;
         if (c < hi) {
             const uint32_t *rec = xrec + c * kIW;
-            u32x4_t D[6];
+            u32x4_t D[kPlanes];
 #pragma unroll
-            for (int d = 0; d < 6; ++d) D[d] = *reinterpret_cast<const u32x4_t *>(rec + 4 * d);
+            for (int d = 0; d < kPlanes; ++d) D[d] = *reinterpret_cast<const u32x4_t *>(rec + 4 * d);
             const IntChunk ic = int_chunk_tail(rec);
             const uint32_t zsh = (((uint32_t)c >> gshift) & 1u) << 2;
             int nz[R];
@@ -761,7 +796,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
                 nz[r] = 8 - (int)__builtin_amdgcn_ubfe(zr[j][r], zsh, 4);
                 t[r] = 0.f;
                 if (r * RG + rgl < nrows)
-                    t[r] = (float)int_chunk_dot(w[j][r], D, nz[r], ic.sxl, ic.sxh, magic8);
+                    t[r] = int_chunk_dot(w[j][r], D, nz[r], ic.sxl, ic.sxh, magic8);
             }
             // Flagged elements: (q - z) * r from their exact residuals.
             for (uint32_t fm = ic.flags; fm; fm &= fm - 1) {
@@ -920,8 +955,8 @@ __global__ __launch_bounds__(W * 64) void gemv_q4_intm_kernel(
                     const int p = min(pb + hc, nx - 1);
                     const int m = p / segC, c = p - m * segC;
                     uint32_t *rec = xrec + (m * segC + c) * kIW;
-                    const int sh = store_int_chunk(xr[q], half, pb + hc < nx, rec);
-                    store_int_residuals(xr[q], sh, half, pb + hc < nx, rec, pool, -1, next, (uint32_t)cap);
+                    const int sh = store_int_chunk<kIntVPT>(xr[q], half, pb + hc < nx, rec);
+                    store_int_flags<kIntVPT>(xr[q], sh, half, pb + hc < nx, rec, pool, -1, next, (uint32_t)cap);
                 }
             }
             for (int pb = 2 * W * 32; pb < nx; pb += W * 32) {
@@ -933,8 +968,8 @@ __global__ __launch_bounds__(W * 64) void gemv_q4_intm_kernel(
                 for (int i = 0; i < 4; ++i)
                     xq[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(x_r, off + 16u * i, 0, 0));
                 uint32_t *rec = xrec + (m * segC + c) * kIW;
-                const int sh = store_int_chunk(xq, half, pb + hc < nx, rec);
-                store_int_residuals(xq, sh, half, pb + hc < nx, rec, pool, -1, next, (uint32_t)cap);
+                const int sh = store_int_chunk<kIntVPT>(xq, half, pb + hc < nx, rec);
+                store_int_flags<kIntVPT>(xq, sh, half, pb + hc < nx, rec, pool, -1, next, (uint32_t)cap);
             }
         }
         __syncthreads();
@@ -975,15 +1010,15 @@ __global__ __launch_bounds__(W * 64) void gemv_q4_intm_kernel(
                 for (int m = 0; m < MP; ++m) {
                     if (m < M) {
                         const uint32_t *rec = xrec + (m * segC + c - seg0) * kIW;
-                        u32x4_t D[6];
+                        u32x4_t D[kPlanes];
 #pragma unroll
-                        for (int d = 0; d < 6; ++d) D[d] = *reinterpret_cast<const u32x4_t *>(rec + 4 * d);
+                        for (int d = 0; d < kPlanes; ++d) D[d] = *reinterpret_cast<const u32x4_t *>(rec + 4 * d);
                         const IntChunk ic = int_chunk_tail(rec);
                         float t[R];
 #pragma unroll
                         for (int r = 0; r < R; ++r) {
                             t[r] = 0.f;
-                            if (r < nrows) t[r] = (float)int_chunk_dot(w[j][r], D, nz[r], ic.sxl, ic.sxh, 0u);
+                            if (r < nrows) t[r] = int_chunk_dot(w[j][r], D, nz[r], ic.sxl, ic.sxh, 0u);
                         }
                         // Flagged elements: (q - z) * r from their exact residuals.
                         for (uint32_t fm = ic.flags; fm; fm &= fm - 1) {
@@ -1141,8 +1176,7 @@ bool plan_integer(Geometry &p, int N, int K, const Knobs &k) {
     const int W = k.waves ? k.waves
                           : ((S == 4 || (S > 1 && !half_cu)) && waves >= 16L * kCUs ? 16
                                                                               : (waves >= 8L * kCUs ? 8 : 4));
-    if (JP > 3 || W < S || (size_t)C * kIW * 4 > (size_t)kLdsBytes ||
-        xbytes + (size_t)W * R * 4 > (size_t)kLdsMax)
+    if (JP > 3 || W < S || xbytes + (size_t)W * R * 4 > (size_t)kLdsMax)
         return false;
     const int groups_per_wg = W / S;
     long grid = (groups + groups_per_wg - 1) / groups_per_wg;
@@ -1175,10 +1209,11 @@ bool plan_integer_m(Geometry &p, int M, int N, int K, const Knobs &k) {
     if (k.waves && k.waves != W) return false;
     const int wpc = MP == 8 ? 1 : 2;
     const int R = 4;
-    // Per segment chunk and x row: its record and a quarter of a chunk's
-    // residuals in the pool (a pool slot holds half a chunk's); the counter.
+    // Per segment chunk and x row: its record and a sixteenth of a chunk's
+    // residuals in the pool (a pool slot holds half a chunk's; under
+    // x ~ N(0, 1) about 0.3% of half chunks hold a flag); the counter.
     const int budget = kLdsMax / wpc - W * R * MP * 4 - 16;
-    int seg = std::min(C, budget / (M * (kIW * 4 + 32)));
+    int seg = std::min(C, budget / (M * (kIW * 4 + 8)));
     if (seg < C) seg = seg / 64 * 64;
     // Segmented x costs a barrier and a pipeline drain per segment: below 5
     // rows the multiply-add path measures faster there (unless asked for).
@@ -1207,7 +1242,7 @@ bool plan_integer_m(Geometry &p, int M, int N, int K, const Knobs &k) {
     p.rows_per_wave = R;
     p.seg_chunks = seg;
     p.segments = (C + seg - 1) / seg;
-    p.pool = std::max(1, M * seg / 2);
+    p.pool = std::max(2, M * seg / 8);
     if (p.pool >= (int)kNoSlot) return false;   // slot numbers are 11-bit fields
     return true;
 }
@@ -1361,7 +1396,7 @@ void dispatch_integer_jp(const Geometry &p, const float *x, const uint8_t *wq, c
             return;
         }
     }
-    const bool multi = K / 32 > W * kIntWaveChunks;
+    const bool multi = K / 32 > W * (2 * kM1XV);
     switch (p.JP) {
     case 1:
         if (multi) launch_integer<W, 1, S, true>(p, x, wq, scales, zeros, y, N, K, gshift, st);
