@@ -80,9 +80,10 @@ int dequant_block(int format, const uint8_t *w, float *w_out, int N, int K, void
  * that many per CU and each workgroup loops over row blocks).  A set
  * geometry applies to every shape; 0, 0, 0 restores the default, a
  * per-format geometry for shapes of at least 512 row blocks and 1 row slot
- * with 4 wavefronts below that.  Process-wide, not thread-safe against concurrent
- * gemv_block calls.  Q4_EINVAL for an unknown format or an unsupported
- * combination. */
+ * with 4 wavefronts below that.  Process-wide (every caller's launches of
+ * the format take it); safe beside concurrent calls on other threads: a
+ * launch reads the setting whole, before or after a change.  Q4_EINVAL for
+ * an unknown format or an unsupported combination. */
 int gemv_block_set_config(int format, int rows_per_lane, int waves_per_group, int groups_per_cu);
 
 /* The geometry gemv_block uses now for `format`. */

@@ -76,7 +76,9 @@ enum q4_status {
  *     |y - y_ref| <= 1e-4 * sum_k |x[m, k] w[n, k]| + 1e-6,
  * with y_ref the exact sum and w = (q - z) * s the dequantised weight.
  *   1 <= M <= 8;  N >= 0 (N == 0 launches nothing);  group_size in {32, 128};
- *   K >= group_size and K % group_size == 0.
+ *   K >= group_size, K % group_size == 0 and K <= 16777216 (2^24: every
+ *   byte offset of the kernels' 32-bit buffer addressing then fits; a
+ *   longer K returns Q4_EINVAL rather than reading short).
  *   x and wq 16-byte aligned; scales 2-byte aligned; y 4-byte aligned.
  *   y must not overlap any input. */
 int gemv_q4(const float *x, const uint8_t *wq, const uint16_t *scales,
@@ -199,11 +201,14 @@ int q4_abi_version(void);
  * K <= 1024, or more than 3 chunk positions per lane); the previous setting
  * for the shape then stays.
  * Setting a shape again replaces its entry; up to 256 shapes.  Host-only:
- * needs no device, launches nothing, and is not safe to call while another
- * thread calls into the library. */
+ * needs no device and launches nothing.  The table is process-wide (every
+ * caller's launches of that shape take the setting) and safe to change
+ * while other threads call into the library: a launch reads a shape's
+ * setting whole, either before or after a concurrent change. */
 int gemv_q4_set_geometry(int M, int N, int K, int group_size, int path, int waves, int ksplit);
 
-/* Forgets every geometry set by gemv_q4_set_geometry.  Returns Q4_OK. */
+/* Forgets every geometry set by gemv_q4_set_geometry (process-wide, safe
+ * beside concurrent calls like gemv_q4_set_geometry).  Returns Q4_OK. */
 int gemv_q4_clear_geometry(void);
 
 #ifdef __cplusplus

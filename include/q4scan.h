@@ -52,8 +52,10 @@ int scan2(const uint32_t *codes, const float *lut, float *scores, int V, int D, 
  * give 16 wavefronts per compute unit).  The page's own tail runs 256
  * threads per workgroup, one vector per thread; the default here is the
  * table in LDS, 1 vector per thread, 1024 threads, automatic threads per
- * vector.  All zero restores the default.  Process-wide, not thread-safe
- * against concurrent scan2 calls.  Q4_EINVAL for any other value. */
+ * vector.  All zero restores the default.  Process-wide (every caller's
+ * scans take it); safe beside concurrent calls on other threads: a launch
+ * reads the setting whole, before or after a change.  Q4_EINVAL for any
+ * other value. */
 int scan2_set_config(int lut_in_lds, int vectors_per_thread, int threads_per_group,
                      int threads_per_vector);
 

@@ -35,6 +35,7 @@
 #include "q4blocks.h"
 
 #include <algorithm>
+#include <atomic>
 
 namespace {
 
@@ -669,13 +670,23 @@ constexpr int kCUs = 256;
 constexpr Cfg kDefault[6] = {{0, 0, 0, false}, {2, 4, 0, false}, {1, 4, 2, false},
                              {2, 4, 0, false}, {2, 4, 2, false}, {1, 4, 2, false}};
 constexpr Cfg kSmall = {1, 4, 0, false};
-Cfg g_cfg[6] = {kDefault[0], kDefault[1], kDefault[2], kDefault[3], kDefault[4], kDefault[5]};
+// The setting of each format, packed into one word so that a launch reads
+// it whole while gemv_block_set_config changes it on another thread:
+// R (bits 0-3), W (4-7), G (8-15), forced (16).
+constexpr uint32_t pack_cfg(Cfg c) {
+    return (uint32_t)c.R | (uint32_t)c.W << 4 | (uint32_t)c.G << 8 | (c.forced ? 1u << 16 : 0u);
+}
+inline Cfg unpack_cfg(uint32_t v) {
+    return {(int)(v & 15u), (int)((v >> 4) & 15u), (int)((v >> 8) & 255u), ((v >> 16) & 1u) != 0};
+}
+std::atomic<uint32_t> g_cfg[6] = {pack_cfg(kDefault[0]), pack_cfg(kDefault[1]), pack_cfg(kDefault[2]),
+                                  pack_cfg(kDefault[3]), pack_cfg(kDefault[4]), pack_cfg(kDefault[5])};
 
 // Lanes per row: the fewest of 64, 32, 16 that hold a row's units.
 int lanes_per_row(int K);
 
 Cfg config_for(int format, int N, int K) {
-    const Cfg c = g_cfg[format];
+    const Cfg c = unpack_cfg(g_cfg[format].load(std::memory_order_acquire));
     if (c.forced) return c;
     const int rpb = c.R * (64 / lanes_per_row(K)) * c.W;
     return (N + rpb - 1) / rpb < 2 * kCUs ? kSmall : c;
@@ -797,11 +808,11 @@ extern "C" int gemv_block_set_config(int format, int rows_per_lane, int waves_pe
     Geo g;
     if (!geometry_of(format, g)) return Q4_EINVAL;
     if (rows_per_lane == 0 && waves_per_group == 0 && groups_per_cu == 0) {
-        g_cfg[format] = kDefault[format];
+        g_cfg[format].store(pack_cfg(kDefault[format]), std::memory_order_release);
         return Q4_OK;
     }
     if (!cfg_ok(format, rows_per_lane, waves_per_group, groups_per_cu)) return Q4_EINVAL;
-    g_cfg[format] = {rows_per_lane, waves_per_group, groups_per_cu, true};
+    g_cfg[format].store(pack_cfg({rows_per_lane, waves_per_group, groups_per_cu, true}), std::memory_order_release);
     return Q4_OK;
 }
 
@@ -810,8 +821,9 @@ extern "C" int gemv_block_config(int format, int *rows_per_lane, int *waves_per_
     if (!rows_per_lane || !waves_per_group || !groups_per_cu) return Q4_ENULL;
     Geo g;
     if (!geometry_of(format, g)) return Q4_EINVAL;
-    *rows_per_lane = g_cfg[format].R;
-    *waves_per_group = g_cfg[format].W;
-    *groups_per_cu = g_cfg[format].G;
+    const Cfg c = unpack_cfg(g_cfg[format].load(std::memory_order_acquire));
+    *rows_per_lane = c.R;
+    *waves_per_group = c.W;
+    *groups_per_cu = c.G;
     return Q4_OK;
 }

@@ -33,6 +33,8 @@
 #include "q4_device.h"
 
 #include <algorithm>
+#include <mutex>
+#include <shared_mutex>
 
 namespace {
 
@@ -99,6 +101,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, uin
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
 }
 
+// The bytes from a wavefront's first row to the end of an array, for a
+// resource's 32-bit range field: formed in 64 bits and clamped.  The
+// wavefront itself only reads its own rows (at most a few rows past the
+// base, well inside 4 GiB for any K that validate() accepts), so the clamp
+// never cuts off a byte it reads.
+__device__ __forceinline__ uint32_t span32(uint64_t rows, uint64_t row_bytes) {
+    const uint64_t b = rows * row_bytes;
+    return b > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)b;
+}
+
 // Cache-policy bits of a buffer load: non-temporal, for the weight stream
 // that is read once.
 constexpr int kNonTemporal = 2;
@@ -149,10 +161,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     // byte offsets are uniform (SGPR soffset) when RG == 1 and per-lane
     // otherwise.  Rows past N re-read row N-1 and are not stored.
     const uint32_t rows_left = (uint32_t)(N - row_base);
-    const __amdgpu_buffer_rsrc_t wq_r = raw_rsrc(wq + (size_t)row_base * RB,
-        (uint32_t)std::min<uint64_t>((uint64_t)rows_left * RB, 0xFFFFFFFFull));
-    const __amdgpu_buffer_rsrc_t sc_r = raw_rsrc(scales + (size_t)row_base * G, rows_left * (uint32_t)G * 2u);
-    const __amdgpu_buffer_rsrc_t zp_r = raw_rsrc(zeros + (size_t)row_base * ZB, rows_left * (uint32_t)ZB);
+    const __amdgpu_buffer_rsrc_t wq_r = raw_rsrc(wq + (size_t)row_base * RB, span32(rows_left, RB));
+    const __amdgpu_buffer_rsrc_t sc_r = raw_rsrc(scales + (size_t)row_base * G, span32(rows_left, 2u * G));
+    const __amdgpu_buffer_rsrc_t zp_r = raw_rsrc(zeros + (size_t)row_base * ZB, span32(rows_left, ZB));
     uint32_t roff[R], soff[R], zoff[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -725,10 +736,9 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1, 4))) 
     const uint8_t *wqp = ph ? wq2 : wq;
     const uint16_t *scp = ph ? scales2 : scales;
     const uint8_t *zpp = ph ? zeros2 : zeros;
-    const __amdgpu_buffer_rsrc_t wq_r = raw_rsrc(wqp + (size_t)rbase * RB,
-        (uint32_t)std::min<uint64_t>((uint64_t)rows_left * RB, 0xFFFFFFFFull));
-    const __amdgpu_buffer_rsrc_t sc_r = raw_rsrc(scp + (size_t)rbase * G, rows_left * (uint32_t)G * 2u);
-    const __amdgpu_buffer_rsrc_t zp_r = raw_rsrc(zpp + (size_t)rbase * ZB, rows_left * (uint32_t)ZB);
+    const __amdgpu_buffer_rsrc_t wq_r = raw_rsrc(wqp + (size_t)rbase * RB, span32(rows_left, RB));
+    const __amdgpu_buffer_rsrc_t sc_r = raw_rsrc(scp + (size_t)rbase * G, span32(rows_left, 2u * G));
+    const __amdgpu_buffer_rsrc_t zp_r = raw_rsrc(zpp + (size_t)rbase * ZB, span32(rows_left, ZB));
     uint32_t sr[JP][R], zr[JP][R];
 #pragma unroll
     for (int j = 0; j < JP; ++j) {
@@ -908,12 +918,11 @@ __global__ __launch_bounds__(W * 64) void gemv_q4_intm_kernel(
     float *comb = pool + cap * 16;                                         // [W][R][MP]
     uint32_t *next = reinterpret_cast<uint32_t *>(comb + W * R * MP);      // next free pool slot
 
-    const __amdgpu_buffer_rsrc_t x_r = raw_rsrc(x, (uint32_t)(M * K) * 4u);
+    const __amdgpu_buffer_rsrc_t x_r = raw_rsrc(x, (uint32_t)(M * K) * 4u);   // M K <= 2^27 (validate)
     const uint32_t rows_left = (uint32_t)(N - rbase);
-    const __amdgpu_buffer_rsrc_t wq_r = raw_rsrc(wq + (size_t)rbase * RB,
-        (uint32_t)std::min<uint64_t>((uint64_t)rows_left * RB, 0xFFFFFFFFull));
-    const __amdgpu_buffer_rsrc_t sc_r = raw_rsrc(scales + (size_t)rbase * G, rows_left * (uint32_t)G * 2u);
-    const __amdgpu_buffer_rsrc_t zp_r = raw_rsrc(zeros + (size_t)rbase * ZB, rows_left * (uint32_t)ZB);
+    const __amdgpu_buffer_rsrc_t wq_r = raw_rsrc(wq + (size_t)rbase * RB, span32(rows_left, RB));
+    const __amdgpu_buffer_rsrc_t sc_r = raw_rsrc(scales + (size_t)rbase * G, span32(rows_left, 2u * G));
+    const __amdgpu_buffer_rsrc_t zp_r = raw_rsrc(zeros + (size_t)rbase * ZB, span32(rows_left, ZB));
     uint32_t lr[R];   // row offset of each slot: slots past the group's rows re-read its last row
 #pragma unroll
     for (int r = 0; r < R; ++r) lr[r] = (uint32_t)min(r, max(nrows, 1) - 1);
@@ -1311,23 +1320,42 @@ struct Override {
 constexpr int kMaxOverrides = 256;
 Override g_over[kMaxOverrides];
 int g_n_over = 0;
+// Callers on several threads: launches read the table under a shared lock,
+// gemv_q4_set_geometry / gemv_q4_clear_geometry write it under an exclusive
+// one, so a launch sees a shape's setting either before or after a change,
+// never half of one.
+std::shared_mutex g_over_mutex;
 
 Geometry plan(int M, int N, int K, int g) {
-    for (int i = 0; i < g_n_over; ++i) {
-        const Override &o = g_over[i];
-        if (o.M == M && o.N == N && o.K == K && o.g == g) {
-            bool ok = true;
-            const Geometry p = plan_with(M, N, K, o.k, &ok);
-            if (ok) return p;
-            break;
+    Knobs k;
+    bool found = false;
+    {
+        std::shared_lock<std::shared_mutex> lock(g_over_mutex);
+        for (int i = 0; i < g_n_over; ++i) {
+            const Override &o = g_over[i];
+            if (o.M == M && o.N == N && o.K == K && o.g == g) {
+                k = o.k;
+                found = true;
+                break;
+            }
         }
+    }
+    if (found) {
+        bool ok = true;
+        const Geometry p = plan_with(M, N, K, k, &ok);
+        if (ok) return p;
     }
     bool ok = true;
     return plan_with(M, N, K, Knobs{}, &ok);
 }
 
+// Longest row a call accepts: every per-lane and per-wavefront byte offset
+// (x up to 8 rows, a wavefront's rows of codes, scales and zero points)
+// then fits the 32-bit offsets and ranges of the buffer loads.
+constexpr int kMaxK = 1 << 24;
+
 int validate(int M, int N, int K, int g) {
-    if (M < 1 || M > 8 || N < 0 || K <= 0) return Q4_EINVAL;
+    if (M < 1 || M > 8 || N < 0 || K <= 0 || K > kMaxK) return Q4_EINVAL;
     if (g != 32 && g != 128) return Q4_EINVAL;
     if (K < g || K % g != 0) return Q4_EINVAL;
     return Q4_OK;
@@ -1502,6 +1530,7 @@ extern "C" int gemv_q4_set_geometry(int M, int N, int K, int group_size, int pat
     bool ok = true;
     plan_with(M, N, K, k, &ok);
     if (!ok) return Q4_EINVAL;
+    std::unique_lock<std::shared_mutex> lock(g_over_mutex);
     int i = 0;
     while (i < g_n_over && !(g_over[i].M == M && g_over[i].N == N && g_over[i].K == K &&
                              g_over[i].g == group_size))
@@ -1513,6 +1542,7 @@ extern "C" int gemv_q4_set_geometry(int M, int N, int K, int group_size, int pat
 }
 
 extern "C" int gemv_q4_clear_geometry(void) {
+    std::unique_lock<std::shared_mutex> lock(g_over_mutex);
     g_n_over = 0;
     return Q4_OK;
 }

@@ -31,6 +31,7 @@
 #include "q4scan.h"
 
 #include <algorithm>
+#include <atomic>
 
 namespace {
 
@@ -228,7 +229,16 @@ struct ScanCfg { int lds, vpt, tpg, tpv; };
 constexpr ScanCfg kScanDefault = {1, 1, 1024, 0};
 constexpr int kCUs = 256;
 constexpr int kMaxDLds = 4096;         // the largest D (the table in memory)
-ScanCfg g_scan = kScanDefault;
+// The scan's setting packed into one word, so that a launch reads it whole
+// while scan2_set_config changes it on another thread: lds (bit 0), vpt
+// (bits 1-2), tpg (3-13), tpv (14-17).
+constexpr uint32_t pack_scan(ScanCfg c) {
+    return (uint32_t)c.lds | (uint32_t)c.vpt << 1 | (uint32_t)c.tpg << 3 | (uint32_t)c.tpv << 14;
+}
+inline ScanCfg unpack_scan(uint32_t v) {
+    return {(int)(v & 1u), (int)((v >> 1) & 3u), (int)((v >> 3) & 2047u), (int)((v >> 14) & 15u)};
+}
+std::atomic<uint32_t> g_scan{pack_scan(kScanDefault)};
 
 bool scan_cfg_ok(int lds, int vpt, int tpg, int tpv) {
     return (lds == 0 || lds == 1) && (vpt == 1 || vpt == 2) && (tpg == 64 || tpg == 256 || tpg == 1024) &&
@@ -308,7 +318,7 @@ void launch_v(const ScanCfg &c, const uint32_t *codes, const float *lut, float *
 
 extern "C" int scan2(const uint32_t *codes, const float *lut, float *scores, int V, int D, int Q,
                      void *stream) {
-    ScanCfg c = g_scan;
+    ScanCfg c = unpack_scan(g_scan.load(std::memory_order_acquire));
     if (Q < 1 || Q > 8 || V < 0 || D < 64 || D % 64 != 0 || D > (c.lds ? 1024 : 4096))
         return Q4_EINVAL;
     if (c.tpv == 0) c.tpv = auto_tpv(V, Q, c.vpt);
@@ -326,21 +336,23 @@ extern "C" int scan2(const uint32_t *codes, const float *lut, float *scores, int
 extern "C" int scan2_set_config(int lut_in_lds, int vectors_per_thread, int threads_per_group,
                                 int threads_per_vector) {
     if (lut_in_lds == 0 && vectors_per_thread == 0 && threads_per_group == 0 && threads_per_vector == 0) {
-        g_scan = kScanDefault;
+        g_scan.store(pack_scan(kScanDefault), std::memory_order_release);
         return Q4_OK;
     }
     if (!scan_cfg_ok(lut_in_lds, vectors_per_thread, threads_per_group, threads_per_vector))
         return Q4_EINVAL;
-    g_scan = {lut_in_lds, vectors_per_thread, threads_per_group, threads_per_vector};
+    g_scan.store(pack_scan({lut_in_lds, vectors_per_thread, threads_per_group, threads_per_vector}),
+                 std::memory_order_release);
     return Q4_OK;
 }
 
 extern "C" int scan2_config(int *lut_in_lds, int *vectors_per_thread, int *threads_per_group,
                             int *threads_per_vector) {
     if (!lut_in_lds || !vectors_per_thread || !threads_per_group || !threads_per_vector) return Q4_ENULL;
-    *lut_in_lds = g_scan.lds;
-    *vectors_per_thread = g_scan.vpt;
-    *threads_per_group = g_scan.tpg;
-    *threads_per_vector = g_scan.tpv;
+    const ScanCfg c = unpack_scan(g_scan.load(std::memory_order_acquire));
+    *lut_in_lds = c.lds;
+    *vectors_per_thread = c.vpt;
+    *threads_per_group = c.tpg;
+    *threads_per_vector = c.tpv;
     return Q4_OK;
 }

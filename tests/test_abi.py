@@ -380,3 +380,121 @@ def test_tuner_candidates_are_what_the_library_accepts():
         q4.scan2_set_config(*c)
     q4.scan2_set_config(0, 0, 0, 0)
     assert q4.scan2_config() == (1, 1, 1024, 0)
+
+
+# ---------------------------------------------------------------- limits and concurrent callers
+
+def test_k_limit_rejected_before_anything_runs():
+    """K past 2^24 would need byte offsets beyond the kernels' 32-bit buffer
+    addressing: every entry point returns Q4_EINVAL for it (host-only query;
+    the launch entry points validate the same way before touching a device)."""
+    assert q4.gemv_q4_path(1, 8, 1 << 24, 128) in (q4.Q4_PATH_FMA, q4.Q4_PATH_INTEGER)
+    for fn in (lambda: q4.gemv_q4_path(1, 8, (1 << 24) + 128, 128),
+               lambda: q4.gemv_q4_geometry(8, 4, (1 << 24) + 128, 128),
+               lambda: q4.gemv_q4_set_geometry(1, 8, (1 << 24) + 128, 128, q4.Q4_PATH_FMA, 0, 0)):
+        with pytest.raises(q4.Q4Error) as e:
+            fn()
+        assert e.value.status == q4.Q4_EINVAL
+    L = q4.lib()
+    assert L.gemv_q4(None, None, None, None, None, 1, 8, (1 << 24) + 128, 128, None) == q4.Q4_EINVAL
+
+
+def test_large_matrices_keep_their_geometry():
+    """Shapes whose scale or code arrays pass 4 GiB from a wavefront's first
+    row (ranges once formed in 32 bits) plan like any other: the ranges are
+    64-bit and clamped, and a wavefront only reads its own rows."""
+    for M, N, K, g in [(1, 1 << 21, 65536, 32), (1, (1 << 22) + 3, 4096, 32), (8, 1 << 20, 1 << 16, 128)]:
+        geo = q4.gemv_q4_geometry(M, N, K, g)
+        assert geo["grid"] >= 1 and geo["lanes_per_row"] in (16, 32, 64)
+
+
+def test_geometry_table_is_safe_beside_concurrent_readers():
+    """One thread flips a shape's override between two settings while others
+    read its geometry: every read is one of the two settings' geometries or
+    the default plan's (never a mix)."""
+    import threading
+    M, N, K, g = 1, 14336, 4096, 128
+    q4.gemv_q4_clear_geometry()
+    default = q4.gemv_q4_geometry(M, N, K, g)
+    q4.gemv_q4_set_geometry(M, N, K, g, q4.Q4_PATH_INTEGER, 4, 0)
+    a = q4.gemv_q4_geometry(M, N, K, g)
+    q4.gemv_q4_set_geometry(M, N, K, g, q4.Q4_PATH_FMA, 0, 2)
+    b = q4.gemv_q4_geometry(M, N, K, g)
+    allowed = [default, a, b]
+    assert a != b
+    stop = threading.Event()
+    bad = []
+
+    def writer():
+        i = 0
+        while not stop.is_set():
+            if i % 3 == 2:
+                q4.gemv_q4_clear_geometry()
+            elif i % 2:
+                q4.gemv_q4_set_geometry(M, N, K, g, q4.Q4_PATH_INTEGER, 4, 0)
+            else:
+                q4.gemv_q4_set_geometry(M, N, K, g, q4.Q4_PATH_FMA, 0, 2)
+            i += 1
+
+    def reader():
+        for _ in range(3000):
+            geo = q4.gemv_q4_geometry(M, N, K, g)
+            if geo not in allowed:
+                bad.append(geo)
+
+    try:
+        w = threading.Thread(target=writer)
+        rs = [threading.Thread(target=reader) for _ in range(3)]
+        w.start()
+        for r in rs:
+            r.start()
+        for r in rs:
+            r.join()
+        stop.set()
+        w.join()
+    finally:
+        q4.gemv_q4_clear_geometry()
+    assert not bad, bad[:3]
+
+
+def test_block_and_scan_settings_read_whole_beside_a_writer():
+    """The block-format and scan settings are single words: readers on other
+    threads see either the old or the new setting, never a mix."""
+    import threading
+    fmt = q4.BLOCK_FORMATS["q4_k"]
+    L = q4.lib()
+    cfgs = [(1, 4, 2), (2, 8, 0)]
+    scans = [(1, 2, 256, 2), (0, 1, 64, 1)]
+    stop = threading.Event()
+    bad = []
+
+    def writer():
+        i = 0
+        while not stop.is_set():
+            L.gemv_block_set_config(fmt, *cfgs[i % 2])
+            L.scan2_set_config(*scans[i % 2])
+            i += 1
+
+    def reader():
+        for _ in range(5000):
+            c = q4.gemv_block_config("q4_k")
+            s = q4.scan2_config()
+            if tuple(c) not in cfgs or tuple(s) not in scans:
+                bad.append((c, s))
+
+    L.gemv_block_set_config(fmt, *cfgs[0])
+    L.scan2_set_config(*scans[0])
+    try:
+        w = threading.Thread(target=writer)
+        rs = [threading.Thread(target=reader) for _ in range(3)]
+        w.start()
+        for r in rs:
+            r.start()
+        for r in rs:
+            r.join()
+        stop.set()
+        w.join()
+    finally:
+        L.gemv_block_set_config(fmt, 0, 0, 0)
+        L.scan2_set_config(0, 0, 0, 0)
+    assert not bad, bad[:3]

@@ -9,6 +9,8 @@ shapes are run in the launch configuration the benchmark times and compared
 on sampled rows the oracle computes one by one.
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -586,3 +588,48 @@ def test_gemv_q4_random_shapes(M, N, K, g):
     y = run_q4(dev(d), g)
     y_ref, b = oracle.gemv_q4(d["x"], d["wq"], d["scales"], d["zeros"], g)
     assert_within(y, y_ref, b, f"M{M} N{N} K{K} g{g} path {q4.gemv_q4_path(M, N, K, g)}")
+
+
+# ---------------------------------------------------------------- the five configs, every row, tuned geometry
+
+def _oracle_all_rows(x, d, g, threads=16):
+    """Every row of the oracle's GEMV, rows split over host threads."""
+    import concurrent.futures
+    N = d["wq"].shape[0]
+    parts = [r for r in np.array_split(np.arange(N, dtype=np.int64), threads) if r.size]
+    with concurrent.futures.ThreadPoolExecutor(len(parts)) as ex:
+        res = list(ex.map(lambda r: oracle.gemv_q4(x, d["wq"], d["scales"], d["zeros"], g, rows=r), parts))
+    return np.concatenate([a for a, _ in res], axis=1), np.concatenate([b for _, b in res], axis=1)
+
+
+def _config_cases():
+    cases = [("config0", wl.SMALL_896, wl.config_seed(0), 0)]
+    cases += [(f"config1 {s.label}", s, wl.config_seed(1), i) for i, s in enumerate(wl.DECODER_LAYER)]
+    cases += [("config2", wl.LM_HEAD, wl.config_seed(2), 0)]
+    cases += [(f"config3 {s.label}", s, wl.config_seed(3), i) for M in (1, 4, 8) for i, s in enumerate(wl.ffn_8b(M))]
+    cases += [("config4", wl.STREAM_SHAPE, wl.config_seed(4), 0)]
+    return cases
+
+
+@pytest.fixture(scope="module")
+def tuned_profile():
+    """The device's tuned geometry profile applied, as the benchmark applies it."""
+    from memory_bandwidth_amd import autotune
+    path = autotune.default_profile_path(DEV)
+    n = autotune.apply_profile(path, DEV) if os.path.exists(path) else 0
+    yield n
+    q4.gemv_q4_clear_geometry()
+    for fmt in q4.BLOCK_FORMATS:
+        q4.gemv_block_set_config(fmt, 0, 0, 0)
+    q4.scan2_set_config(0, 0, 0, 0)
+
+
+@pytest.mark.parametrize("case", _config_cases(), ids=lambda c: c[0].replace(" ", "_"))
+def test_config_every_row_tuned_geometry(case, tuned_profile):
+    """Each configured GEMV in the geometry the benchmark runs (the tuned
+    profile applied), every output row against the oracle at the plain bound."""
+    label, s, seed, index = case
+    d = wl.make_q4_problem(seed, s, index=index)
+    y = run_q4(dev(d), s.g)
+    y_ref, b = _oracle_all_rows(d["x"], d, s.g)
+    assert_within(y, y_ref, b, f"{label} (tuned profile: {tuned_profile} settings)")
