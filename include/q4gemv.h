@@ -57,11 +57,12 @@ enum q4_status {
 /* int4 decode GEMV: y[M, N] = x[M, K] . dequant(W_q[N, K])^T, fp32 accumulate
  * (gerbil "WGSL Kernel Reference", section 3 MatMulInt4, "Dequantization").
  * Two arithmetic paths (gemv_q4_path tells which one a shape takes):
- *   - fused multiply-add: (q - z) formed exactly in binary16, multiplied by
- *     the fp32 x and accumulated in fp32, the group scale applied per
- *     32-code chunk;
- *   - integer (M == 1: 512 < K <= 19264; 2 to 4 rows: K > 1024 while their
- *     x fits one LDS segment; 5 to 8 rows: K > 1024): every chunk of 32 values
+ *   - fused multiply-add (2 to 8 rows; one row with K <= 512 or
+ *     K > 19264): (q - z) formed exactly (in fp32 for 2 to 8 rows, in
+ *     binary16 for one row), multiplied by the fp32 x with fp32 fused
+ *     multiply-adds, the group scale applied per 32-code chunk;
+ *   - integer (M == 1: 512 < K <= 19264; 2 to 8 rows with K > 1024 only when
+ *     fixed with gemv_q4_set_geometry): every chunk of 32 values
  *     of an x row (x[m][32c .. 32c+31]) is written as X + r with
  *     X = rint(x * 2^sh) an integer, |X| <= 2^26 (2^(25-sh) <= max|x| over
  *     the chunk < 2^(26-sh)), and r the exact residual; the sum of (q - z) * X
@@ -192,8 +193,8 @@ int q4_abi_version(void);
  * best configuration per device is kept as a profile).
  *   path     Q4_PATH_FMA or Q4_PATH_INTEGER
  *   waves    wavefronts per workgroup: 4, 8 or 16, or 0 for the plan's choice
- *            (the multiply-add path has 4; the integer path for 2 to 8 rows
- *            has 8, or 16 above 4 rows)
+ *            (the multiply-add path has 4 for one row and 8 for 2 to 8 rows;
+ *            the integer path for 2 to 8 rows has 8, or 16 above 4 rows)
  *   ksplit   wavefronts splitting one row's K range: 1, 2 or 4, or 0 for the
  *            plan's choice
  * Returns Q4_EINVAL for an invalid shape or knob, or a combination the

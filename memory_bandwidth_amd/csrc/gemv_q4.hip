@@ -1108,6 +1108,274 @@ __global__ __launch_bounds__(W * 64) void gemv_q4_intm_kernel(
     }
 }
 
+// ---------------------------------------------------------------- 2 to 8 activation rows: fp32 multiply-add
+//
+// With several activation rows every weight serves M products, so it pays to
+// form each weight once as an exact fp32 value and to run plain fp32 fused
+// multiply-adds, which on gfx950 issue at about twice the rate of the 4-bit
+// dot products and the mixed-precision multiply-adds, and which need no
+// conversion of x.  A code q at bits 4p..4p+3 of a 32-bit word (p <= 4) is
+// masked into the mantissa of a float whose exponent is that of 2^23: the
+// float is 2^23 + q 16^p, and subtracting 2^23 + z 16^p (both in [2^23,
+// 2^24), so the difference is exact) leaves (q - z) 16^p.  The word's upper
+// three codes take the same steps after a shift by 20.  x is staged in LDS
+// divided by the same power of two 16^p (exact), so every product is
+// (q - z) x, and the group scale multiplies each 32-code chunk's partial sum.
+// Per weight: one AND and one subtract, both of the fast-issuing kind.
+//
+// Lanes: 16 per row.  One 16-byte load instruction covers four rows (256
+// contiguous bytes each), and the four rows' lanes read the same x from LDS
+// (a broadcast), so four rows share each read of x.  A wavefront owns R
+// slots of four rows; S wavefronts split a row group's K range and meet in
+// LDS; a workgroup's rpg rows are dealt to its W / S row groups.
+constexpr int kFmStride = 36;   // floats per staged chunk of x: 144 bytes, an odd number of 16-byte slots
+
+// 16^-p for the code at nibble k (0..7) of its word: nibbles 0-4 in place,
+// 5-7 after the shift by 20 (positions 0-2).
+__host__ __device__ constexpr float fm_x_scale(int k) {
+    return k == 0 || k == 5 ? 1.0f : k == 1 || k == 6 ? 0.0625f : k == 2 || k == 7 ? 0.00390625f
+                                                             : k == 3 ? 0.000244140625f : 1.52587890625e-05f;
+}
+
+// The value of v, hidden from the compiler's algebra (so that a mask on a
+// pre-ORed base stays one AND rather than being re-associated into two).
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+template <int W, int MX, int R, int LPR, int S, int JP, int PD = 2, bool XPD = (W <= 8 || MX * R <= 4)>
+__global__ __launch_bounds__(W * 64) void gemv_q4_fm_kernel(
+    const float *__restrict__ x, const uint8_t *__restrict__ wq,
+    const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
+    float *__restrict__ y, int N, int K, int gshift, int rpg, int seg_chunks, int epi) {
+    constexpr int SUBR = 64 / LPR;             // rows one load instruction covers (a slot)
+    constexpr int NG = W / S;                  // row groups per workgroup
+    // float4 of one x row one thread loads ahead of the weights: the first
+    // 512 / 256 / 128 chunks of the segment for 2 / 3-4 / 5-8 rows
+    constexpr int XQ = (MX <= 2 ? 256 : 128) * 8 / (W * 64) > 0 ? (MX <= 2 ? 256 : 128) * 8 / (W * 64) : 1;
+    extern __shared__ float fms[];
+    float *xs = fms;                                                   // [MX][seg][kFmStride]
+    float *comb = fms + MX * seg_chunks * kFmStride;                   // [W][SUBR R][MX]
+    // every argument in registers at once: one round trip for the kernel
+    // arguments instead of one per use site
+    asm volatile("" ::"s"(x), "s"(wq), "s"(scales), "s"(zeros), "s"(y), "s"(N), "s"(K), "s"(gshift),
+                 "s"(rpg), "s"(seg_chunks), "s"(epi));
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int sub = lane / LPR, li = lane % LPR;
+    const int rg = wave / S, ks = wave - rg * S;
+    const int C = K >> 5;
+    const int G = K >> (gshift + 5);
+    const int ZB = (G + 1) >> 1;
+    const int RB = K >> 1;
+    const int gq = rpg / NG, grem = rpg - gq * NG;
+    const int gstart = blockIdx.x * rpg + rg * gq + min(rg, grem);
+    const int nrows = max(0, min(gq + (rg < grem ? 1 : 0), N - gstart));   // rows of this group, <= SUBR R
+    const int rbase = min(gstart, N - 1);
+    const uint32_t rows_left = (uint32_t)(N - rbase);
+    const __amdgpu_buffer_rsrc_t x_r = raw_rsrc(x, (uint32_t)(MX * K) * 4u);   // M K <= 2^27 (validate)
+    const __amdgpu_buffer_rsrc_t wq_r = raw_rsrc(wq + (size_t)rbase * RB, span32(rows_left, RB));
+    const __amdgpu_buffer_rsrc_t sc_r = raw_rsrc(scales + (size_t)rbase * G, span32(rows_left, 2u * G));
+    const __amdgpu_buffer_rsrc_t zp_r = raw_rsrc(zeros + (size_t)rbase * ZB, span32(rows_left, ZB));
+    // the row each slot of this lane works on (past the group's rows: its last row, not stored)
+    uint32_t lr[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) lr[r] = (uint32_t)min(SUBR * r + sub, max(nrows, 1) - 1);
+
+    float acc[R][MX];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MX; ++m) acc[r][m] = 0.f;
+
+    for (int seg0 = 0; seg0 < C; seg0 += seg_chunks) {
+        const int segC = min(seg_chunks, C - seg0);
+        const int part = (segC + S - 1) / S;
+        const int lo = seg0 + ks * part;
+        const int hi = min(seg0 + segC, lo + part);
+        const int clast = max(lo, hi - 1);        // loads past the range re-read a chunk inside it
+        const int n4 = segC * 8;                   // float4 of one x row in the segment
+        // x of the segment first (a CU returns loads in issue order), its
+        // first XQ * W * 64 float4 per row; then every code and metadata load of this
+        // wavefront's chunks; then x into LDS, divided by its codes' 16^p.
+        f32x4_t xv4[MX][XQ];
+#pragma unroll
+        for (int m = 0; m < MX; ++m)
+#pragma unroll
+            for (int q = 0; q < XQ; ++q) {
+                const int i = min(q * W * 64 + tid, n4 - 1);
+                xv4[m][q] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                    x_r, (uint32_t)(m * K + seg0 * 32 + 4 * i) * 4u, 0, 0));
+            }
+        __builtin_amdgcn_sched_barrier(0);
+        // Code and metadata loads, PD chunk positions ahead of the arithmetic:
+        // each wavefront's loads are paced by its own work, so that the
+        // wavefronts of a CU (whose loads return in issue order) receive
+        // their data at the same rate rather than one after another.
+        u32x4_t w[JP][R];
+        uint32_t sr[JP][R], zr[JP][R];
+        auto issue = [&](int j) {
+            const uint32_t c = (uint32_t)min(lo + li + LPR * j, clast);
+            const uint32_t gi = c >> gshift;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                sr[j][r] = __builtin_amdgcn_raw_buffer_load_b16(sc_r, gi * 2u + lr[r] * (uint32_t)G * 2u, 0, 0);
+                zr[j][r] = __builtin_amdgcn_raw_buffer_load_b8(zp_r, (gi >> 1) + lr[r] * (uint32_t)ZB, 0, 0);
+                w[j][r] = __builtin_amdgcn_raw_buffer_load_b128(wq_r, c * 16u + lr[r] * (uint32_t)RB, 0, kNonTemporal);
+            }
+        };
+        const f32x4_t sc_even = {fm_x_scale(0), fm_x_scale(1), fm_x_scale(2), fm_x_scale(3)};
+        const f32x4_t sc_odd = {fm_x_scale(4), fm_x_scale(5), fm_x_scale(6), fm_x_scale(7)};
+        for (int m = 0; m < MX; ++m)                  // the rest of longer segments, before any weight load
+            for (int i = XQ * W * 64 + tid; i < n4; i += W * 64) {
+                const f32x4_t v = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                    x_r, (uint32_t)(m * K + seg0 * 32 + 4 * i) * 4u, 0, 0));
+                *reinterpret_cast<f32x4_t *>(xs + (m * segC + (i >> 3)) * kFmStride + 4 * (i & 7)) =
+                    v * ((i & 1) ? sc_odd : sc_even);
+            }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < PD && j < JP; ++j) issue(j);
+        __builtin_amdgcn_sched_barrier(0);
+        // Threads past the segment store their clamped (last) element again:
+        // the same value to the same place, and no store under a condition,
+        // which would let the compiler sink the x load below the weight loads.
+#pragma unroll
+        for (int m = 0; m < MX; ++m)
+#pragma unroll
+            for (int q = 0; q < XQ; ++q) {
+                const int i = min(q * W * 64 + tid, n4 - 1);
+                *reinterpret_cast<f32x4_t *>(xs + (m * segC + (i >> 3)) * kFmStride + 4 * (i & 7)) =
+                    xv4[m][q] * ((i & 1) ? sc_odd : sc_even);
+            }
+        __syncthreads();
+
+        // x of each (chunk, half word) is read from LDS one step ahead of its use
+        // (XPD), or just before it where the second buffer would not fit in registers.
+        float xw[XPD ? 2 : 1][MX][4];
+        auto xload = [&](int stp, float (&xr)[MX][4]) {
+            const int c = min(lo + li + LPR * (stp >> 3), clast);
+            const float *xc = xs + (c - seg0) * kFmStride + 4 * (stp & 7);
+#pragma unroll
+            for (int m = 0; m < MX; ++m) {
+                const f32x4_t a = *reinterpret_cast<const f32x4_t *>(xc + m * segC * kFmStride);
+                xr[m][0] = a.x; xr[m][1] = a.y; xr[m][2] = a.z; xr[m][3] = a.w;
+            }
+        };
+        if constexpr (XPD) xload(0, xw[0]);
+#pragma unroll
+        for (int j = 0; j < JP; ++j) {
+            if (j + PD < JP) issue(j + PD);
+            __builtin_amdgcn_sched_barrier(0);
+            const int c = lo + li + LPR * j;
+            const uint32_t gi = (uint32_t)min(c, clast) >> gshift;
+            float t[R][MX];
+            float cz[R][5];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float zf = (float)__builtin_amdgcn_ubfe(zr[j][r], (gi & 1u) << 2, 4);
+#pragma unroll
+                for (int p = 0; p < 5; ++p) cz[r][p] = __builtin_fmaf(zf, (float)(1 << (4 * p)), 8388608.0f);
+#pragma unroll
+                for (int m = 0; m < MX; ++m) t[r][m] = 0.f;
+            }
+#pragma unroll
+            for (int wd = 0; wd < 4; ++wd) {
+                float f[R][8];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const uint32_t cw = wd == 0 ? w[j][r].x : wd == 1 ? w[j][r].y : wd == 2 ? w[j][r].z : w[j][r].w;
+                    const uint32_t blo = opaque((cw & 0x000FFFFFu) | 0x4B000000u);
+                    const uint32_t bhi = opaque((cw >> 20) | 0x4B000000u);
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const uint32_t bb = k < 5 ? blo : bhi;
+                        const int p = k < 5 ? k : k - 5;
+                        f[r][k] = __builtin_bit_cast(float, bb & (0xFF800000u | (0xFu << (4 * p)))) - cz[r][p];
+                    }
+                }
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int stp = 8 * j + 2 * wd + h;
+                    // the fence keeps each LDS read one step ahead, not hoisted further
+                    __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (XPD) {
+                        if (stp + 1 < 8 * JP) xload(stp + 1, xw[(stp + 1) & 1]);
+                    } else {
+                        xload(stp, xw[0]);
+                    }
+                    const int xb = XPD ? (stp & 1) : 0;
+                    // R x MX independent accumulators, element by element
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+#pragma unroll
+                        for (int m = 0; m < MX; ++m)
+#pragma unroll
+                            for (int r = 0; r < R; ++r)
+                                t[r][m] = __builtin_fmaf(f[r][4 * h + k], xw[xb][m][k], t[r][m]);
+                    // pin this step's products before the next fence (pure arithmetic
+                    // is otherwise free to sink past it, and the reads pile up)
+#pragma unroll
+                    for (int m = 0; m < MX; ++m)
+#pragma unroll
+                        for (int r = 0; r < R; ++r) asm volatile("" : "+v"(t[r][m]));
+                }
+            }
+            if (c < hi) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const float scf = (float)__builtin_bit_cast(_Float16, (uint16_t)sr[j][r]);
+#pragma unroll
+                    for (int m = 0; m < MX; ++m) acc[r][m] = __builtin_fmaf(scf, t[r][m], acc[r][m]);
+                }
+            }
+        }
+        if (seg0 + seg_chunks < C) __syncthreads();   // x segment fully read before the next overwrites it
+    }
+
+    // Each slot's sum over its LPR lanes; lane 0 of the group holds it.
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MX; ++m) acc[r][m] = q4::group_sum<LPR>(acc[r][m]);
+    if (S == 1) {
+        if (li == 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int rr = SUBR * r + sub;
+                if (rr < nrows)
+#pragma unroll
+                    for (int m = 0; m < MX; ++m)
+                        store_y(y, (size_t)m * N + gstart + rr, acc[r][m], epi);
+            }
+        }
+        return;
+    }
+    if (li == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < MX; ++m) comb[(wave * SUBR * R + SUBR * r + sub) * MX + m] = acc[r][m];
+    }
+    __syncthreads();
+    if (ks == 0 && li == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int rr = SUBR * r + sub;
+            if (rr < nrows) {
+#pragma unroll
+                for (int m = 0; m < MX; ++m) {
+                    float v = acc[r][m];
+                    for (int u = 1; u < S; ++u) v += comb[((wave + u) * SUBR * R + SUBR * r + sub) * MX + m];
+                    store_y(y, (size_t)m * N + gstart + rr, v, epi);
+                }
+            }
+        }
+    }
+}
+
 // One int4 matrix of a call.
 struct Q4Matrix {
     const uint8_t *wq;
@@ -1122,6 +1390,7 @@ struct Geometry {
     int waves;      // wavefronts per workgroup
     int mp;         // integer path, M > 1: M rounded up to 2, 4 or 8
     int pool;       // integer path, M > 1: residual slots (half chunks) per x segment
+    bool fm;        // M > 1: fp32 multiply-add on exactly dequantised weights (gemv_q4_fm_kernel)
     int epi;        // launch-time: finish a SwiGLU block in the store (see store_y)
     int fma_r;      // multiply-add path: row slots per wavefront
     const Q4Matrix *swi;   // launch-time: the up matrix of a one-launch SwiGLU block
@@ -1256,6 +1525,58 @@ bool plan_integer_m(Geometry &p, int M, int N, int K, const Knobs &k) {
     return true;
 }
 
+// The fp32 multiply-add kernel for 2 to 8 activation rows: 8 wavefronts of
+// two 4-row slots (16 lanes per row), one workgroup per CU (more only past
+// 64 rows per CU), the rows of a workgroup dealt to its row groups, and the
+// K-split the largest that still leaves every row group room for its rows
+// (or the one a caller fixed; then a workgroup takes no more rows than its
+// row groups hold).  x is staged in segments when M rows of it exceed the
+// LDS.
+constexpr int kFmW = 8, kFmR = 2, kFmLPR = 16;   // wavefronts, slots per wavefront, lanes per row
+// Chunk positions per lane and segment: past 8 for 7-8 rows of x the unrolled
+// body no longer fits the compiler's unrolling budget.
+constexpr int fm_jp_max(int M) { return M >= 7 ? 8 : 16; }
+
+bool plan_fm(Geometry &p, int M, int N, int K, const Knobs &k) {
+    const int C = K / 32;
+    constexpr int W = kFmW, R = kFmR, LPR = kFmLPR, SUBR = 64 / LPR;
+    if ((k.waves && k.waves != W) || (k.ksplit && W % k.ksplit != 0)) return false;
+    long grid = std::min<long>(kCUs, N);
+    long rpg = (N + grid - 1) / grid;
+    int S = k.ksplit ? k.ksplit : 4;
+    if (!k.ksplit)
+        while (S > 1 && (W / S) * SUBR * R < rpg) S /= 2;
+    const long cap = (long)(W / S) * SUBR * R;    // rows the row groups hold
+    if (rpg > cap) {
+        rpg = cap;
+        grid = (N + rpg - 1) / rpg;
+    }
+    const int comb = W * SUBR * R * M * 4;
+    int seg = std::min(C, (kLdsMax - comb) / (M * kFmStride * 4));
+    if (seg < C) seg = std::max(LPR * S, seg / (LPR * S) * (LPR * S));
+    const int part = (seg + S - 1) / S;
+    int JP = (part + LPR - 1) / LPR;
+    const int jmax = fm_jp_max(M);
+    JP = JP <= 2 ? 2 : (JP <= 4 ? 4 : (JP <= 8 ? 8 : 16));
+    if ((part + LPR - 1) / LPR > jmax) {        // at most jmax chunk positions per lane and segment
+        seg = jmax * LPR * S;
+        JP = jmax;
+    }
+    p.fm = true;
+    p.integer = false;
+    p.mp = M;
+    p.waves = W;
+    p.S = S;
+    p.LPR = LPR;
+    p.JP = JP;
+    p.grid = (int)grid;
+    p.rpg = (int)rpg;
+    p.rows_per_wave = SUBR * R;
+    p.seg_chunks = seg;
+    p.segments = (C + seg - 1) / seg;
+    return true;
+}
+
 // Chooses the launch geometry for a validated shape, with any knobs fixed;
 // *ok is cleared when the knobs cannot be met.
 Geometry plan_with(int M, int N, int K, const Knobs &k, bool *ok) {
@@ -1303,6 +1624,10 @@ Geometry plan_with(int M, int N, int K, const Knobs &k, bool *ok) {
     const long rows_per_wg = (long)p.rows_per_wave * (kWaves / p.S);
     p.grid = (int)((N + rows_per_wg - 1) / rows_per_wg);
     p.rpg = (int)std::min<long>(rows_per_wg, N);
+    if (M > 1 && k.path != Q4_PATH_INTEGER) {
+        if (!plan_fm(p, M, N, K, k)) *ok = false;
+        return p;
+    }
     if (k.path == Q4_PATH_FMA) {
         if (k.waves && k.waves != kWaves) *ok = false;
         return p;
@@ -1364,6 +1689,8 @@ int validate(int M, int N, int K, int g) {
 // LDS bytes a launch needs: the x segment plus, with a K-split, one partial
 // sum per (wavefront, row, m).
 size_t lds_bytes(const Geometry &p) {
+    if (p.fm)                   // x segment, partial sums
+        return (size_t)p.M * p.seg_chunks * kFmStride * 4 + (size_t)p.waves * p.rows_per_wave * p.M * 4;
     if (p.integer && p.M > 1)   // records, residual pool, partial sums, pool counter
         return (size_t)p.M * p.seg_chunks * kIW * 4 + (size_t)p.pool * 64 +
                (size_t)p.waves * p.rows_per_wave * p.mp * 4 + 16;
@@ -1473,6 +1800,49 @@ void dispatch_intm_mp(const Geometry &p, const float *x, const uint8_t *wq, cons
     }
 }
 
+template <int MX, int S, int JP>
+void launch_fm(const Geometry &p, const float *x, const uint8_t *wq, const uint16_t *scales,
+               const uint8_t *zeros, float *y, int N, int K, int gshift, hipStream_t st) {
+    hipLaunchKernelGGL((gemv_q4_fm_kernel<kFmW, MX, kFmR, kFmLPR, S, JP>), dim3(p.grid), dim3(kFmW * 64),
+                       lds_bytes(p), st, x, wq, scales, zeros, y, N, K, gshift, p.rpg, p.seg_chunks, p.epi);
+}
+
+template <int MX, int S>
+void dispatch_fm_jp(const Geometry &p, const float *x, const uint8_t *wq, const uint16_t *scales,
+                    const uint8_t *zeros, float *y, int N, int K, int gshift, hipStream_t st) {
+    switch (p.JP) {
+    case 2: launch_fm<MX, S, 2>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
+    case 4: launch_fm<MX, S, 4>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
+    case 8: launch_fm<MX, S, 8>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
+    default:
+        if constexpr (fm_jp_max(MX) >= 16) launch_fm<MX, S, 16>(p, x, wq, scales, zeros, y, N, K, gshift, st);
+        break;
+    }
+}
+
+template <int MX>
+void dispatch_fm_s(const Geometry &p, const float *x, const uint8_t *wq, const uint16_t *scales,
+                   const uint8_t *zeros, float *y, int N, int K, int gshift, hipStream_t st) {
+    switch (p.S) {
+    case 1: dispatch_fm_jp<MX, 1>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
+    case 2: dispatch_fm_jp<MX, 2>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
+    default: dispatch_fm_jp<MX, 4>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
+    }
+}
+
+void dispatch_fm(const Geometry &p, const float *x, const uint8_t *wq, const uint16_t *scales,
+                 const uint8_t *zeros, float *y, int M, int N, int K, int gshift, hipStream_t st) {
+    switch (M) {
+    case 2: dispatch_fm_s<2>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
+    case 3: dispatch_fm_s<3>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
+    case 4: dispatch_fm_s<4>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
+    case 5: dispatch_fm_s<5>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
+    case 6: dispatch_fm_s<6>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
+    case 7: dispatch_fm_s<7>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
+    default: dispatch_fm_s<8>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
+    }
+}
+
 void dispatch_intm(const Geometry &p, const float *x, const uint8_t *wq, const uint16_t *scales,
                    const uint8_t *zeros, float *y, int M, int N, int K, int gshift, hipStream_t st) {
     switch (p.mp) {
@@ -1501,7 +1871,7 @@ extern "C" int gemv_q4_geometry(int M, int N, int K, int group_size, int *grid, 
     if (v != Q4_OK) return v;
     const Geometry p = plan(M, N, K, group_size);
     if (grid) *grid = p.grid;
-    if (block) *block = p.integer ? p.waves * q4::kWave : kBlock;
+    if (block) *block = (p.integer || p.fm) ? p.waves * q4::kWave : kBlock;
     if (rows_per_wave) *rows_per_wave = p.rows_per_wave;
     if (lanes_per_row) *lanes_per_row = p.LPR;
     if (ksplit) *ksplit = p.S;
@@ -1558,6 +1928,10 @@ int launch_gemv_q4(const float *x, const uint8_t *wq, const uint16_t *scales, co
     p.swi = swi;
     const int gshift = group_size == 32 ? 0 : 2;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (p.fm) {
+        dispatch_fm(p, x, wq, scales, zeros, y, M, N, K, gshift, st);
+        return q4::launch_status();
+    }
     if (p.integer && M > 1) {
         dispatch_intm(p, x, wq, scales, zeros, y, M, N, K, gshift, st);
         return q4::launch_status();
@@ -1570,16 +1944,10 @@ int launch_gemv_q4(const float *x, const uint8_t *wq, const uint16_t *scales, co
         }
         return q4::launch_status();
     }
-    switch (M) {
-    case 1: dispatch_lpr<1>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
-    case 2: dispatch_lpr<2>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
-    case 3: dispatch_lpr<3>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
-    case 4: dispatch_lpr<4>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
-    case 5: dispatch_lpr<5>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
-    case 6: dispatch_lpr<6>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
-    case 7: dispatch_lpr<7>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
-    default: dispatch_lpr<8>(p, x, wq, scales, zeros, y, N, K, gshift, st); break;
-    }
+    // The half-precision multiply-add kernel: one activation row only (the
+    // planner sends 2 to 8 rows to the fp32 multiply-add or integer kernels).
+    if (M != 1) return Q4_EINVAL;
+    dispatch_lpr<1>(p, x, wq, scales, zeros, y, N, K, gshift, st);
     return q4::launch_status();
 }
 

@@ -20,10 +20,23 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
-// Sum over aligned groups of LPR lanes (16, 32 or 64); every lane of a group
-// gets its group's sum.
+// Sum over the 8 lanes of each half of a DPP row: the quad sums, then
+// row_half_mirror pairs the two quads.
+__device__ __forceinline__ float row8_sum(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+             0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+             0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+             0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+    return v;
+}
+
+// Sum over aligned groups of LPR lanes (8, 16, 32 or 64); every lane of a
+// group gets its group's sum.
 template <int LPR>
 __device__ __forceinline__ float group_sum(float v) {
+    if constexpr (LPR == 8) return row8_sum(v);
     v = row16_sum(v);
     if constexpr (LPR >= 32) v += __shfl_xor(v, 16);
     if constexpr (LPR >= 64) v += __shfl_xor(v, 32);

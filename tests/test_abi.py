@@ -149,25 +149,33 @@ def test_geometry_covers_every_row(shape):
     geo = q4.gemv_q4_geometry(shape.M, shape.N, shape.K, shape.g)
     lpr, S = geo["lanes_per_row"], geo["ksplit"]
     integer = q4.gemv_q4_path(shape.M, shape.N, shape.K, shape.g) == q4.Q4_PATH_INTEGER
+    fm = not integer and shape.M > 1      # the fp32 multiply-add kernel
     assert lpr in (16, 32, 64) and S in (1, 2, 4)
-    assert geo["block"] in ((256, 512, 1024) if integer else (256,))
+    assert geo["block"] in ((256, 512, 1024) if integer else ((512,) if fm else (256,)))
     waves = geo["block"] // 64
     rows_per_wg = geo["rows_per_wave"] * waves // S
     C = shape.K // 32
-    if integer:
+    if integer or fm:
         # each workgroup owns ceil(N / grid) rows, at most rows_per_wave per row group
         rpg = -(-shape.N // geo["grid"])
         assert rpg <= rows_per_wg and geo["grid"] * rpg >= shape.N > (geo["grid"] - 1) * rpg
-        seg = -(-C // geo["segments"])
-        if shape.M == 1:
-            assert geo["segments"] == 1 and C * 112 + waves * geo["rows_per_wave"] * 4 <= 64 * 1024
-            # a lane holds at most 3 chunk positions of its K slice
-            assert -(-C // S) <= 3 * 64
-        else:
-            # M rows of 112-byte chunk records per segment, within the CU's LDS
-            mp = 2 if shape.M <= 2 else (4 if shape.M <= 4 else 8)
-            assert shape.M * seg * 112 + waves * geo["rows_per_wave"] * mp * 4 <= 160 * 1024
-            assert -(-seg // S) <= 2 * 64
+    seg = -(-C // geo["segments"])
+    if integer and shape.M == 1:
+        # 144-byte records and 128 bytes of residual slots per chunk of the whole x
+        assert geo["segments"] == 1 and C * 272 + waves * geo["rows_per_wave"] * 4 <= 160 * 1024
+        # a lane holds at most 3 chunk positions of its K slice
+        assert -(-C // S) <= 3 * 64
+    elif integer:
+        # M rows of 144-byte records and pool slots per segment, within the CU's LDS
+        mp = 2 if shape.M <= 2 else (4 if shape.M <= 4 else 8)
+        assert shape.M * seg * 152 + waves * geo["rows_per_wave"] * mp * 4 <= 160 * 1024
+        assert -(-seg // S) <= 2 * 64
+    elif fm:
+        # M rows of 144-byte staged chunks per segment and the partial sums, within the LDS;
+        # at most 16 chunk positions per lane (8 for 7 and 8 rows)
+        assert shape.M * seg * 144 + waves * geo["rows_per_wave"] * shape.M * 4 <= 160 * 1024
+        part = -(-seg // S)
+        assert lpr == 16 and -(-part // 16) <= (8 if shape.M >= 7 else 16)
     else:
         assert geo["grid"] * rows_per_wg >= shape.N > (geo["grid"] - 1) * rows_per_wg
         seg = -(-C // geo["segments"])
@@ -180,10 +188,10 @@ PATHS = [
     (1, 14336, 4096, 128, 1), (1, 4096, 14336, 128, 1), (1, 65, 2048, 128, 1),
     (1, 1, 18688, 128, 1), (1, 1, 19200, 128, 1), (1, 4, 19328, 128, 0), (1, 2, 19264, 32, 1), (1, 896, 896, 32, 1), (1, 151936, 896, 32, 1),
     (1, 63, 2016, 32, 1), (1, 7, 1024, 32, 1), (1, 9, 512, 32, 0), (1, 9, 544, 32, 1),
-    (2, 14336, 4096, 128, 1), (8, 4096, 14336, 128, 1),
-    (4, 896, 896, 32, 0), (2, 64, 1024, 32, 0), (3, 4864, 896, 32, 0), (7, 100, 2048, 128, 1),
-    # x records of 2..4 rows that need segments take the multiply-add path
-    (4, 4096, 14336, 128, 0), (2, 4096, 14336, 128, 0), (2, 300, 8192, 128, 1),
+    # 2 to 8 activation rows take the fp32 multiply-add path (the integer one only on request)
+    (2, 14336, 4096, 128, 0), (8, 4096, 14336, 128, 0),
+    (4, 896, 896, 32, 0), (2, 64, 1024, 32, 0), (3, 4864, 896, 32, 0), (7, 100, 2048, 128, 0),
+    (4, 4096, 14336, 128, 0), (2, 4096, 14336, 128, 0), (2, 300, 8192, 128, 0),
 ]
 
 
@@ -246,6 +254,9 @@ def test_set_geometry_changes_the_plan(clean_geometry):
     (1, 64, 4096, 128, 1, 4, 8),         # ksplit not in {1, 2, 4}
     (1, 64, 4096, 128, 0, 8, 0),         # the multiply-add path has 4 wavefronts
     (4, 64, 4096, 128, 1, 16, 0),        # 2..4 rows use 8 wavefronts
+    (4, 64, 4096, 128, 0, 4, 0),         # so does the multiply-add path for 2..8 rows
+    (8, 64, 4096, 128, 0, 16, 0),
+    (2, 64, 1024, 32, 1, 0, 0),          # the integer path for several rows needs K > 1024
     (1, 64, 4096, 128, 2, 0, 0),         # no such path
     (1, 64, 100, 32, 0, 0, 0),           # invalid shape
 ])
