@@ -173,7 +173,7 @@ class Graph:
 
 def setup_stream(torch, q4, dev):
     s = wl.STREAM_SHAPE
-    seed = wl.config_seed(4)
+    seed = wl.workload_seed(4)
     x = torch.from_numpy(wl.make_x(seed, 1, s.K)).to(dev)
     mats = []
     t0 = time.time()
@@ -226,7 +226,7 @@ def _oracle_rate(budget_s: float, threads: int):
     import numpy as np
     import oracle
     s = wl.STREAM_SHAPE
-    seed = wl.config_seed(4)
+    seed = wl.workload_seed(4)
     x = wl.make_x(seed, 1, s.K)
     parts = np.array_split(np.arange(s.N, dtype=np.int64), threads)
     done, t_used, times = 0, 0.0, []
@@ -588,17 +588,17 @@ def run_configs(torch, q4, dev, W, two_pt: dict, floor: dict | None, cpu_s: floa
     HBM-streaming ones (distinct copies cycled past the Infinity Cache), each
     with its two-point per-launch statistics, GB/s, fraction of the 8 TB/s
     peak and cache class, and beside it the CPU oracle on bounded samples of
-    the same config (one thread and all threads).  configs[4]'s cells are the
-    headline's two-point cells and the single-launch read floor."""
+    the same workload (one thread and all threads).  The stream workload's
+    cells are the headline's two-point cells and the single-launch read floor."""
     import numpy as np
     gen = torch.Generator(device=dev)
-    gen.manual_seed(wl.config_seed(7))
+    gen.manual_seed(wl.workload_seed(7))
     cells = []
 
     def add(config, name, rec):
         rec = dict(rec, config=config, name=name)
         cells.append(rec)
-        log(f"config[{config}] {name:44s} {rec['kernel']:14s} {rec['us_per_launch']['median']:9.3f} us "
+        log(f"{config:14s} {name:44s} {rec['kernel']:14s} {rec['us_per_launch']['median']:9.3f} us "
             f"{rec['GBps_median']:8.1f} GB/s  {rec['cache_class']}")
 
     def q4_pass(x, mats, ys, g, reps=1):
@@ -619,25 +619,25 @@ def run_configs(torch, q4, dev, W, two_pt: dict, floor: dict | None, cpu_s: floa
         return q4.dequant_q4(m["wq"], m["scales"], m["zeros"], g, want_codes=False)[0]
 
     cpu = {}
-    # ---- configs[0]: one 896 x 896 g32 GEMV
+    # ---- one 896 x 896 g32 GEMV
     s = wl.SMALL_896
-    d = wl.make_q4_problem(wl.config_seed(0), s)
+    d = wl.make_q4_problem(wl.workload_seed(0), s)
     x = torch.from_numpy(d["x"]).to(dev)
     m = {k: torch.from_numpy(v).to(dev) for k, v in d.items() if k != "x"}
     y = [torch.empty((1, s.N), device=dev)]
     nb = wl.q4_weight_bytes(s.N, s.K, s.g)
-    add(0, "single 896x896 g32, one matrix looped", cell_record(
+    add("gemv-896", "single 896x896 g32, one matrix looped", cell_record(
         "gemv_q4", time_pass(torch, q4_pass(x, [m], y, s.g, 64), 64), nb, nb))
     w = dequant(m, s.g)
-    add(0, "single 896x896 fp32 control, one matrix looped", cell_record(
+    add("gemv-896", "single 896x896 fp32 control, one matrix looped", cell_record(
         "gemv_f32", time_pass(torch, f32_pass(x, [w], y, 64), 64), 4 * s.N * s.K, 4 * s.N * s.K))
     cpu_for_ = (lambda probs: cpu_for(probs, cpu_s)) if cpu_s else (lambda probs: None)
     cpu[0] = cpu_for_([(d["x"], d, s.g, np.arange(s.N))])
     del m, w
 
-    # ---- configs[1]: the seven decoder-layer GEMVs back to back
+    # ---- the seven decoder-layer GEMVs back to back
     shapes = wl.DECODER_LAYER
-    hosts = [wl.make_q4_problem(wl.config_seed(1), sh, index=i) for i, sh in enumerate(shapes)]
+    hosts = [wl.make_q4_problem(wl.workload_seed(1), sh, index=i) for i, sh in enumerate(shapes)]
     xs = [torch.from_numpy(h["x"]).to(dev) for h in hosts]
     layer = [{k: torch.from_numpy(v).to(dev) for k, v in h.items() if k != "x"} for h in hosts]
     ys = [torch.empty((1, sh.N), device=dev) for sh in shapes]
@@ -656,53 +656,53 @@ def run_configs(torch, q4, dev, W, two_pt: dict, floor: dict | None, cpu_s: floa
         return fn
 
     st = time_pass(torch, layer_pass([layer], reps=16), 16)
-    add(1, "decoder layer, 7 GEMVs g32, one layer looped", cell_record(
+    add("decoder-layer", "decoder layer, 7 GEMVs g32, one layer looped", cell_record(
         "gemv_q4 x7", st, lb, lb, unit="per layer"))
     copies = -(-(1 << 30) // lb)
     many = [layer] + [[{k: v.clone() for k, v in mm.items()} for mm in layer] for _ in range(copies - 1)]
     st = time_pass(torch, layer_pass(many), copies)
-    add(1, f"decoder layer, 7 GEMVs g32, {copies} layers cycled", cell_record(
+    add("decoder-layer", f"decoder layer, 7 GEMVs g32, {copies} layers cycled", cell_record(
         "gemv_q4 x7", st, lb, lb * copies, unit="per layer"))
     del many
     fl = [dequant(mm, 32) for mm in layer]
     st = time_pass(torch, layer_pass([fl], f32=True, reps=4), 4)
-    add(1, "decoder layer, 7 fp32 control GEMVs, one layer looped", cell_record(
+    add("decoder-layer", "decoder layer, 7 fp32 control GEMVs, one layer looped", cell_record(
         "gemv_f32 x7", st, fb, fb, unit="per layer"))
     fcopies = -(-(1 << 30) // fb)
     fmany = [fl] + [[w.clone() for w in fl] for _ in range(fcopies - 1)]
     st = time_pass(torch, layer_pass(fmany, f32=True), fcopies)
-    add(1, f"decoder layer, 7 fp32 control GEMVs, {fcopies} layers cycled", cell_record(
+    add("decoder-layer", f"decoder layer, 7 fp32 control GEMVs, {fcopies} layers cycled", cell_record(
         "gemv_f32 x7", st, fb, fb * fcopies, unit="per layer"))
     del fmany, fl, layer
     cpu[1] = cpu_for_([(h["x"], h, 32, np.arange(sh.N)) for h, sh in zip(hosts, shapes)])
     torch.cuda.empty_cache()
 
-    # ---- configs[2]: the LM head 896 -> 151936 g32
+    # ---- the LM head 896 -> 151936 g32
     s = wl.LM_HEAD
-    d = wl.make_q4_problem(wl.config_seed(2), s)
+    d = wl.make_q4_problem(wl.workload_seed(2), s)
     x = torch.from_numpy(d["x"]).to(dev)
     nb = wl.q4_weight_bytes(s.N, s.K, s.g)
     mats = dev_mats(torch, dev, {k: v for k, v in d.items() if k != "x"}, 8, gen)
     y = [torch.empty((1, s.N), device=dev) for _ in mats]
-    add(2, "LM head 896->151936 g32, one matrix looped", cell_record(
+    add("lm-head", "LM head 896->151936 g32, one matrix looped", cell_record(
         "gemv_q4", time_pass(torch, q4_pass(x, mats[:1], y[:1], s.g, 8), 8), nb, nb))
-    add(2, "LM head 896->151936 g32, 8 matrices rotated", cell_record(
+    add("lm-head", "LM head 896->151936 g32, 8 matrices rotated", cell_record(
         "gemv_q4", time_pass(torch, q4_pass(x, mats, y, s.g), 8), nb, 8 * nb))
     ws = [dequant(mats[0], s.g)]
     ws.append(ws[0].clone())
     fbytes = 4 * s.N * s.K
-    add(2, "LM head fp32 control, 2 matrices rotated", cell_record(
+    add("lm-head", "LM head fp32 control, 2 matrices rotated", cell_record(
         "gemv_f32", time_pass(torch, f32_pass(x, ws, y[:2]), 2), fbytes, 2 * fbytes))
     del mats, ws
     rng = np.random.default_rng(2)
     cpu[2] = cpu_for_([(d["x"], d, s.g, np.sort(rng.choice(s.N, 16384, replace=False)))])
     torch.cuda.empty_cache()
 
-    # ---- configs[3]: the 8B-class FFN pair at M = 1, 4, 8
+    # ---- the 8B-class FFN pair at M = 1, 4, 8
     probs = []
     for M in (1, 4, 8):
         for i, sh in enumerate(wl.ffn_8b(M)):
-            h = wl.make_q4_problem(wl.config_seed(3), sh, index=i)
+            h = wl.make_q4_problem(wl.workload_seed(3), sh, index=i)
             xx = torch.from_numpy(h["x"]).to(dev)
             mm = {k: torch.from_numpy(v).to(dev) for k, v in h.items() if k != "x"}
             yy = [torch.empty((M, sh.N), device=dev)]
@@ -710,13 +710,13 @@ def run_configs(torch, q4, dev, W, two_pt: dict, floor: dict | None, cpu_s: floa
             path = "integer" if q4.gemv_q4_path(M, sh.N, sh.K, sh.g) == q4.Q4_PATH_INTEGER else "multiply-add"
             st = time_pass(torch, q4_pass(xx, [mm], yy, sh.g, 8), 8)
             flops = 2 * M * sh.N * sh.K
-            add(3, f"{sh.label}, one matrix looped", cell_record(
+            add("ffn-8b", f"{sh.label}, one matrix looped", cell_record(
                 "gemv_q4", st, nb, nb, M=M, path=path,
                 TFLOPs=round(flops / st["median"] / 1e12, 2),
                 valu_frac_of_fp32_peak=round(flops / st["median"] / FP32_VECTOR_PEAK, 4)))
             if M == 1:
                 w = dequant(mm, sh.g)
-                add(3, f"{sh.label} fp32 control, one matrix looped", cell_record(
+                add("ffn-8b", f"{sh.label} fp32 control, one matrix looped", cell_record(
                     "gemv_f32", time_pass(torch, f32_pass(xx, [w], yy, 2), 2), 4 * sh.N * sh.K, 4 * sh.N * sh.K))
                 del w
             probs.append((h["x"], h, sh.g, np.arange(0, sh.N, max(1, sh.N // 512))))
@@ -724,7 +724,7 @@ def run_configs(torch, q4, dev, W, two_pt: dict, floor: dict | None, cpu_s: floa
     cpu[3] = cpu_for_(probs)
     torch.cuda.empty_cache()
 
-    # ---- configs[4]: the headline's cells
+    # ---- the headline's cells
     s = wl.STREAM_SHAPE
     nb = wl.q4_weight_bytes(s.N, s.K, s.g)
     names = {"gemv_q4": ("stream 4096x14336 g128, 32 matrices cycled", nb, wl.STREAM_MATRICES * nb),
@@ -737,9 +737,9 @@ def run_configs(torch, q4, dev, W, two_pt: dict, floor: dict | None, cpu_s: floa
         if not r:
             continue
         st = {q: (v * 1e-6 if v is not None and q != "n" else v) for q, v in r["per_launch_us"].items()}
-        add(4, name, cell_record(k, st, b, ws_))
+        add("stream", name, cell_record(k, st, b, ws_))
     if floor:
-        add(4, "read_reduce over 32 distinct 30.5 MB buffers (one launch each)",
+        add("stream", "read_reduce over 32 distinct 30.5 MB buffers (one launch each)",
             cell_record("read_reduce", floor["stats"], floor["bytes_per_launch"], floor["working_set_bytes"],
                         workgroups=floor["workgroups"]))
     return {"cells_cache_resident": [c for c in cells if c["cache_class"] != "hbm-streaming"],
@@ -796,7 +796,7 @@ def run_block_formats(torch, q4, dev, reps_target_s: float = 0.02, only=None) ->
     matrix 0, then timed by two-point differences of graph replays (median
     of three), per launch."""
     out = {}
-    seed = wl.config_seed(5)
+    seed = wl.workload_seed(5)
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed)
     for fmt, (code, e, bb, offs) in wl.BLOCK_FORMATS.items():
@@ -862,7 +862,7 @@ def run_scan(torch, q4, dev, reps_target_s: float = 0.02) -> dict:
     lookup as a GEMV: score[v] = lut[Q, 4D] . onehot(codes[v])), then timed by two-point
     differences of graph replays, per scan."""
     V, Q, D = wl.SCAN_VECTORS, wl.SCAN_QUERIES, wl.SCAN_DIM
-    seed = wl.config_seed(6)
+    seed = wl.workload_seed(6)
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed)
     n_corpora = 64
@@ -929,7 +929,7 @@ def run_ffn_rows(torch, q4, W, reps_target_s: float = 0.02) -> dict:
     against the fp32 vector peak)."""
     g = wl.STREAM_SHAPE.g
     dev = W["x"].device
-    seed = wl.config_seed(3)
+    seed = wl.workload_seed(3)
     out = {}
     for label, N, K in (("up 4096->14336", 14336, 4096), ("down 14336->4096", 4096, 14336)):
         G = K // g
@@ -1091,7 +1091,7 @@ def run_decoder_layer(torch, q4, dev, reps_target_s: float = 0.02) -> dict:
     distinct layers are device copies of it.  The fused q/k/v output is gated
     against gemv_f32 on the dequantised matrix; both passes are timed by
     two-point differences of graph replays (median of three), per layer."""
-    seed = wl.config_seed(1)
+    seed = wl.workload_seed(1)
     shapes = wl.DECODER_LAYER
     mats = [wl.make_q4_weights(seed, s.N, s.K, s.g, s.s_lo, s.s_hi, index=20 + i)
             for i, s in enumerate(shapes)]
@@ -1207,8 +1207,8 @@ def run_pmc_workload(args):
     torch.cuda.empty_cache()
     # every block format at the stream shape, 8 distinct matrices launched twice
     gen = torch.Generator(device=dev)
-    gen.manual_seed(wl.config_seed(5))
-    x = torch.from_numpy(wl.make_x(wl.config_seed(5), 1, s.K)).to(dev)
+    gen.manual_seed(wl.workload_seed(5))
+    x = torch.from_numpy(wl.make_x(wl.workload_seed(5), 1, s.K)).to(dev)
     y = torch.empty((1, s.N), dtype=torch.float32, device=dev)
     for fmt, (code, e, bb, offs) in wl.BLOCK_FORMATS.items():
         mats = []
@@ -1226,7 +1226,7 @@ def run_pmc_workload(args):
         del mats
     # the scan over 8 distinct corpora of the Refractometer workload
     V, Q, D = wl.SCAN_VECTORS, wl.SCAN_QUERIES, wl.SCAN_DIM
-    lut = torch.from_numpy(wl.make_scan_lut(wl.config_seed(6), Q, D)).to(dev)
+    lut = torch.from_numpy(wl.make_scan_lut(wl.workload_seed(6), Q, D)).to(dev)
     out = torch.empty((V, Q), dtype=torch.float32, device=dev)
     for _ in range(PMC_BLOCK_MATRICES):
         c = torch.randint(-2**31, 2**31 - 1, (V, D // 16), dtype=torch.int32, device=dev, generator=gen)

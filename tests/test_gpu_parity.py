@@ -48,11 +48,11 @@ def sample_rows(N, n, seed):
     return np.unique(np.r_[edge, mid]).astype(np.int64)
 
 
-# ---------------------------------------------------------------- configs
+# ---------------------------------------------------------------- workloads
 
 def test_config0_single_896():
     s = wl.SMALL_896
-    d = wl.make_q4_problem(wl.config_seed(0), s)
+    d = wl.make_q4_problem(wl.workload_seed(0), s)
     y = run_q4(dev(d), s.g)
     y_ref, b = oracle.gemv_q4(d["x"], d["wq"], d["scales"], d["zeros"], s.g)
     assert_within(y, y_ref, b, s.label)
@@ -61,9 +61,9 @@ def test_config0_single_896():
 def test_config1_fused_layer():
     """The decoder layer in four launches: q, k and v as one matrix whose rows
     are theirs one after another, o, the SwiGLU block of gate and up, down."""
-    mats = [wl.make_q4_weights(wl.config_seed(1), s.N, s.K, s.g, s.s_lo, s.s_hi, index=10 + i)
+    mats = [wl.make_q4_weights(wl.workload_seed(1), s.N, s.K, s.g, s.s_lo, s.s_hi, index=10 + i)
             for i, s in enumerate(wl.DECODER_LAYER)]
-    x = wl.make_x(wl.config_seed(1), 1, 896, index=10)
+    x = wl.make_x(wl.workload_seed(1), 1, 896, index=10)
     qkv = wl.fuse_rows(*mats[:3])
     assert qkv["wq"].shape == (896 + 128 + 128, 448)
     t = dev(dict(qkv, x=x))
@@ -87,7 +87,7 @@ def test_config1_fused_layer():
 
 def test_config1_decoder_layer():
     for i, s in enumerate(wl.DECODER_LAYER):
-        d = wl.make_q4_problem(wl.config_seed(1), s, index=i)
+        d = wl.make_q4_problem(wl.workload_seed(1), s, index=i)
         t = dev(d)
         y = run_q4(t, s.g)
         y_ref, b = oracle.gemv_q4(d["x"], d["wq"], d["scales"], d["zeros"], s.g)
@@ -102,7 +102,7 @@ def test_config1_decoder_layer():
 
 def test_config2_lm_head_sampled():
     s = wl.LM_HEAD
-    d = wl.make_q4_problem(wl.config_seed(2), s)
+    d = wl.make_q4_problem(wl.workload_seed(2), s)
     y = run_q4(dev(d), s.g)
     rows = sample_rows(s.N, 3000, 2)
     y_ref, b = oracle.gemv_q4(d["x"], d["wq"], d["scales"], d["zeros"], s.g, rows=rows)
@@ -112,7 +112,7 @@ def test_config2_lm_head_sampled():
 @pytest.mark.parametrize("M", [1, 4, 8])
 def test_config3_ffn_sampled(M):
     for i, s in enumerate(wl.ffn_8b(M)):
-        d = wl.make_q4_problem(wl.config_seed(3), s, index=i)
+        d = wl.make_q4_problem(wl.workload_seed(3), s, index=i)
         y = run_q4(dev(d), s.g)
         rows = sample_rows(s.N, 200, 3 + M)
         y_ref, b = oracle.gemv_q4(d["x"], d["wq"], d["scales"], d["zeros"], s.g, rows=rows)
@@ -121,7 +121,7 @@ def test_config3_ffn_sampled(M):
 
 def test_config4_stream_sampled():
     s = wl.STREAM_SHAPE
-    seed = wl.config_seed(4)
+    seed = wl.workload_seed(4)
     x = wl.make_x(seed, 1, s.K)
     xt = torch.from_numpy(x).to(DEV)
     for idx in (0, 13, 31):
@@ -590,7 +590,7 @@ def test_gemv_q4_random_shapes(M, N, K, g):
     assert_within(y, y_ref, b, f"M{M} N{N} K{K} g{g} path {q4.gemv_q4_path(M, N, K, g)}")
 
 
-# ---------------------------------------------------------------- the five configs, every row, tuned geometry
+# ---------------------------------------------------------------- the five workloads, every row, tuned geometry
 
 def _oracle_all_rows(x, d, g, threads=16):
     """Every row of the oracle's GEMV, rows split over host threads."""
@@ -603,11 +603,11 @@ def _oracle_all_rows(x, d, g, threads=16):
 
 
 def _config_cases():
-    cases = [("config0", wl.SMALL_896, wl.config_seed(0), 0)]
-    cases += [(f"config1 {s.label}", s, wl.config_seed(1), i) for i, s in enumerate(wl.DECODER_LAYER)]
-    cases += [("config2", wl.LM_HEAD, wl.config_seed(2), 0)]
-    cases += [(f"config3 {s.label}", s, wl.config_seed(3), i) for M in (1, 4, 8) for i, s in enumerate(wl.ffn_8b(M))]
-    cases += [("config4", wl.STREAM_SHAPE, wl.config_seed(4), 0)]
+    cases = [("config0", wl.SMALL_896, wl.workload_seed(0), 0)]
+    cases += [(f"config1 {s.label}", s, wl.workload_seed(1), i) for i, s in enumerate(wl.DECODER_LAYER)]
+    cases += [("config2", wl.LM_HEAD, wl.workload_seed(2), 0)]
+    cases += [(f"config3 {s.label}", s, wl.workload_seed(3), i) for M in (1, 4, 8) for i, s in enumerate(wl.ffn_8b(M))]
+    cases += [("config4", wl.STREAM_SHAPE, wl.workload_seed(4), 0)]
     return cases
 
 

@@ -92,8 +92,8 @@ STREAM_F32_MATRICES = 4       # distinct f32 control matrices cycled (939,524,09
 PROBE_BYTES = 2 * 1024**3     # read_reduce buffer for the measured HBM roofline
 
 
-def config_seed(config_index: int) -> int:
-    return 0x5EED0000 + config_index
+def workload_seed(index: int) -> int:
+    return 0x5EED0000 + index
 
 
 def _rng(seed: int, stream: int, index: int) -> np.random.Generator:
