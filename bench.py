@@ -632,7 +632,7 @@ def run_configs(torch, q4, dev, W, two_pt: dict, floor: dict | None, cpu_s: floa
     add("gemv-896", "single 896x896 fp32 control, one matrix looped", cell_record(
         "gemv_f32", time_pass(torch, f32_pass(x, [w], y, 64), 64), 4 * s.N * s.K, 4 * s.N * s.K))
     cpu_for_ = (lambda probs: cpu_for(probs, cpu_s)) if cpu_s else (lambda probs: None)
-    cpu[0] = cpu_for_([(d["x"], d, s.g, np.arange(s.N))])
+    cpu["gemv-896"] = cpu_for_([(d["x"], d, s.g, np.arange(s.N))])
     del m, w
 
     # ---- the seven decoder-layer GEMVs back to back
@@ -674,7 +674,7 @@ def run_configs(torch, q4, dev, W, two_pt: dict, floor: dict | None, cpu_s: floa
     add("decoder-layer", f"decoder layer, 7 fp32 control GEMVs, {fcopies} layers cycled", cell_record(
         "gemv_f32 x7", st, fb, fb * fcopies, unit="per layer"))
     del fmany, fl, layer
-    cpu[1] = cpu_for_([(h["x"], h, 32, np.arange(sh.N)) for h, sh in zip(hosts, shapes)])
+    cpu["decoder-layer"] = cpu_for_([(h["x"], h, 32, np.arange(sh.N)) for h, sh in zip(hosts, shapes)])
     torch.cuda.empty_cache()
 
     # ---- the LM head 896 -> 151936 g32
@@ -695,7 +695,7 @@ def run_configs(torch, q4, dev, W, two_pt: dict, floor: dict | None, cpu_s: floa
         "gemv_f32", time_pass(torch, f32_pass(x, ws, y[:2]), 2), fbytes, 2 * fbytes))
     del mats, ws
     rng = np.random.default_rng(2)
-    cpu[2] = cpu_for_([(d["x"], d, s.g, np.sort(rng.choice(s.N, 16384, replace=False)))])
+    cpu["lm-head"] = cpu_for_([(d["x"], d, s.g, np.sort(rng.choice(s.N, 16384, replace=False)))])
     torch.cuda.empty_cache()
 
     # ---- the 8B-class FFN pair at M = 1, 4, 8
@@ -721,7 +721,7 @@ def run_configs(torch, q4, dev, W, two_pt: dict, floor: dict | None, cpu_s: floa
                 del w
             probs.append((h["x"], h, sh.g, np.arange(0, sh.N, max(1, sh.N // 512))))
             del mm
-    cpu[3] = cpu_for_(probs)
+    cpu["ffn-8b"] = cpu_for_(probs)
     torch.cuda.empty_cache()
 
     # ---- the headline's cells
@@ -917,6 +917,7 @@ def run_scan(torch, q4, dev, reps_target_s: float = 0.02) -> dict:
 # ---------------------------------------------------------------- several activation rows
 
 FP32_VECTOR_PEAK = 157.3e12     # MI355X fp32 vector FLOP/s, AMD published
+SIMDS = 256 * 4                # MI355X: 256 CUs of 4 SIMDs
 
 
 def run_ffn_rows(torch, q4, W, reps_target_s: float = 0.02) -> dict:
@@ -1181,6 +1182,8 @@ def run_blocks_only(args):
 
 PMC_BLOCK_MATRICES = 8
 PMC_READ_KERNEL = "read_reduce_kernel<true>"   # read_reduce's (non-temporal) kernel
+PMC_FLOOR_GRID = 2048       # workgroups of the single-launch floor (its fastest in FLOOR_GRIDS)
+PMC_FFN_MATRICES = 8        # distinct matrices per FFN projection at M = 4 and 8
 
 
 def run_pmc_workload(args):
@@ -1204,6 +1207,30 @@ def run_pmc_workload(args):
         q4.gemv_f32(W["x"], w, out=y)
     torch.cuda.synchronize()
     del W
+    torch.cuda.empty_cache()
+    # the single-launch read floor: read_reduce over 32 distinct buffers of one
+    # stream matrix's bytes, one launch each
+    nf = wl.q4_weight_bytes(s.N, s.K, s.g) // 4
+    buf = torch.rand(wl.STREAM_MATRICES * nf, device=dev)
+    parts = torch.empty(PMC_FLOOR_GRID, device=dev)
+    for i in range(wl.STREAM_MATRICES):
+        q4.read_reduce(buf[i * nf:(i + 1) * nf], PMC_FLOOR_GRID, partials=parts)
+    torch.cuda.synchronize()
+    del buf
+    torch.cuda.empty_cache()
+    # 4 and 8 activation rows: each FFN projection over distinct matrices
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.workload_seed(3))
+    for M in (4, 8):
+        for i, sh in enumerate(wl.ffn_8b(M)):
+            h = wl.make_q4_problem(wl.workload_seed(3), sh, index=i)
+            xx = torch.from_numpy(h["x"]).to(dev)
+            mats = dev_mats(torch, dev, {k: v for k, v in h.items() if k != "x"}, PMC_FFN_MATRICES, gen)
+            y = torch.empty((M, sh.N), device=dev)
+            for m in mats:
+                q4.gemv_q4(xx, m["wq"], m["scales"], m["zeros"], sh.g, out=y)
+            torch.cuda.synchronize()
+            del mats
     torch.cuda.empty_cache()
     # every block format at the stream shape, 8 distinct matrices launched twice
     gen = torch.Generator(device=dev)
@@ -1247,10 +1274,80 @@ def _rows(pattern):
 
 def _kernel_short(name: str) -> str:
 
-    m = re.search(r"(gemv_q4(?:_int)?_kernel<[^>]*>|gemv_f32_kernel<[^>]*>|read_reduce_kernel(?:<[^>]*>)?|"
+    m = re.search(r"(gemv_q4(?:_int|_intm|_fm)?_kernel<[^>]*>|gemv_f32_kernel<[^>]*>|read_reduce_kernel(?:<[^>]*>)?|"
                   r"write_fill_kernel|copy_kernel|dequant_q4_kernel|gemv_blk_kernel<[^>]*>|"
                   r"dequant_blk_kernel<[^>]*>|scan2_kernel<[^>]*>|at::native::\w+|__amd_rocclr_\w+)", name)
     return m.group(1).replace("(anonymous namespace)::", "") if m else name.split("(")[0][:60]
+
+
+def _kernel_key(r: dict) -> str:
+    """Short kernel name, with the grid for read_reduce (whose 2 GiB
+    calibration probe and 30.5 MB floor dispatches share one kernel)."""
+    k = _kernel_short(r["Kernel_Name"])
+    return f"{k} grid {r['Grid_Size']}" if k.startswith("read_reduce") else k
+
+
+def _probe_key(mean: dict) -> str:
+    """The read_reduce dispatch group of the 2 GiB probe: the largest fetch."""
+    return max((k for k, c in mean if k.startswith(PMC_READ_KERNEL) and c == "FETCH_SIZE"),
+               key=lambda k: mean[(k, "FETCH_SIZE")])
+
+
+# Counters of the SQ/TA/TCC/GRBM summary, one rocprofv3 --pmc pass each
+# (per-block limits: 8 SQ, 4 TCC, 2 TA, 2 GRBM per pass).
+PMC_COUNTER_PASSES = (
+    "SQ_WAVES SQ_BUSY_CYCLES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY "
+    "SQ_INSTS_LDS SQ_INSTS_VMEM_RD",
+    "TA_BUSY_avr TA_BUFFER_READ_WAVEFRONTS_sum TCC_REQ_sum TCC_HIT_sum TCC_MISS_sum GRBM_GUI_ACTIVE "
+    "GRBM_COUNT",
+)
+
+
+def summarize_counters(dirs: list[str], name: str, command: str) -> str:
+    """rocprofv3 --pmc runs of --pmc-workload, one per PMC_COUNTER_PASSES entry
+    -> profiles/<name>.md: per kernel (and grid, for read_reduce), the mean
+    of every counter per dispatch, the mean dispatch duration under the
+    profiler, and the VALU issue figures derived from them."""
+    per, dur, grid = {}, {}, {}
+    for d in dirs:
+        for r in _rows(os.path.join(d, "**", "*counter_collection.csv")):
+            k = _kernel_key(r)
+            if not re.match(r"(gemv_q4|gemv_blk|read_reduce)", k):
+                continue
+            per.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            dur.setdefault(k, {})[(d, r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+            grid[k] = int(r["Grid_Size"]) // int(r["Workgroup_Size"])
+    lines = [f"# {name}: rocprofv3 counters per dispatch", "", f"command: `{command}`", "",
+             "Means over the dispatches of each kernel in one --pmc-workload run per pass "
+             "(the stream kernel: 64 launches over 32 matrices; the read floor: 32 buffers of "
+             "30.5 MB, one launch each; 4 and 8 rows: 8 matrices per FFN projection; the block "
+             "formats at the stream shape: 16 launches over 8 matrices each).  "
+             "Durations are those of the counter runs (serialised dispatches).", ""]
+    ctrs = [c for p in PMC_COUNTER_PASSES for c in p.split()]
+    for k in sorted(per):
+        c = {n: statistics.mean(v) for n, v in per[k].items()}
+        us = statistics.mean(dur[k].values()) / 1e3
+        lines += [f"## {k} ({grid[k]} workgroups)", "", "| counter | mean per dispatch |", "|---|---|"]
+        lines += [f"| {n} | {c[n]:.1f} |" for n in ctrs if n in c]
+        lines += ["", f"mean dispatch duration under the profiler: {us:.2f} us."]
+        if "SQ_INSTS_VALU" in c and "SQ_WAVES" in c and c["SQ_WAVES"]:
+            rate = c["SQ_INSTS_VALU"] / (SIMDS * us * 1e3)
+            lines.append(f"VALU: {c['SQ_INSTS_VALU'] / c['SQ_WAVES']:.0f} wavefront-instructions per "
+                         f"wavefront; {rate:.3f} issued per SIMD per ns over the dispatch "
+                         f"({SIMDS} SIMDs; one SIMD issues at most about 0.95 per ns with two or "
+                         "more wavefronts ready, 0.5 with one).")
+        if "SQ_ACTIVE_INST_VALU" in c and "SQ_INSTS_VALU" in c and c["SQ_INSTS_VALU"]:
+            lines.append(f"SQ_ACTIVE_INST_VALU / SQ_INSTS_VALU = "
+                         f"{c['SQ_ACTIVE_INST_VALU'] / c['SQ_INSTS_VALU']:.2f}.")
+        if "SQ_WAIT_INST_ANY" in c and "SQ_ACTIVE_INST_ANY" in c and c["SQ_ACTIVE_INST_ANY"]:
+            lines.append(f"SQ_WAIT_INST_ANY / SQ_ACTIVE_INST_ANY = "
+                         f"{c['SQ_WAIT_INST_ANY'] / c['SQ_ACTIVE_INST_ANY']:.2f}.")
+        if "GRBM_GUI_ACTIVE" in c:
+            lines.append(f"GRBM_GUI_ACTIVE {c['GRBM_GUI_ACTIVE']:.0f} cycles per dispatch.")
+        lines.append("")
+    out = os.path.join(PROFILES, name + ".md")
+    open(out, "w").write("\n".join(lines) + "\n")
+    return out
 
 
 def summarize_stats(d: str, name: str, command: str) -> str:
@@ -1264,7 +1361,7 @@ def summarize_stats(d: str, name: str, command: str) -> str:
                      f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} | "
                      f"{float(r['Percentage']):.2f} |")
     # per-kernel bandwidth lines for the workload the summary is named for
-    q = [r for r in stats if re.search(r"gemv_q4(_int)?_kernel", r["Name"])]
+    q = [r for r in stats if re.search(r"gemv_q4(_int)?_kernel<8, 64, 2, 4, 1, false, false", r["Name"])]
     if q and name.startswith("gemv_q4_stream"):
         avg = float(q[0]["AverageNs"]) * 1e-9
         b = wl.q4_weight_bytes(wl.STREAM_SHAPE.N, wl.STREAM_SHAPE.K, wl.STREAM_SHAPE.g)
@@ -1304,11 +1401,14 @@ def summarize_pmc(fetch_dir: str, write_dir: str, name: str, command: str) -> st
     for d, ctr in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
         for r in _rows(os.path.join(d, "**", "*counter_collection.csv")):
             if r["Counter_Name"] == ctr:
-                per.setdefault((_kernel_short(r["Kernel_Name"]), ctr), []).append(float(r["Counter_Value"]))
+                per.setdefault((_kernel_key(r), ctr), []).append(float(r["Counter_Value"]))
     mean = {k: statistics.mean(v) for k, v in per.items()}
-    fetch_factor = wl.PROBE_BYTES / (mean[(PMC_READ_KERNEL, "FETCH_SIZE")] * 1024)
+    probe = _probe_key(mean)
+    fetch_factor = wl.PROBE_BYTES / (mean[(probe, "FETCH_SIZE")] * 1024)
     write_factor = wl.PROBE_BYTES / (mean[("write_fill_kernel", "WRITE_SIZE")] * 1024)
-    qk = next(k for k, _ in mean if k.startswith("gemv_q4_"))
+    # the stream kernel: the gemv_q4 kernel with the most dispatches (2 x 32)
+    qk = max((k for k, c in mean if k.startswith("gemv_q4_") and c == "FETCH_SIZE"),
+             key=lambda k: len(per[(k, "FETCH_SIZE")]))
     s = wl.STREAM_SHAPE
     alg = wl.q4_weight_bytes(s.N, s.K, s.g)
     fetch_b = mean[(qk, "FETCH_SIZE")] * 1024 * fetch_factor
@@ -1325,7 +1425,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, name: str, command: str) -> st
     json.dump(summary, open(PMC_SUMMARY, "w"), indent=1)
     lines = [f"# {name}: HBM traffic from rocprofv3 counters", "", f"command: `{command}`", "",
              f"Calibration: read_reduce over {wl.PROBE_BYTES} B reads FETCH_SIZE "
-             f"{mean[(PMC_READ_KERNEL, 'FETCH_SIZE')]:.1f} KiB -> factor {fetch_factor:.4f}; "
+             f"{mean[(probe, 'FETCH_SIZE')]:.1f} KiB -> factor {fetch_factor:.4f}; "
              f"write_fill over {wl.PROBE_BYTES} B reads WRITE_SIZE "
              f"{mean[('write_fill_kernel', 'WRITE_SIZE')]:.1f} KiB -> factor {write_factor:.4f}.", "",
              "| kernel | counter | dispatches | mean KiB/dispatch | scaled bytes/dispatch |",
@@ -1362,7 +1462,9 @@ def summarize_pmc(fetch_dir: str, write_dir: str, name: str, command: str) -> st
 
 def summarize_profile(args):
     os.makedirs(PROFILES, exist_ok=True)
-    if args.summarize_write:
+    if args.summarize_counters:
+        log("wrote", summarize_counters([args.summarize] + args.summarize_counters, args.name, args.command))
+    elif args.summarize_write:
         log("wrote", summarize_pmc(args.summarize, args.summarize_write, args.name, args.command))
     else:
         log("wrote", summarize_stats(args.summarize, args.name, args.command))
@@ -1391,6 +1493,8 @@ def main(argv=None):
     ap.add_argument("--pmc-workload", action="store_true")
     ap.add_argument("--summarize", metavar="DIR", help="rocprofv3 CSV dir (stats, or FETCH_SIZE pmc)")
     ap.add_argument("--summarize-write", metavar="DIR", help="WRITE_SIZE pmc dir (with --summarize)")
+    ap.add_argument("--summarize-counters", metavar="DIR", nargs="+",
+                    help="further pmc dirs (with --summarize): the SQ/TA/TCC/GRBM counter summary")
     ap.add_argument("--name", default="summary")
     ap.add_argument("--command", default="")
     args = ap.parse_args(argv)
