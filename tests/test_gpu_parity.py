@@ -50,7 +50,7 @@ def sample_rows(N, n, seed):
 
 # ---------------------------------------------------------------- workloads
 
-def test_config0_single_896():
+def test_single_896():
     s = wl.SMALL_896
     d = wl.make_q4_problem(wl.workload_seed(0), s)
     y = run_q4(dev(d), s.g)
@@ -58,7 +58,7 @@ def test_config0_single_896():
     assert_within(y, y_ref, b, s.label)
 
 
-def test_config1_fused_layer():
+def test_fused_decoder_layer():
     """The decoder layer in four launches: q, k and v as one matrix whose rows
     are theirs one after another, o, the SwiGLU block of gate and up, down."""
     mats = [wl.make_q4_weights(wl.workload_seed(1), s.N, s.K, s.g, s.s_lo, s.s_hi, index=10 + i)
@@ -85,7 +85,7 @@ def test_config1_fused_layer():
     assert np.all(np.abs(ys.cpu().numpy().astype(np.float64) - ys_ref) <= tol)
 
 
-def test_config1_decoder_layer():
+def test_decoder_layer():
     for i, s in enumerate(wl.DECODER_LAYER):
         d = wl.make_q4_problem(wl.workload_seed(1), s, index=i)
         t = dev(d)
@@ -100,7 +100,7 @@ def test_config1_decoder_layer():
         assert_within(yf.cpu().numpy(), yf_ref, bf, "f32 " + s.label)
 
 
-def test_config2_lm_head_sampled():
+def test_lm_head_sampled():
     s = wl.LM_HEAD
     d = wl.make_q4_problem(wl.workload_seed(2), s)
     y = run_q4(dev(d), s.g)
@@ -110,7 +110,7 @@ def test_config2_lm_head_sampled():
 
 
 @pytest.mark.parametrize("M", [1, 4, 8])
-def test_config3_ffn_sampled(M):
+def test_ffn_sampled(M):
     for i, s in enumerate(wl.ffn_8b(M)):
         d = wl.make_q4_problem(wl.workload_seed(3), s, index=i)
         y = run_q4(dev(d), s.g)
@@ -119,7 +119,7 @@ def test_config3_ffn_sampled(M):
         assert_within(y[:, rows], y_ref, b, s.label)
 
 
-def test_config4_stream_sampled():
+def test_stream_sampled():
     s = wl.STREAM_SHAPE
     seed = wl.workload_seed(4)
     x = wl.make_x(seed, 1, s.K)
@@ -602,12 +602,12 @@ def _oracle_all_rows(x, d, g, threads=16):
     return np.concatenate([a for a, _ in res], axis=1), np.concatenate([b for _, b in res], axis=1)
 
 
-def _config_cases():
-    cases = [("config0", wl.SMALL_896, wl.workload_seed(0), 0)]
-    cases += [(f"config1 {s.label}", s, wl.workload_seed(1), i) for i, s in enumerate(wl.DECODER_LAYER)]
-    cases += [("config2", wl.LM_HEAD, wl.workload_seed(2), 0)]
-    cases += [(f"config3 {s.label}", s, wl.workload_seed(3), i) for M in (1, 4, 8) for i, s in enumerate(wl.ffn_8b(M))]
-    cases += [("config4", wl.STREAM_SHAPE, wl.workload_seed(4), 0)]
+def _workload_cases():
+    cases = [("gemv-896", wl.SMALL_896, wl.workload_seed(0), 0)]
+    cases += [(f"decoder-layer {s.label}", s, wl.workload_seed(1), i) for i, s in enumerate(wl.DECODER_LAYER)]
+    cases += [("lm-head", wl.LM_HEAD, wl.workload_seed(2), 0)]
+    cases += [(f"ffn-8b {s.label}", s, wl.workload_seed(3), i) for M in (1, 4, 8) for i, s in enumerate(wl.ffn_8b(M))]
+    cases += [("stream", wl.STREAM_SHAPE, wl.workload_seed(4), 0)]
     return cases
 
 
@@ -624,8 +624,8 @@ def tuned_profile():
     q4.scan2_set_config(0, 0, 0, 0)
 
 
-@pytest.mark.parametrize("case", _config_cases(), ids=lambda c: c[0].replace(" ", "_"))
-def test_config_every_row_tuned_geometry(case, tuned_profile):
+@pytest.mark.parametrize("case", _workload_cases(), ids=lambda c: c[0].replace(" ", "_"))
+def test_workload_every_row_tuned_geometry(case, tuned_profile):
     """Each configured GEMV in the geometry the benchmark runs (the tuned
     profile applied), every output row against the oracle at the plain bound."""
     label, s, seed, index = case
