@@ -1551,17 +1551,29 @@ bool plan_fm(Geometry &p, int M, int N, int K, const Knobs &k) {
         rpg = cap;
         grid = (N + rpg - 1) / rpg;
     }
+    // x segments: JP chunk positions per lane (a power of two from 2 to
+    // jmax) cover LPR * S * JP chunks; of the JP whose segments fit the LDS,
+    // the one with the fewest positions in all (a lane's steps, each a full
+    // pass of arithmetic whether its chunk exists or not), then the fewest
+    // segments.
     const int comb = W * SUBR * R * M * 4;
-    int seg = std::min(C, (kLdsMax - comb) / (M * kFmStride * 4));
-    if (seg < C) seg = std::max(LPR * S, seg / (LPR * S) * (LPR * S));
-    const int part = (seg + S - 1) / S;
-    int JP = (part + LPR - 1) / LPR;
+    const int fit = (kLdsMax - comb) / (M * kFmStride * 4);
     const int jmax = fm_jp_max(M);
-    JP = JP <= 2 ? 2 : (JP <= 4 ? 4 : (JP <= 8 ? 8 : 16));
-    if ((part + LPR - 1) / LPR > jmax) {        // at most jmax chunk positions per lane and segment
-        seg = jmax * LPR * S;
-        JP = jmax;
+    int seg = 0, JP = 0;
+    long best = -1;
+    for (int jp = 2; jp <= jmax; jp *= 2) {
+        const int sweep = LPR * S * jp;
+        if (sweep > fit && jp > 2) break;
+        const int sg = std::min(C, sweep);
+        const long steps = (long)(C + sg - 1) / sg * jp;   // every segment runs all jp positions
+        if (best < 0 || steps < best || (steps == best && sg > seg)) {
+            best = steps;
+            seg = sg;
+            JP = jp;
+        }
     }
+    if (seg > fit) seg = fit / (LPR * S) * (LPR * S);   // jp = 2 did not fit: a partial sweep
+    if (seg < LPR * S) seg = std::min(C, LPR * S);
     p.fm = true;
     p.integer = false;
     p.mp = M;

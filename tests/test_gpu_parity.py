@@ -150,6 +150,8 @@ RAGGED = [
     (7, 257, 4864, 32), (8, 67, 14336, 128), (1, 45, 14336, 128), (2, 300, 8192, 128),
     (1, 1, 16384, 128), (8, 9, 18432, 128), (1, 4097, 384, 128), (8, 1, 32, 32),
     (8, 100, 32768, 128), (3, 70, 32768, 32), (1, 33, 32768, 128),
+    # several x segments of the multiply-add kernel, the last one shorter
+    (3, 300, 14336, 128), (5, 200, 14336, 128), (4, 96, 14336, 32), (6, 50, 9216, 128),
 ]
 
 
