@@ -86,6 +86,35 @@ int gemv_q4(const float *x, const uint8_t *wq, const uint16_t *scales,
             const uint8_t *zeros, float *y, int M, int N, int K, int group_size,
             void *stream);
 
+/* gemv_q4 with a caller-provided device workspace, which lets the 2-8 row
+ * multiply-add path split K over workgroups where x would otherwise be
+ * staged in several LDS segments (a long K at several rows: each CU would
+ * read all of x for the weights of a few rows).  The workgroups then write
+ * partial sums into the workspace and a second launch on the same stream adds
+ * them, in a fixed order, into y.  Same computation, rules and errors as
+ * gemv_q4 (gerbil "WGSL Kernel Reference", section 3 MatMulInt4); the result
+ * may differ from gemv_q4's in the last bits (another summation order), both
+ * within the stated bound.
+ *   workspace        device memory, 16-byte aligned, not overlapping any
+ *                    argument; NULL, or fewer bytes than
+ *                    gemv_q4_workspace_size reports, runs gemv_q4's plan.
+ *                    Its contents need no initialisation and are
+ *                    meaningless after the call.  The caller owns it; the
+ *                    library keeps no pointer to it after the call (a graph
+ *                    that captured the call keeps using it when replayed).
+ *   workspace_bytes  its size in bytes.
+ * Calls that use the same workspace must not overlap in time (stream order
+ * serialises calls on one stream).  Q4_EALIGN for a misaligned workspace. */
+int gemv_q4_ws(const float *x, const uint8_t *wq, const uint16_t *scales,
+               const uint8_t *zeros, float *y, int M, int N, int K, int group_size,
+               void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes gemv_q4_ws uses for a shape: 4 * ks * M * N (ks the
+ * workgroups splitting K, 2 to 8) where it splits K, 0 where it does not.
+ * Host-only; launches nothing and needs no device.  Q4_EINVAL for an invalid
+ * shape, Q4_ENULL for a NULL bytes. */
+int gemv_q4_workspace_size(int M, int N, int K, int group_size, size_t *bytes);
+
 /* SwiGLU block of a decoder layer on int4 weights: the gate and up
  * projections, each a gemv_q4 of the same x, combined as
  *   y[m, n] = silu(g[m, n]) * u[m, n],   silu(v) = v / (1 + e^-v)

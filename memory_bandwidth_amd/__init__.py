@@ -26,7 +26,7 @@ Q4_OK, Q4_EINVAL, Q4_ENULL, Q4_EALIGN, Q4_EDEVICE, Q4_ELAUNCH = 0, -1, -2, -3, -
 
 # Exported C symbols, in the order include/q4gemv.h, include/q4blocks.h and
 # include/q4scan.h declare them.
-EXPORTS = ("gemv_q4", "gemv_q4_swiglu", "gemv_f32", "dequant_q4", "read_reduce",
+EXPORTS = ("gemv_q4", "gemv_q4_ws", "gemv_q4_workspace_size", "gemv_q4_swiglu", "gemv_f32", "dequant_q4", "read_reduce",
            "read_reduce_passes", "copy_vec4", "write_fill",
            "gemv_q4_geometry", "gemv_q4_path", "q4_strerror", "q4_abi_version",
            "gemv_q4_set_geometry", "gemv_q4_clear_geometry",
@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     L.gemv_q4.argtypes = [P, P, P, P, P, I, I, I, I, P]
+    L.gemv_q4_ws.argtypes = [P, P, P, P, P, I, I, I, I, P, Z, P]
+    L.gemv_q4_workspace_size.argtypes = [I, I, I, I, ctypes.POINTER(Z)]
     L.gemv_q4_swiglu.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, P]
     L.gemv_f32.argtypes = [P, P, P, I, I, I, P]
     L.dequant_q4.argtypes = [P, P, P, P, P, I, I, I, P]
@@ -83,7 +85,7 @@ def lib() -> ctypes.CDLL:
     L.q4_strerror.argtypes = [I]
     L.q4_strerror.restype = ctypes.c_char_p
     L.q4_abi_version.argtypes = []
-    for f in ("gemv_q4", "gemv_q4_swiglu", "gemv_f32", "dequant_q4", "read_reduce",
+    for f in ("gemv_q4", "gemv_q4_ws", "gemv_q4_workspace_size", "gemv_q4_swiglu", "gemv_f32", "dequant_q4", "read_reduce",
               "read_reduce_passes", "copy_vec4", "write_fill", "gemv_q4_geometry", "gemv_q4_path", "q4_abi_version",
               "gemv_q4_set_geometry", "gemv_q4_clear_geometry", "block_geometry", "gemv_block",
               "dequant_block", "gemv_block_set_config", "gemv_block_config", "scan2",
@@ -153,13 +155,35 @@ def _out(out: torch.Tensor | None, M: int, N: int, dev: torch.device) -> torch.T
     return out
 
 
+def gemv_q4_workspace_size(M: int, N: int, K: int, group_size: int) -> int:
+    """Workspace bytes with which gemv_q4_ws may split K over workgroups (0: none needed)."""
+    n = ctypes.c_size_t()
+    _check("gemv_q4_workspace_size", lib().gemv_q4_workspace_size(M, N, K, group_size, ctypes.byref(n)))
+    return n.value
+
+
 def gemv_q4(x: torch.Tensor, wq: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
-            group_size: int, out: torch.Tensor | None = None) -> torch.Tensor:
-    """y[M, N] = x[M, K] . dequant(W_q[N, K])^T on the current stream."""
+            group_size: int, out: torch.Tensor | None = None,
+            workspace: torch.Tensor | bool | None = None) -> torch.Tensor:
+    """y[M, N] = x[M, K] . dequant(W_q[N, K])^T on the current stream.
+
+    workspace: None takes one from torch's allocator when the shape can use
+    it (gemv_q4_ws); a uint8 tensor on x's device is used as given; False
+    calls gemv_q4 without one."""
     M, N, K, g = _q4_operands(x, wq, scales, zeros, group_size)
     out = _out(out, M, N, x.device)
-    _check("gemv_q4", lib().gemv_q4(_ptr(x), _ptr(wq), _ptr(scales), _ptr(zeros), _ptr(out),
-                                    M, N, K, g, _stream(x.device)))
+    if workspace is False:
+        _check("gemv_q4", lib().gemv_q4(_ptr(x), _ptr(wq), _ptr(scales), _ptr(zeros), _ptr(out),
+                                        M, N, K, g, _stream(x.device)))
+        return out
+    if workspace is None or workspace is True:
+        n = gemv_q4_workspace_size(M, N, K, g)
+        workspace = torch.empty(n, dtype=torch.uint8, device=x.device) if n else None
+    else:
+        _need(workspace, "workspace", (torch.uint8,), x.device)
+    wp, wn = (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
+    _check("gemv_q4_ws", lib().gemv_q4_ws(_ptr(x), _ptr(wq), _ptr(scales), _ptr(zeros), _ptr(out),
+                                          M, N, K, g, wp, wn, _stream(x.device)))
     return out
 
 

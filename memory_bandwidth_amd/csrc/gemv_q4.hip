@@ -1148,7 +1148,8 @@ template <int W, int MX, int R, int LPR, int S, int JP, int PD = 2, bool XPD = (
 __global__ __launch_bounds__(W * 64) void gemv_q4_fm_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ wq,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
-    float *__restrict__ y, int N, int K, int gshift, int rpg, int seg_chunks, int epi) {
+    float *__restrict__ y, int N, int K, int gshift, int rpg, int seg_chunks, int epi,
+    float *__restrict__ part, int KS, int kpart) {
     constexpr int SUBR = 64 / LPR;             // rows one load instruction covers (a slot)
     constexpr int NG = W / S;                  // row groups per workgroup
     // float4 of one x row one thread loads ahead of the weights: the first
@@ -1160,7 +1161,7 @@ __global__ __launch_bounds__(W * 64) void gemv_q4_fm_kernel(
     // every argument in registers at once: one round trip for the kernel
     // arguments instead of one per use site
     asm volatile("" ::"s"(x), "s"(wq), "s"(scales), "s"(zeros), "s"(y), "s"(N), "s"(K), "s"(gshift),
-                 "s"(rpg), "s"(seg_chunks), "s"(epi));
+                 "s"(rpg), "s"(seg_chunks), "s"(epi), "s"(part), "s"(KS), "s"(kpart));
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
@@ -1170,8 +1171,13 @@ __global__ __launch_bounds__(W * 64) void gemv_q4_fm_kernel(
     const int G = K >> (gshift + 5);
     const int ZB = (G + 1) >> 1;
     const int RB = K >> 1;
+    // KS workgroups may split the K range of one block of rpg rows: this one
+    // takes chunks [kc0, kc1) of the rows from rb * rpg, and with KS > 1
+    // writes partial sums that fm_sum_parts adds.
+    const int rb = (int)blockIdx.x / KS, kb = (int)blockIdx.x - rb * KS;
+    const int kc0 = kb * kpart, kc1 = min(C, kc0 + kpart);
     const int gq = rpg / NG, grem = rpg - gq * NG;
-    const int gstart = blockIdx.x * rpg + rg * gq + min(rg, grem);
+    const int gstart = rb * rpg + rg * gq + min(rg, grem);
     const int nrows = max(0, min(gq + (rg < grem ? 1 : 0), N - gstart));   // rows of this group, <= SUBR R
     const int rbase = min(gstart, N - 1);
     const uint32_t rows_left = (uint32_t)(N - rbase);
@@ -1190,8 +1196,8 @@ __global__ __launch_bounds__(W * 64) void gemv_q4_fm_kernel(
 #pragma unroll
         for (int m = 0; m < MX; ++m) acc[r][m] = 0.f;
 
-    for (int seg0 = 0; seg0 < C; seg0 += seg_chunks) {
-        const int segC = min(seg_chunks, C - seg0);
+    for (int seg0 = kc0; seg0 < kc1; seg0 += seg_chunks) {
+        const int segC = min(seg_chunks, kc1 - seg0);
         const int part = (segC + S - 1) / S;
         const int lo = seg0 + ks * part;
         const int hi = min(seg0 + segC, lo + part);
@@ -1332,7 +1338,7 @@ __global__ __launch_bounds__(W * 64) void gemv_q4_fm_kernel(
                 }
             }
         }
-        if (seg0 + seg_chunks < C) __syncthreads();   // x segment fully read before the next overwrites it
+        if (seg0 + seg_chunks < kc1) __syncthreads();   // x segment fully read before the next overwrites it
     }
 
     // Each slot's sum over its LPR lanes; lane 0 of the group holds it.
@@ -1340,6 +1346,14 @@ __global__ __launch_bounds__(W * 64) void gemv_q4_fm_kernel(
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int m = 0; m < MX; ++m) acc[r][m] = q4::group_sum<LPR>(acc[r][m]);
+    // A row's sum over this workgroup's K range: the output itself, or (K
+    // split over KS workgroups) this workgroup's partial sum, [kb][m][row].
+    auto emit = [&](int m, int row, float v) {
+        if (KS == 1)
+            store_y(y, (size_t)m * N + row, v, epi);
+        else
+            part[((size_t)kb * MX + m) * N + row] = v;
+    };
     if (S == 1) {
         if (li == 0) {
 #pragma unroll
@@ -1347,8 +1361,7 @@ __global__ __launch_bounds__(W * 64) void gemv_q4_fm_kernel(
                 const int rr = SUBR * r + sub;
                 if (rr < nrows)
 #pragma unroll
-                    for (int m = 0; m < MX; ++m)
-                        store_y(y, (size_t)m * N + gstart + rr, acc[r][m], epi);
+                    for (int m = 0; m < MX; ++m) emit(m, gstart + rr, acc[r][m]);
             }
         }
         return;
@@ -1369,11 +1382,23 @@ __global__ __launch_bounds__(W * 64) void gemv_q4_fm_kernel(
                 for (int m = 0; m < MX; ++m) {
                     float v = acc[r][m];
                     for (int u = 1; u < S; ++u) v += comb[((wave + u) * SUBR * R + SUBR * r + sub) * MX + m];
-                    store_y(y, (size_t)m * N + gstart + rr, v, epi);
+                    emit(m, gstart + rr, v);
                 }
             }
         }
     }
+}
+
+// The second launch of a K split over workgroups: every output is the sum of
+// its KS partial sums, added in workgroup order (the result does not depend
+// on which workgroup finished first), then stored as gemv_q4_fm_kernel would.
+__global__ __launch_bounds__(256) void fm_sum_parts(float *__restrict__ y, const float *__restrict__ part,
+                                                   int MN, int KS, int epi) {
+    const int i = (int)blockIdx.x * 256 + (int)threadIdx.x;
+    if (i >= MN) return;
+    float v = 0.f;
+    for (int k = 0; k < KS; ++k) v += part[(size_t)k * MN + i];
+    store_y(y, (size_t)i, v, epi);
 }
 
 // One int4 matrix of a call.
@@ -1393,7 +1418,10 @@ struct Geometry {
     bool fm;        // M > 1: fp32 multiply-add on exactly dequantised weights (gemv_q4_fm_kernel)
     int epi;        // launch-time: finish a SwiGLU block in the store (see store_y)
     int fma_r;      // multiply-add path: row slots per wavefront
+    int ks_wg;      // fm: workgroups splitting one row block's K range (partial sums in a workspace)
+    int kpart;      // fm: chunks of K per workgroup
     const Q4Matrix *swi;   // launch-time: the up matrix of a one-launch SwiGLU block
+    float *work;           // launch-time: the workspace of a K split over workgroups
 };
 
 constexpr int kCUs = 256;   // compute units of an MI355X
@@ -1537,29 +1565,18 @@ constexpr int kFmW = 8, kFmR = 2, kFmLPR = 16;   // wavefronts, slots per wavefr
 // body no longer fits the compiler's unrolling budget.
 constexpr int fm_jp_max(int M) { return M >= 7 ? 8 : 16; }
 
-bool plan_fm(Geometry &p, int M, int N, int K, const Knobs &k) {
-    const int C = K / 32;
+// Segments of x for a K range of C chunks: JP chunk positions per lane (a
+// power of two from 2 to jmax) cover LPR * S * JP chunks; of the JP whose
+// segments fit the LDS, the one with the fewest positions in all (a lane's
+// steps, each a full pass of arithmetic whether its chunk exists or not),
+// then the fewest segments.
+void fm_segments(int M, int C, int S, int &seg, int &JP) {
     constexpr int W = kFmW, R = kFmR, LPR = kFmLPR, SUBR = 64 / LPR;
-    if ((k.waves && k.waves != W) || (k.ksplit && W % k.ksplit != 0)) return false;
-    long grid = std::min<long>(kCUs, N);
-    long rpg = (N + grid - 1) / grid;
-    int S = k.ksplit ? k.ksplit : 4;
-    if (!k.ksplit)
-        while (S > 1 && (W / S) * SUBR * R < rpg) S /= 2;
-    const long cap = (long)(W / S) * SUBR * R;    // rows the row groups hold
-    if (rpg > cap) {
-        rpg = cap;
-        grid = (N + rpg - 1) / rpg;
-    }
-    // x segments: JP chunk positions per lane (a power of two from 2 to
-    // jmax) cover LPR * S * JP chunks; of the JP whose segments fit the LDS,
-    // the one with the fewest positions in all (a lane's steps, each a full
-    // pass of arithmetic whether its chunk exists or not), then the fewest
-    // segments.
     const int comb = W * SUBR * R * M * 4;
     const int fit = (kLdsMax - comb) / (M * kFmStride * 4);
     const int jmax = fm_jp_max(M);
-    int seg = 0, JP = 0;
+    seg = 0;
+    JP = 0;
     long best = -1;
     for (int jp = 2; jp <= jmax; jp *= 2) {
         const int sweep = LPR * S * jp;
@@ -1574,24 +1591,66 @@ bool plan_fm(Geometry &p, int M, int N, int K, const Knobs &k) {
     }
     if (seg > fit) seg = fit / (LPR * S) * (LPR * S);   // jp = 2 did not fit: a partial sweep
     if (seg < LPR * S) seg = std::min(C, LPR * S);
-    p.fm = true;
-    p.integer = false;
-    p.mp = M;
-    p.waves = W;
-    p.S = S;
-    p.LPR = LPR;
-    p.JP = JP;
-    p.grid = (int)grid;
-    p.rpg = (int)rpg;
-    p.rows_per_wave = SUBR * R;
-    p.seg_chunks = seg;
-    p.segments = (C + seg - 1) / seg;
-    return true;
+}
+
+// split: a workspace is available for a K split over workgroups.  It is
+// taken when x would otherwise be staged in several segments (long K at
+// several rows: every CU would read all of x for a few rows' weights):
+// KS workgroups per block of rows, each over a KS-th of K, KS doubling while
+// the blocks still fill half their CUs' row slots and every part keeps at
+// least one lane sweep (measured: 8 rows of 14336 -> 4096, 27.2 -> 23.6 us
+// with the partial sums' own launch; 2 rows, one segment, 11.6 -> 13.3).
+bool plan_fm(Geometry &p, int M, int N, int K, const Knobs &k, bool split = false) {
+    const int C = K / 32;
+    constexpr int W = kFmW, R = kFmR, LPR = kFmLPR, SUBR = 64 / LPR;
+    constexpr int slots = W * SUBR * R;           // rows one workgroup holds
+    if ((k.waves && k.waves != W) || (k.ksplit && W % k.ksplit != 0)) return false;
+    int KS = 1;
+    for (int pass = 0; pass < 2; ++pass) {
+        long blocks = std::max<long>(1, std::min<long>(kCUs / KS, N));
+        long rpg = (N + blocks - 1) / blocks;
+        int S = k.ksplit ? k.ksplit : 4;
+        if (!k.ksplit)
+            while (S > 1 && (W / S) * SUBR * R < rpg) S /= 2;
+        const long cap = (long)(W / S) * SUBR * R;    // rows the row groups hold
+        if (rpg > cap) rpg = cap;
+        blocks = (N + rpg - 1) / rpg;
+        const int kpart = (C + KS - 1) / KS;
+        int seg, JP;
+        fm_segments(M, kpart, S, seg, JP);
+        if (pass == 0 && split && seg < C) {
+            // several segments unsplit: split K over workgroups and plan again
+            while (KS < 8 && (long)N * 2 * KS <= (long)kCUs * slots && C >= 2 * KS * LPR * S) KS *= 2;
+            if (KS > 1) continue;
+        }
+        p.fm = true;
+        p.integer = false;
+        p.mp = M;
+        p.waves = W;
+        p.S = S;
+        p.LPR = LPR;
+        p.JP = JP;
+        p.ks_wg = KS;
+        p.kpart = kpart;
+        p.grid = (int)(blocks * KS);
+        p.rpg = (int)rpg;
+        p.rows_per_wave = SUBR * R;
+        p.seg_chunks = seg;
+        p.segments = (kpart + seg - 1) / seg;
+        return true;
+    }
+    return false;
+}
+
+// Workspace bytes a launch needs: KS partial sums per output of a K split
+// over workgroups, none otherwise.
+size_t fm_work_bytes(const Geometry &p, int N) {
+    return p.fm && p.ks_wg > 1 ? (size_t)p.ks_wg * p.M * N * sizeof(float) : 0;
 }
 
 // Chooses the launch geometry for a validated shape, with any knobs fixed;
 // *ok is cleared when the knobs cannot be met.
-Geometry plan_with(int M, int N, int K, const Knobs &k, bool *ok) {
+Geometry plan_with(int M, int N, int K, const Knobs &k, bool *ok, bool split = false) {
     Geometry p{};
     p.M = M;
     const int C = K / 32;
@@ -1637,7 +1696,7 @@ Geometry plan_with(int M, int N, int K, const Knobs &k, bool *ok) {
     p.grid = (int)((N + rows_per_wg - 1) / rows_per_wg);
     p.rpg = (int)std::min<long>(rows_per_wg, N);
     if (M > 1 && k.path != Q4_PATH_INTEGER) {
-        if (!plan_fm(p, M, N, K, k)) *ok = false;
+        if (!plan_fm(p, M, N, K, k, split)) *ok = false;
         return p;
     }
     if (k.path == Q4_PATH_FMA) {
@@ -1663,7 +1722,7 @@ int g_n_over = 0;
 // never half of one.
 std::shared_mutex g_over_mutex;
 
-Geometry plan(int M, int N, int K, int g) {
+Geometry plan(int M, int N, int K, int g, bool split = false) {
     Knobs k;
     bool found = false;
     {
@@ -1679,11 +1738,11 @@ Geometry plan(int M, int N, int K, int g) {
     }
     if (found) {
         bool ok = true;
-        const Geometry p = plan_with(M, N, K, k, &ok);
+        const Geometry p = plan_with(M, N, K, k, &ok, split);
         if (ok) return p;
     }
     bool ok = true;
-    return plan_with(M, N, K, Knobs{}, &ok);
+    return plan_with(M, N, K, Knobs{}, &ok, split);
 }
 
 // Longest row a call accepts: every per-lane and per-wavefront byte offset
@@ -1816,7 +1875,12 @@ template <int MX, int S, int JP>
 void launch_fm(const Geometry &p, const float *x, const uint8_t *wq, const uint16_t *scales,
                const uint8_t *zeros, float *y, int N, int K, int gshift, hipStream_t st) {
     hipLaunchKernelGGL((gemv_q4_fm_kernel<kFmW, MX, kFmR, kFmLPR, S, JP>), dim3(p.grid), dim3(kFmW * 64),
-                       lds_bytes(p), st, x, wq, scales, zeros, y, N, K, gshift, p.rpg, p.seg_chunks, p.epi);
+                       lds_bytes(p), st, x, wq, scales, zeros, y, N, K, gshift, p.rpg, p.seg_chunks, p.epi,
+                       p.work, p.ks_wg, p.kpart);
+    if (p.ks_wg > 1) {
+        const int MN = MX * N;   // the split is planned only for N * KS <= 8192
+        hipLaunchKernelGGL(fm_sum_parts, dim3((MN + 255) / 256), dim3(256), 0, st, y, p.work, MN, p.ks_wg, p.epi);
+    }
 }
 
 template <int MX, int S>
@@ -1934,10 +1998,12 @@ namespace {
 // Launches one GEMV of a validated, checked call (see gemv_q4, gemv_q4_swiglu).
 int launch_gemv_q4(const float *x, const uint8_t *wq, const uint16_t *scales, const uint8_t *zeros,
                    float *y, int M, int N, int K, int group_size, int epi, void *stream,
-                   const Q4Matrix *swi = nullptr) {
-    Geometry p = plan(M, N, K, group_size);
+                   const Q4Matrix *swi = nullptr, float *work = nullptr, size_t work_bytes = 0) {
+    Geometry p = plan(M, N, K, group_size, work != nullptr);
+    if (fm_work_bytes(p, N) > work_bytes) p = plan(M, N, K, group_size, false);
     p.epi = epi;
     p.swi = swi;
+    p.work = work;
     const int gshift = group_size == 32 ? 0 : 2;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (p.fm) {
@@ -1985,6 +2051,30 @@ extern "C" int gemv_q4(const float *x, const uint8_t *wq, const uint16_t *scales
     const int dev = q4::check_device();
     if (dev != Q4_OK) return dev;
     return launch_gemv_q4(x, wq, scales, zeros, y, M, N, K, group_size, 0, stream);
+}
+
+extern "C" int gemv_q4_workspace_size(int M, int N, int K, int group_size, size_t *bytes) {
+    const int v = validate(M, N, K, group_size);
+    if (v != Q4_OK) return v;
+    if (!bytes) return Q4_ENULL;
+    *bytes = N == 0 ? 0 : fm_work_bytes(plan(M, N, K, group_size, true), N);
+    return Q4_OK;
+}
+
+extern "C" int gemv_q4_ws(const float *x, const uint8_t *wq, const uint16_t *scales,
+                          const uint8_t *zeros, float *y, int M, int N, int K, int group_size,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    const int v = validate(M, N, K, group_size);
+    if (v != Q4_OK) return v;
+    if (N == 0) return Q4_OK;
+    const int a = check_q4_args(x, wq, scales, zeros, y);
+    if (a != Q4_OK) return a;
+    if (workspace && !q4::aligned(workspace, 16)) return Q4_EALIGN;
+    const int dev = q4::check_device();
+    if (dev != Q4_OK) return dev;
+    return launch_gemv_q4(x, wq, scales, zeros, y, M, N, K, group_size, 0, stream, nullptr,
+                          workspace ? static_cast<float *>(workspace) : nullptr,
+                          workspace ? workspace_bytes : 0);
 }
 
 extern "C" int gemv_q4_swiglu(const float *x, const uint8_t *wq_gate, const uint16_t *scales_gate,

@@ -233,6 +233,32 @@ def clean_geometry():
     q4.gemv_q4_clear_geometry()
 
 
+@pytest.mark.parametrize("M,N,K,g,split", [
+    (8, 4096, 14336, 128, True), (4, 4096, 14336, 128, True), (3, 300, 14336, 128, True),
+    (2, 4096, 14336, 128, False),     # x in one segment: no split
+    (8, 14336, 4096, 128, False),     # likewise
+    (1, 4096, 14336, 128, False),     # one row: the integer path
+    (8, 16384, 14336, 128, False),    # too many rows per CU for the split to pay
+])
+def test_workspace_size(M, N, K, g, split):
+    n = q4.gemv_q4_workspace_size(M, N, K, g)
+    if split:
+        assert n > 0 and n % (4 * M * N) == 0 and 2 <= n // (4 * M * N) <= 8
+    else:
+        assert n == 0
+    assert q4.gemv_q4_workspace_size(M, 0, K, g) == 0
+
+
+def test_workspace_entry_points_validate(L):
+    n = ctypes.c_size_t()
+    assert L.gemv_q4_workspace_size(1, 8, 100, 32, ctypes.byref(n)) == q4.Q4_EINVAL
+    assert L.gemv_q4_workspace_size(8, 4096, 14336, 128, None) == q4.Q4_ENULL
+    assert L.gemv_q4_ws(A16, A16, A16, A16, A16, 1, 8, 100, 32, A16B, 64, None) == q4.Q4_EINVAL
+    assert L.gemv_q4_ws(A16, A16, A16, A16, A16, 8, 0, 14336, 128, None, 0, None) == q4.Q4_OK
+    assert L.gemv_q4_ws(A16, A16, A16, A16, A16, 8, 64, 14336, 128, A16B + 4, 64, None) == q4.Q4_EALIGN
+    assert L.gemv_q4_ws(None, A16, A16, A16, A16, 8, 64, 14336, 128, A16B, 64, None) == q4.Q4_ENULL
+
+
 def test_set_geometry_changes_the_plan(clean_geometry):
     M, N, K, g = 1, 14336, 4096, 128
     default = q4.gemv_q4_geometry(M, N, K, g)

@@ -536,6 +536,66 @@ def test_gemv_q4_swiglu_zero_gate_is_exactly_zero():
     assert np.all(y.cpu().numpy() == 0.0)
 
 
+# ---------------------------------------------------------------- K split over workgroups (gemv_q4_ws)
+
+WS_SHAPES = [
+    # M, N, K, g: several x segments unsplit, so gemv_q4_ws splits K over workgroups
+    (8, 4096, 14336, 128), (4, 4096, 14336, 128), (3, 300, 14336, 128), (8, 100, 32768, 128),
+    (5, 77, 9216, 32), (8, 2048, 28672, 128), (6, 33, 14336, 128), (7, 1, 16384, 32),
+]
+
+
+@pytest.mark.parametrize("M,N,K,g", WS_SHAPES, ids=[f"M{a}N{b}K{c}g{d}" for a, b, c, d in WS_SHAPES])
+def test_gemv_q4_workspace_split(M, N, K, g):
+    """gemv_q4_ws with its workspace (partial sums of a K split, then their
+    sum) and gemv_q4 without one both meet the bound; a workspace one byte
+    short runs gemv_q4's plan."""
+    n = q4.gemv_q4_workspace_size(M, N, K, g)
+    assert n > 0 and n % (4 * M * N) == 0 and 2 <= n // (4 * M * N) <= 8
+    s = wl.Q4Shape(M, N, K, g, 0.002, 0.02)
+    d = wl.make_q4_problem(500 + N + M, s)
+    t = dev(d)
+    rows = sample_rows(N, 400, N) if N > 1000 else np.arange(N)
+    y_ref, b = oracle.gemv_q4(d["x"], d["wq"], d["scales"], d["zeros"], g, rows=rows)
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device=DEV)     # contents need no initialisation
+    y_ws = q4.gemv_q4(t["x"], t["wq"], t["scales"], t["zeros"], g, workspace=ws)
+    y_plain = q4.gemv_q4(t["x"], t["wq"], t["scales"], t["zeros"], g, workspace=False)
+    y_short = q4.gemv_q4(t["x"], t["wq"], t["scales"], t["zeros"], g, workspace=ws[:n - 16])
+    torch.cuda.synchronize()
+    assert_within(y_ws.cpu().numpy()[:, rows], y_ref, b, f"split M{M} N{N} K{K}")
+    assert_within(y_plain.cpu().numpy()[:, rows], y_ref, b, f"unsplit M{M} N{N} K{K}")
+    assert np.array_equal(y_short.cpu().numpy(), y_plain.cpu().numpy())
+
+
+def test_gemv_q4_workspace_split_graph_replay():
+    """The split's two launches captured in a graph: every replay, with the
+    workspace overwritten between them, equals the eager result."""
+    M, N, K, g = 8, 640, 14336, 128
+    s = wl.Q4Shape(M, N, K, g, 0.002, 0.02)
+    d = wl.make_q4_problem(77, s)
+    t = dev(d)
+    n = q4.gemv_q4_workspace_size(M, N, K, g)
+    assert n > 0
+    ws = torch.empty(n, dtype=torch.uint8, device=DEV)
+    y = torch.empty((M, N), device=DEV)
+    eager = q4.gemv_q4(t["x"], t["wq"], t["scales"], t["zeros"], g, workspace=ws).clone()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        q4.gemv_q4(t["x"], t["wq"], t["scales"], t["zeros"], g, out=y, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(graph):
+        q4.gemv_q4(t["x"], t["wq"], t["scales"], t["zeros"], g, out=y, workspace=ws)
+    for i in range(4):
+        y.fill_(float("nan"))
+        ws.fill_(i * 37 % 256)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager), f"replay {i}"
+
+
 # ---------------------------------------------------------------- every tunable geometry
 
 GEOM_SHAPES = [(1, 14336, 4096, 128), (1, 4096, 14336, 128), (4, 515, 4096, 128),
