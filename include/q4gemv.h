@@ -115,6 +115,21 @@ int gemv_q4_ws(const float *x, const uint8_t *wq, const uint16_t *scales,
  * shape, Q4_ENULL for a NULL bytes. */
 int gemv_q4_workspace_size(int M, int N, int K, int group_size, size_t *bytes);
 
+/* For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): gemv_q4_ws with the
+ * library's own workspace, a static 512 KiB device array on each GPU (enough
+ * for every K split gemv_q4_ws makes), so the call allocates nothing.  Same
+ * arguments, results, rules and errors as gemv_q4_ws with a large enough
+ * workspace (bit-identical to it); Q4_EINVAL should a shape ever need more
+ * than the array holds.  The first call on a device looks up the array's
+ * address there (no allocation).  Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (from different streams or
+ * threads) race and may return wrong results; calls on one stream are
+ * ordered and safe.  Nothing in the array needs clearing between calls. */
+int gemv_q4_static(const float *x, const uint8_t *wq, const uint16_t *scales,
+                   const uint8_t *zeros, float *y, int M, int N, int K, int group_size,
+                   void *stream);
+
 /* SwiGLU block of a decoder layer on int4 weights: the gate and up
  * projections, each a gemv_q4 of the same x, combined as
  *   y[m, n] = silu(g[m, n]) * u[m, n],   silu(v) = v / (1 + e^-v)

@@ -26,7 +26,7 @@ Q4_OK, Q4_EINVAL, Q4_ENULL, Q4_EALIGN, Q4_EDEVICE, Q4_ELAUNCH = 0, -1, -2, -3, -
 
 # Exported C symbols, in the order include/q4gemv.h, include/q4blocks.h and
 # include/q4scan.h declare them.
-EXPORTS = ("gemv_q4", "gemv_q4_ws", "gemv_q4_workspace_size", "gemv_q4_swiglu", "gemv_f32", "dequant_q4", "read_reduce",
+EXPORTS = ("gemv_q4", "gemv_q4_ws", "gemv_q4_workspace_size", "gemv_q4_static", "gemv_q4_swiglu", "gemv_f32", "dequant_q4", "read_reduce",
            "read_reduce_passes", "copy_vec4", "write_fill",
            "gemv_q4_geometry", "gemv_q4_path", "q4_strerror", "q4_abi_version",
            "gemv_q4_set_geometry", "gemv_q4_clear_geometry",
@@ -62,6 +62,7 @@ def lib() -> ctypes.CDLL:
     L.gemv_q4.argtypes = [P, P, P, P, P, I, I, I, I, P]
     L.gemv_q4_ws.argtypes = [P, P, P, P, P, I, I, I, I, P, Z, P]
     L.gemv_q4_workspace_size.argtypes = [I, I, I, I, ctypes.POINTER(Z)]
+    L.gemv_q4_static.argtypes = [P, P, P, P, P, I, I, I, I, P]
     L.gemv_q4_swiglu.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, P]
     L.gemv_f32.argtypes = [P, P, P, I, I, I, P]
     L.dequant_q4.argtypes = [P, P, P, P, P, I, I, I, P]
@@ -85,7 +86,7 @@ def lib() -> ctypes.CDLL:
     L.q4_strerror.argtypes = [I]
     L.q4_strerror.restype = ctypes.c_char_p
     L.q4_abi_version.argtypes = []
-    for f in ("gemv_q4", "gemv_q4_ws", "gemv_q4_workspace_size", "gemv_q4_swiglu", "gemv_f32", "dequant_q4", "read_reduce",
+    for f in ("gemv_q4", "gemv_q4_ws", "gemv_q4_workspace_size", "gemv_q4_static", "gemv_q4_swiglu", "gemv_f32", "dequant_q4", "read_reduce",
               "read_reduce_passes", "copy_vec4", "write_fill", "gemv_q4_geometry", "gemv_q4_path", "q4_abi_version",
               "gemv_q4_set_geometry", "gemv_q4_clear_geometry", "block_geometry", "gemv_block",
               "dequant_block", "gemv_block_set_config", "gemv_block_config", "scan2",

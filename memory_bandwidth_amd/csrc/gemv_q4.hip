@@ -2077,6 +2077,66 @@ extern "C" int gemv_q4_ws(const float *x, const uint8_t *wq, const uint16_t *sca
                           workspace ? workspace_bytes : 0);
 }
 
+// ---------------------------------------------------------------- without allocation
+// gemv_q4_static's workspace: a file-scope device array, one copy on each GPU
+// the library runs on, held until the process ends.  512 KiB covers every
+// K split the planner makes (KS * N <= 16384 at M <= 8, 4 bytes each).  Its
+// contents carry nothing from one call to the next (partial sums are written
+// before they are read), so nothing in it needs clearing.
+namespace {
+constexpr size_t kScratchBytes = 512 * 1024;
+__device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+// In host code `scratch` names a host-side stand-in, not the device array:
+// each device's address is looked up once, with that device current, and
+// kept here.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+float *g_scratch_ptr[kMaxDevices];
+
+float *scratch_on_current_device(int *status) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        *status = Q4_EDEVICE;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            *status = Q4_EDEVICE;
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = static_cast<float *>(ptr);
+    }
+    return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" int gemv_q4_static(const float *x, const uint8_t *wq, const uint16_t *scales,
+                              const uint8_t *zeros, float *y, int M, int N, int K, int group_size,
+                              void *stream) {
+    const int v = validate(M, N, K, group_size);
+    if (v != Q4_OK) return v;
+    if (N == 0) return Q4_OK;
+    const int a = check_q4_args(x, wq, scales, zeros, y);
+    if (a != Q4_OK) return a;
+    const int dev = q4::check_device();
+    if (dev != Q4_OK) return dev;
+    const size_t need = fm_work_bytes(plan(M, N, K, group_size, true), N);
+    if (need > kScratchBytes) return Q4_EINVAL;
+    float *work = nullptr;
+    if (need) {
+        int status = Q4_OK;
+        work = scratch_on_current_device(&status);
+        if (!work) return status;
+    }
+    return launch_gemv_q4(x, wq, scales, zeros, y, M, N, K, group_size, 0, stream, nullptr, work,
+                          work ? kScratchBytes : 0);
+}
+
 extern "C" int gemv_q4_swiglu(const float *x, const uint8_t *wq_gate, const uint16_t *scales_gate,
                               const uint8_t *zeros_gate, const uint8_t *wq_up,
                               const uint16_t *scales_up, const uint8_t *zeros_up, float *y,
