@@ -11,7 +11,10 @@ profile keyed by the device.
 Knobs: the arithmetic path (multiply-add or integer), wavefronts per
 workgroup and the K-split, i.e. every combination gemv_q4_set_geometry
 accepts for the shape; the library plans the rest (rows per workgroup,
-chunk positions per lane, x segments).
+chunk positions per lane, x segments).  Candidates are timed through
+gemv_q4 without a workspace, the plan the knobs set: where gemv_q4_ws splits
+K over workgroups its plan takes the wavefront split from the rows, not from
+the knob.
 
 Reference: the library's dense fp32 GEMV on the device-dequantised weights,
 with the bound |x| . |W|^T from the same GEMV of absolute values; a
@@ -131,7 +134,7 @@ class _Case:
     def check(self) -> bool:
         M, N, K, g = self.shape
         m0 = self.mats[0]
-        y = q4.gemv_q4(self.x, m0["wq"], m0["scales"], m0["zeros"], g).double()
+        y = q4.gemv_q4(self.x, m0["wq"], m0["scales"], m0["zeros"], g, workspace=False).double()
         return bool(((y - self.ref).abs() <= self.tol).all())
 
     def time(self) -> dict:
@@ -139,7 +142,7 @@ class _Case:
 
         def one_pass():
             for m, y in zip(self.mats, self.ys):
-                q4.gemv_q4(self.x, m["wq"], m["scales"], m["zeros"], g, out=y)
+                q4.gemv_q4(self.x, m["wq"], m["scales"], m["zeros"], g, out=y, workspace=False)
 
         return _sample(one_pass, self.n_mats, self.bytes)
 

@@ -1149,7 +1149,7 @@ __global__ __launch_bounds__(W * 64) void gemv_q4_fm_kernel(
     const float *__restrict__ x, const uint8_t *__restrict__ wq,
     const uint16_t *__restrict__ scales, const uint8_t *__restrict__ zeros,
     float *__restrict__ y, int N, int K, int gshift, int rpg, int seg_chunks, int epi,
-    float *__restrict__ part, int KS, int kpart) {
+    float *__restrict__ part, int ks_log2, int kpart) {
     constexpr int SUBR = 64 / LPR;             // rows one load instruction covers (a slot)
     constexpr int NG = W / S;                  // row groups per workgroup
     // float4 of one x row one thread loads ahead of the weights: the first
@@ -1161,7 +1161,7 @@ __global__ __launch_bounds__(W * 64) void gemv_q4_fm_kernel(
     // every argument in registers at once: one round trip for the kernel
     // arguments instead of one per use site
     asm volatile("" ::"s"(x), "s"(wq), "s"(scales), "s"(zeros), "s"(y), "s"(N), "s"(K), "s"(gshift),
-                 "s"(rpg), "s"(seg_chunks), "s"(epi), "s"(part), "s"(KS), "s"(kpart));
+                 "s"(rpg), "s"(seg_chunks), "s"(epi), "s"(part), "s"(ks_log2), "s"(kpart));
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
@@ -1174,7 +1174,8 @@ __global__ __launch_bounds__(W * 64) void gemv_q4_fm_kernel(
     // KS workgroups may split the K range of one block of rpg rows: this one
     // takes chunks [kc0, kc1) of the rows from rb * rpg, and with KS > 1
     // writes partial sums that fm_sum_parts adds.
-    const int rb = (int)blockIdx.x / KS, kb = (int)blockIdx.x - rb * KS;
+    const int KS = 1 << ks_log2;   // a power of two: no division on the way to the first load
+    const int rb = (int)blockIdx.x >> ks_log2, kb = (int)blockIdx.x & (KS - 1);
     const int kc0 = kb * kpart, kc1 = min(C, kc0 + kpart);
     const int gq = rpg / NG, grem = rpg - gq * NG;
     const int gstart = rb * rpg + rg * gq + min(rg, grem);
@@ -1609,8 +1610,11 @@ bool plan_fm(Geometry &p, int M, int N, int K, const Knobs &k, bool split = fals
     for (int pass = 0; pass < 2; ++pass) {
         long blocks = std::max<long>(1, std::min<long>(kCUs / KS, N));
         long rpg = (N + blocks - 1) / blocks;
-        int S = k.ksplit ? k.ksplit : 4;
-        if (!k.ksplit)
+        // a K split over workgroups takes the wavefront split from its rows,
+        // not from the knob (which sets the unsplit plan)
+        const int ks_knob = KS > 1 ? 0 : k.ksplit;
+        int S = ks_knob ? ks_knob : 4;
+        if (!ks_knob)
             while (S > 1 && (W / S) * SUBR * R < rpg) S /= 2;
         const long cap = (long)(W / S) * SUBR * R;    // rows the row groups hold
         if (rpg > cap) rpg = cap;
@@ -1876,7 +1880,7 @@ void launch_fm(const Geometry &p, const float *x, const uint8_t *wq, const uint1
                const uint8_t *zeros, float *y, int N, int K, int gshift, hipStream_t st) {
     hipLaunchKernelGGL((gemv_q4_fm_kernel<kFmW, MX, kFmR, kFmLPR, S, JP>), dim3(p.grid), dim3(kFmW * 64),
                        lds_bytes(p), st, x, wq, scales, zeros, y, N, K, gshift, p.rpg, p.seg_chunks, p.epi,
-                       p.work, p.ks_wg, p.kpart);
+                       p.work, p.ks_wg == 8 ? 3 : (p.ks_wg == 4 ? 2 : (p.ks_wg == 2 ? 1 : 0)), p.kpart);
     if (p.ks_wg > 1) {
         const int MN = MX * N;   // the split is planned only for N * KS <= 8192
         hipLaunchKernelGGL(fm_sum_parts, dim3((MN + 255) / 256), dim3(256), 0, st, y, p.work, MN, p.ks_wg, p.epi);
