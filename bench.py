@@ -1276,7 +1276,7 @@ def _kernel_short(name: str) -> str:
 
     m = re.search(r"(gemv_q4(?:_int|_intm|_fm)?_kernel<[^>]*>|gemv_f32_kernel<[^>]*>|read_reduce_kernel(?:<[^>]*>)?|"
                   r"write_fill_kernel|copy_kernel|dequant_q4_kernel|gemv_blk_kernel<[^>]*>|"
-                  r"dequant_blk_kernel<[^>]*>|scan2_kernel<[^>]*>|at::native::\w+|__amd_rocclr_\w+)", name)
+                  r"dequant_blk_kernel<[^>]*>|scan2_kernel<[^>]*>|fm_sum_parts|at::native::\w+|__amd_rocclr_\w+)", name)
     return m.group(1).replace("(anonymous namespace)::", "") if m else name.split("(")[0][:60]
 
 
@@ -1285,6 +1285,18 @@ def _kernel_key(r: dict) -> str:
     calibration probe and 30.5 MB floor dispatches share one kernel)."""
     k = _kernel_short(r["Kernel_Name"])
     return f"{k} grid {r['Grid_Size']}" if k.startswith("read_reduce") else k
+
+
+def _keyed_rows(d: str) -> list[tuple[str, dict]]:
+    """The counter rows under d, each with its summary key: _kernel_key, and
+    " K split" for a multiply-add dispatch that fm_sum_parts follows (the
+    down projection with a workspace, whose grid equals the up projection's)."""
+    rows = _rows(os.path.join(d, "**", "*counter_collection.csv"))
+    kern = {int(r["Dispatch_Id"]): _kernel_key(r) for r in rows}
+    ids = sorted(kern)
+    split = {a for a, b in zip(ids, ids[1:]) if kern[b] == "fm_sum_parts" and "_fm_" in kern[a]}
+    return [(kern[int(r["Dispatch_Id"])] + (" K split" if int(r["Dispatch_Id"]) in split else ""), r)
+            for r in rows]
 
 
 def _probe_key(mean: dict) -> str:
@@ -1310,9 +1322,8 @@ def summarize_counters(dirs: list[str], name: str, command: str) -> str:
     profiler, and the VALU issue figures derived from them."""
     per, dur, grid = {}, {}, {}
     for d in dirs:
-        for r in _rows(os.path.join(d, "**", "*counter_collection.csv")):
-            k = _kernel_key(r)
-            if not re.match(r"(gemv_q4|gemv_blk|read_reduce)", k):
+        for k, r in _keyed_rows(d):
+            if not re.match(r"(gemv_q4|gemv_blk|read_reduce|fm_sum_parts)", k):
                 continue
             per.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
             dur.setdefault(k, {})[(d, r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
@@ -1320,7 +1331,9 @@ def summarize_counters(dirs: list[str], name: str, command: str) -> str:
     lines = [f"# {name}: rocprofv3 counters per dispatch", "", f"command: `{command}`", "",
              "Means over the dispatches of each kernel in one --pmc-workload run per pass "
              "(the stream kernel: 64 launches over 32 matrices; the read floor: 32 buffers of "
-             "30.5 MB, one launch each; 4 and 8 rows: 8 matrices per FFN projection; the block "
+             "30.5 MB, one launch each; 4 and 8 rows: 8 matrices per FFN projection, the "
+             "up projection 4096 -> 14336 plain, the down projection 14336 -> 4096 split over "
+             "K with a workspace (marked K split, then fm_sum_parts adds the parts); the block "
              "formats at the stream shape: 16 launches over 8 matrices each).  "
              "Durations are those of the counter runs (serialised dispatches).", ""]
     ctrs = [c for p in PMC_COUNTER_PASSES for c in p.split()]
@@ -1399,14 +1412,15 @@ def summarize_pmc(fetch_dir: str, write_dir: str, name: str, command: str) -> st
     known size: read_reduce streams PROBE_BYTES, write_fill writes PROBE_BYTES."""
     per = {}
     for d, ctr in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
-        for r in _rows(os.path.join(d, "**", "*counter_collection.csv")):
+        for k, r in _keyed_rows(d):
             if r["Counter_Name"] == ctr:
-                per.setdefault((_kernel_key(r), ctr), []).append(float(r["Counter_Value"]))
+                per.setdefault((k, ctr), []).append(float(r["Counter_Value"]))
     mean = {k: statistics.mean(v) for k, v in per.items()}
     probe = _probe_key(mean)
     fetch_factor = wl.PROBE_BYTES / (mean[(probe, "FETCH_SIZE")] * 1024)
     write_factor = wl.PROBE_BYTES / (mean[("write_fill_kernel", "WRITE_SIZE")] * 1024)
     # the stream kernel: the gemv_q4 kernel with the most dispatches (2 x 32)
+    # (the multiply-add launches at 4 and 8 rows: 8 per FFN projection)
     qk = max((k for k, c in mean if k.startswith("gemv_q4_") and c == "FETCH_SIZE"),
              key=lambda k: len(per[(k, "FETCH_SIZE")]))
     s = wl.STREAM_SHAPE
@@ -1448,6 +1462,17 @@ def summarize_pmc(fetch_dir: str, write_dir: str, name: str, command: str) -> st
             f = mean[(k, "FETCH_SIZE")] * 1024 * fetch_factor
             lines.append(f"gemv_block {fmt} per launch (stream shape): {f:.0f} B fetched against "
                          f"{a} algorithmic bytes: ratio {f / a:.4f}.")
+        elif k.startswith("gemv_q4_fm_kernel"):
+            a = wl.q4_weight_bytes(s.N, s.K, s.g)
+            f = mean[(k, "FETCH_SIZE")] * 1024 * fetch_factor
+            w = mean.get((k, "WRITE_SIZE"), 0.0) * 1024 * write_factor
+            lines.append(f"{k} per launch (an FFN projection, {a} B of weights): {f:.0f} B fetched "
+                         f"(ratio {f / a:.4f}), {w:.0f} B written.")
+        elif k == "fm_sum_parts":
+            f = mean[(k, "FETCH_SIZE")] * 1024 * fetch_factor
+            w = mean.get((k, "WRITE_SIZE"), 0.0) * 1024 * write_factor
+            lines.append(f"fm_sum_parts per launch (the K parts of a split down projection): "
+                         f"{f:.0f} B fetched, {w:.0f} B written.")
         elif k.startswith("scan2_kernel"):
             a = wl.SCAN_VECTORS * wl.SCAN_DIM // 4
             f = mean[(k, "FETCH_SIZE")] * 1024 * fetch_factor
