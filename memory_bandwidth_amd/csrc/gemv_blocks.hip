@@ -14,6 +14,12 @@
 //     units' slices hit 16 different bank groups, and a lane keeps its
 //     unit's 64 x values in registers while they stay the same.  The loads
 //     of the next block are issued before the arithmetic of the current one.
+//   * The default launch gives each workgroup one row block in one pass.
+//     That kernel keeps no second set of loads, and Q4_0 / Q4_K lanes hold
+//     only the 32 x values of the run they are on, with the sums of x of the
+//     Q4_K min term formed once per workgroup in LDS: 55-70 VGPRs, so that
+//     all seven wavefronts per SIMD of a 4096 -> 14336 launch are resident
+//     at once (162 VGPRs, three at a time, before).
 //   * Unit bytes come in with dword-aligned buffer loads.  Fields that start
 //     2 bytes past a dword boundary (the first block of a Q4_0 or Q8_0 pair,
 //     every odd Q6_K block) are shifted into place with v_alignbyte_b32;
@@ -112,6 +118,10 @@ constexpr uint32_t kMagic = 0x64006400u;
 //   dot(raw, u, xv, dk)     (formats with kDot) dk[k] = sum over lane
 //                           elements 16k .. 16k + 15 of v * xv[e], the same
 //                           products as visit, decoded two at a time
+//   dot_half<R>(raws, u, x32, d, h)
+//                           (formats with kHalf) the same sums for k = 2h,
+//                           2h + 1 of every row slot into d[r][k], from the
+//                           32 x values of run h alone
 // kMin: the format has a min term (b != -0).  kMaxR: the most row slots per
 // lane that compile without spilling.
 // ---------------------------------------------------------------------------
@@ -120,6 +130,7 @@ struct FmtQ4_0 {
     static constexpr int kMaxR = 4;   // row slots per lane without spilling
     static constexpr bool kMin = false;
     static constexpr bool kDot = true;
+    static constexpr bool kHalf = true;
     struct Raw { uint32_t v[9]; };
     __device__ static void load(Raw &r, rsrc_t rs, uint32_t ro, int u) {
         const uint32_t o = ro + 36u * (uint32_t)u;      // two 18-byte blocks
@@ -163,6 +174,37 @@ struct FmtQ4_0 {
             dk[2 * blk + 1] = hi * 0.0625f;
         }
     }
+    // Block blk of the pair for every row slot, one slot after another (the
+    // low and high nibbles' chains interleave; one slot's codes are live at
+    // a time).
+    template <int R>
+    __device__ static void dot_half(const Raw (&raw)[R], int, const float (&x32)[32], float (&d)[R][4], int blk) {
+        const half2_t z1 = as_h2(0x64086408u), z16 = as_h2(0x64806480u);   // 1024 + 8, 1024 + 128
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float lo = 0.f, hi = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float *x = x32 + 4 * i;
+                const uint32_t w = blk == 0 ? realign(raw[r].v[i], raw[r].v[i + 1], 2) : raw[r].v[5 + i];
+                const uint32_t w8 = w >> 8;
+                const half2_t d0 = as_h2(and_or(w, 0x000F000Fu, kMagic)) - z1;
+                const half2_t d1 = as_h2(and_or(w8, 0x000F000Fu, kMagic)) - z1;
+                const half2_t d2 = as_h2(and_or(w, 0x00F000F0u, kMagic)) - z16;
+                const half2_t d3 = as_h2(and_or(w8, 0x00F000F0u, kMagic)) - z16;
+                lo = __builtin_fmaf((float)d0.x, x[0], lo);
+                lo = __builtin_fmaf((float)d1.x, x[1], lo);
+                lo = __builtin_fmaf((float)d0.y, x[2], lo);
+                lo = __builtin_fmaf((float)d1.y, x[3], lo);
+                hi = __builtin_fmaf((float)d2.x, x[16], hi);
+                hi = __builtin_fmaf((float)d3.x, x[17], hi);
+                hi = __builtin_fmaf((float)d2.y, x[18], hi);
+                hi = __builtin_fmaf((float)d3.y, x[19], hi);
+            }
+            d[r][2 * blk] = lo;
+            d[r][2 * blk + 1] = hi * 0.0625f;
+        }
+    }
     template <class Fn> __device__ static void visit(const Raw &r, int, Fn &&fn) {
         // Nibble c ^ 8, sign-extended, is c - 8.
 #pragma unroll
@@ -184,6 +226,7 @@ struct FmtQ8_0 {
     static constexpr int kMaxR = 4;   // row slots per lane without spilling
     static constexpr bool kMin = false;
     static constexpr bool kDot = false;
+    static constexpr bool kHalf = false;
     struct Raw { uint32_t v[17]; };
     __device__ static void load(Raw &r, rsrc_t rs, uint32_t ro, int u) {
         const uint32_t o = ro + 68u * (uint32_t)u;      // two 34-byte blocks
@@ -239,6 +282,7 @@ struct FmtQ4_K {
     static constexpr int kMaxR = 4;   // row slots per lane without spilling
     static constexpr bool kMin = true;
     static constexpr bool kDot = true;
+    static constexpr bool kHalf = true;
     struct Raw { uint32_t v[12]; };
     __device__ static void load(Raw &r, rsrc_t rs, uint32_t ro, int u) {
         const uint32_t ob = ro + 144u * (uint32_t)(u >> 2);
@@ -279,6 +323,38 @@ struct FmtQ4_K {
         dk[2] = hi[0] * 0.0625f;
         dk[3] = hi[1] * 0.0625f;
     }
+    // h = 0: sub-block 2p (low nibbles) into d[r][0], d[r][1]; h = 1:
+    // sub-block 2p + 1 (high nibbles) into d[r][2], d[r][3].  x32 holds the
+    // sub-block's 32 x values; the row slots' chains interleave.
+    template <int R>
+    __device__ static void dot_half(const Raw (&raw)[R], int, const float (&x32)[32], float (&d)[R][4], int h) {
+        const half2_t z = as_h2(kMagic);                 // 1024
+        const uint32_t m = h ? 0x00F000F0u : 0x000F000Fu;
+#pragma unroll
+        for (int r = 0; r < R; ++r) d[r][2 * h] = d[r][2 * h + 1] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int k = 2 * h + (i >> 2);
+            const float *xa = x32 + 4 * i;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint32_t w = raw[r].v[4 + i], w8 = w >> 8;
+                const half2_t d0 = as_h2(and_or(w, m, kMagic)) - z;    // elements 4i, 4i + 2 (16 x for h = 1)
+                const half2_t d1 = as_h2(and_or(w8, m, kMagic)) - z;   // 4i + 1, 4i + 3
+                d[r][k] = __builtin_fmaf((float)d0.x, xa[0], d[r][k]);
+                d[r][k] = __builtin_fmaf((float)d1.x, xa[1], d[r][k]);
+                d[r][k] = __builtin_fmaf((float)d0.y, xa[2], d[r][k]);
+                d[r][k] = __builtin_fmaf((float)d1.y, xa[3], d[r][k]);
+            }
+        }
+        if (h) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                d[r][2] *= 0.0625f;
+                d[r][3] *= 0.0625f;
+            }
+        }
+    }
     template <class Fn> __device__ static void visit(const Raw &r, int, Fn &&fn) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -297,6 +373,7 @@ struct FmtQ5_K {
     static constexpr int kMaxR = 2;   // row slots per lane without spilling
     static constexpr bool kMin = true;
     static constexpr bool kDot = false;
+    static constexpr bool kHalf = false;
     struct Raw { uint32_t v[20]; };
     __device__ static void load(Raw &r, rsrc_t rs, uint32_t ro, int u) {
         const uint32_t ob = ro + 176u * (uint32_t)(u >> 2);
@@ -354,6 +431,7 @@ struct FmtQ6_K {
     static constexpr int kMaxR = 2;   // row slots per lane without spilling
     static constexpr bool kMin = false;
     static constexpr bool kDot = true;
+    static constexpr bool kHalf = false;
     struct Raw { uint32_t l[9], h[9], sa, sb, d, sh; };
     __device__ static void load(Raw &r, rsrc_t rs, uint32_t ro, int u) {
         const uint32_t hf = (uint32_t)(u >> 1) & 1u, s = (uint32_t)u & 1u;
@@ -447,7 +525,7 @@ struct FmtQ6_K {
 // LDS slot of x's float4 number f: one float4 of padding after every 16.
 __device__ __forceinline__ int xslot(int f) { return f + (f >> 4); }
 
-template <class T, int R, int W, int LPR>
+template <class T, int R, int W, int LPR, bool ONE>
 __global__ __launch_bounds__(W * 64) void gemv_blk_kernel(const float *__restrict__ x,
                                                           const uint8_t *__restrict__ w,
                                                           float *__restrict__ y, int N, int K,
@@ -508,6 +586,25 @@ __global__ __launch_bounds__(W * 64) void gemv_blk_kernel(const float *__restric
     }
     for (int i = XB * W * 64 + tid; i < nx4; i += W * 64) xs[xslot(i)] = x4[i];
     __syncthreads();
+    // One item per workgroup (ONE): formats with kHalf decode a run of the
+    // unit at a time with only its 32 x values in registers, and keep no
+    // second set of loads, so that every wavefront of a CU fits at once.
+    // A min term's sums of x over each 16 consecutive elements are formed
+    // once per workgroup here (a quarter of them per wavefront, for four)
+    // and read after a barrier that follows the dot products.
+    constexpr bool HALF = ONE && T::kHalf;
+    float *sxs = reinterpret_cast<float *>(xs + xslot(nx4 - 1) + 1);
+    if constexpr (HALF && T::kMin) {
+        for (int i = tid; i < (K >> 4); i += W * 64) {
+            float t = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4_t v = xs[xslot(4 * i + q)];
+                t += v.x; t += v.y; t += v.z; t += v.w;
+            }
+            sxs[i] = t;
+        }
+    }
 
     float xv[64], sx[4];
     int xpass = -1;
@@ -522,7 +619,51 @@ __global__ __launch_bounds__(W * 64) void gemv_blk_kernel(const float *__restric
         const int pass = it % P;
         const int u = pass * LPR + ul;
         const int uc = min(u, U - 1);
-        if (pass != xpass) {
+        if constexpr (HALF) {
+            float a[R][4], b[R][4], d[R][4];
+            if (u < U) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) T::affine(raw[r], uc, a[r], b[r]);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    __builtin_amdgcn_sched_barrier(0);   // run h's x reads stay after run h - 1's arithmetic
+                    float x32[32];
+                    const int f = T::xstart(uc, h) >> 2;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const f32x4_t v = xs[xslot(f + i)];
+                        x32[4 * i] = v.x; x32[4 * i + 1] = v.y; x32[4 * i + 2] = v.z; x32[4 * i + 3] = v.w;
+                    }
+                    T::template dot_half<R>(raw, uc, x32, d, h);
+                    if constexpr (!T::kMin) {
+#pragma unroll
+                        for (int r = 0; r < R; ++r) {
+                            float c = acc[r];
+                            c = __builtin_fmaf(a[r][2 * h], d[r][2 * h], c);
+                            c = __builtin_fmaf(a[r][2 * h + 1], d[r][2 * h + 1], c);
+                            acc[r] = c;
+                        }
+                    }
+                }
+            }
+            if constexpr (T::kMin) {
+                __syncthreads();                      // the sums of x are written
+                if (u < U) {
+                    const f32x4_t v = *reinterpret_cast<const f32x4_t *>(sxs + 4 * uc);
+                    const float s4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        float c = acc[r];
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            c = __builtin_fmaf(a[r][k], d[r][k], c);
+                            c = __builtin_fmaf(b[r][k], s4[k], c);
+                        }
+                        acc[r] = c;
+                    }
+                }
+            }
+        } else if (pass != xpass) {
             xpass = pass;
 #pragma unroll
             for (int run = 0; run < 2; ++run) {
@@ -546,7 +687,7 @@ __global__ __launch_bounds__(W * 64) void gemv_blk_kernel(const float *__restric
                 }
             }
         }
-        if (u < U) {
+        if (!HALF && u < U) {
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 float a[4], b[4];
@@ -592,6 +733,10 @@ __global__ __launch_bounds__(W * 64) void gemv_blk_kernel(const float *__restric
         }
     };
 
+    if constexpr (ONE) {             // one item per workgroup: no second set of loads
+        process(ra, 0);
+        return;
+    }
     for (int it = 0; it < nitems; it += 2) {
         if (it + 1 < nitems) load_item(rb, it + 1);
         process(ra, it);
@@ -663,12 +808,16 @@ bool geometry_of(int f, Geo &g) {
 // workgroups; 0 = one workgroup per row block).
 // Defaults (measured on the 4096 -> 14336 stream and 1024 -> 65536 shapes)
 // apply to shapes of at least 2 * CUs row blocks; smaller ones, latency-
-// bound, take one row slot and 4 wavefronts, the most workgroups.  A
-// configuration set through gemv_block_set_config applies to every shape.
+// bound, take one row slot and 4 wavefronts, the most workgroups.  One
+// workgroup per row block (G = 0) runs the one-item kernel, whose small
+// register footprint lets every wavefront of a CU be resident at once;
+// every format takes it (at the stream shape Q5_K 11.7 -> 10.8 us, Q6_K
+// 13.9 -> 12.2 us, Q8_0 12.9 -> 12.5 us against looping over row blocks).
+// A configuration set through gemv_block_set_config applies to every shape.
 struct Cfg { int R, W, G; bool forced; };
 constexpr int kCUs = 256;
-constexpr Cfg kDefault[6] = {{0, 0, 0, false}, {2, 4, 0, false}, {1, 4, 2, false},
-                             {2, 4, 0, false}, {2, 4, 2, false}, {1, 4, 2, false}};
+constexpr Cfg kDefault[6] = {{0, 0, 0, false}, {2, 4, 0, false}, {1, 8, 0, false},
+                             {2, 4, 0, false}, {2, 4, 0, false}, {1, 8, 0, false}};
 constexpr Cfg kSmall = {1, 4, 0, false};
 // The setting of each format, packed into one word so that a launch reads
 // it whole while gemv_block_set_config changes it on another thread:
@@ -709,9 +858,13 @@ void launch_l(Cfg c, const float *x, const uint8_t *w, float *y, int N, int K, u
     constexpr int RPB = R * (64 / LPR) * W;
     const int nblk = (N + RPB - 1) / RPB;
     const int grid = c.G > 0 ? std::min(nblk, c.G * kCUs) : nblk;
-    const size_t lds = (size_t)(K / 4 + K / 64) * 16;
-    hipLaunchKernelGGL((gemv_blk_kernel<T, R, W, LPR>), dim3(grid), dim3(W * 64), lds, st, x, w, y, N, K,
-                       RB);
+    const size_t lds = (size_t)(K / 4 + K / 64) * 16 + (size_t)(K / 16) * 4;   // x, then its sums of 16
+    if (grid == nblk && K / 64 <= LPR)   // every workgroup has exactly one item (one block, one pass)
+        hipLaunchKernelGGL((gemv_blk_kernel<T, R, W, LPR, true>), dim3(grid), dim3(W * 64), lds, st, x, w, y, N,
+                           K, RB);
+    else
+        hipLaunchKernelGGL((gemv_blk_kernel<T, R, W, LPR, false>), dim3(grid), dim3(W * 64), lds, st, x, w, y,
+                           N, K, RB);
 }
 
 template <class T, int R, int W>
