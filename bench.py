@@ -917,7 +917,8 @@ def run_scan(torch, q4, dev, reps_target_s: float = 0.02) -> dict:
 # ---------------------------------------------------------------- several activation rows
 
 FP32_VECTOR_PEAK = 157.3e12     # MI355X fp32 vector FLOP/s, AMD published
-SIMDS = 256 * 4                # MI355X: 256 CUs of 4 SIMDs
+CUS = 256                      # MI355X compute units
+SIMDS = CUS * 4                # 4 SIMDs per CU
 
 
 def run_ffn_rows(torch, q4, W, reps_target_s: float = 0.02) -> dict:
@@ -1312,7 +1313,10 @@ PMC_COUNTER_PASSES = (
     "SQ_INSTS_LDS SQ_INSTS_VMEM_RD",
     "TA_BUSY_avr TA_BUFFER_READ_WAVEFRONTS_sum TCC_REQ_sum TCC_HIT_sum TCC_MISS_sum GRBM_GUI_ACTIVE "
     "GRBM_COUNT",
+    "SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS SQ_INSTS_VALU_FMA_F32 "
+    "SQ_INSTS_VALU_INT32 SQ_INSTS_VALU_ADD_F32 SQ_INSTS_VALU_MUL_F32",
 )
+CLOCK_GHZ = 2.4            # MI355X peak engine clock, for cycle counts over a dispatch
 
 
 def summarize_counters(dirs: list[str], name: str, command: str) -> str:
@@ -1357,6 +1361,14 @@ def summarize_counters(dirs: list[str], name: str, command: str) -> str:
                          f"{c['SQ_WAIT_INST_ANY'] / c['SQ_ACTIVE_INST_ANY']:.2f}.")
         if "GRBM_GUI_ACTIVE" in c:
             lines.append(f"GRBM_GUI_ACTIVE {c['GRBM_GUI_ACTIVE']:.0f} cycles per dispatch.")
+        if "SQ_LDS_IDX_ACTIVE" in c:
+            cyc = CUS * us * 1e3 * CLOCK_GHZ
+            lines.append(f"LDS busy {100 * c['SQ_LDS_IDX_ACTIVE'] / cyc:.1f}% of the dispatch's CU cycles "
+                         f"({CUS} CUs at {CLOCK_GHZ} GHz); bank-conflict cycles "
+                         f"{c.get('SQ_LDS_BANK_CONFLICT', 0):.0f}.")
+        if "SQ_INSTS_VALU_FMA_F32" in c and c.get("SQ_INSTS_VALU"):
+            lines.append(f"fp32 FMA {100 * c['SQ_INSTS_VALU_FMA_F32'] / c['SQ_INSTS_VALU']:.1f}% of the VALU "
+                         "instructions.")
         lines.append("")
     out = os.path.join(PROFILES, name + ".md")
     open(out, "w").write("\n".join(lines) + "\n")
