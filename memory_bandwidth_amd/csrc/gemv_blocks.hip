@@ -590,7 +590,7 @@ __global__ __launch_bounds__(W * 64) void gemv_blk_kernel(const float *__restric
     // unit at a time with only its 32 x values in registers, and keep no
     // second set of loads, so that every wavefront of a CU fits at once.
     // A min term's sums of x over each 16 consecutive elements are formed
-    // once per workgroup here (a quarter of them per wavefront, for four)
+    // once per workgroup here (one per thread at K = 4096 and 256 threads),
     // and read after a barrier that follows the dot products.
     constexpr bool HALF = ONE && T::kHalf;
     float *sxs = reinterpret_cast<float *>(xs + xslot(nx4 - 1) + 1);
