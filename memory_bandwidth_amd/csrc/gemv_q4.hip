@@ -1882,7 +1882,7 @@ void launch_fm(const Geometry &p, const float *x, const uint8_t *wq, const uint1
                        lds_bytes(p), st, x, wq, scales, zeros, y, N, K, gshift, p.rpg, p.seg_chunks, p.epi,
                        p.work, p.ks_wg == 8 ? 3 : (p.ks_wg == 4 ? 2 : (p.ks_wg == 2 ? 1 : 0)), p.kpart);
     if (p.ks_wg > 1) {
-        const int MN = MX * N;   // the split is planned only for N * KS <= 8192
+        const int MN = MX * N;   // the split is planned only for KS * N <= 16384
         hipLaunchKernelGGL(fm_sum_parts, dim3((MN + 255) / 256), dim3(256), 0, st, y, p.work, MN, p.ks_wg, p.epi);
     }
 }
