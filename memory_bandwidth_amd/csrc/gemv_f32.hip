@@ -3,19 +3,31 @@
 // The control of cera 0.5.0 wgpu_gemv_bench.rs (the f32 kernel kept in the
 // table to tell harness artefacts from kernel properties).  It shares the
 // int4 kernel's geometry: a wavefront owns R rows, LPR lanes share a row and
-// stream it with 16-byte loads (four weights per lane-load), x is staged in
-// LDS (consecutive lanes read consecutive float4, so no swizzle is needed),
-// and partial sums are reduced with DPP and cross-row shuffles, meeting in
-// LDS only when S wavefronts split a row's K range.
+// stream it with 16-byte non-temporal loads (four weights per lane-load; the
+// weights are read once), x is staged in LDS (consecutive lanes read
+// consecutive float4, so no swizzle is needed), and partial sums are reduced
+// with DPP and cross-row shuffles, meeting in LDS only when S wavefronts
+// split a row's K range.  Each lane keeps two batches of loads: the next
+// batch is issued before the current one's arithmetic, so a wavefront's
+// loads stay in flight across its whole row instead of one batch at a time.
 #include "q4_common.h"
 #include "q4_device.h"
 
 namespace {
 
 constexpr int kWaves = 4;
+constexpr int kCUs = 256;                     // MI355X compute units
 constexpr int kBlock = kWaves * q4::kWave;
 constexpr int kLdsBytes = 64 * 1024;          // dynamic LDS budget per workgroup
-constexpr int kUnroll = 4;                    // float4 positions per lane per batch
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+// A weight float4, read once: a non-temporal load.
+__device__ __forceinline__ float4 ldnt(const float4 *p) {
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+// float4 positions per lane in each of the two batches in flight: 2 at one
+// or two activation rows (fewer registers, more wavefronts), 4 at more.
+constexpr int batch(int M) { return M <= 2 ? 2 : 4; }
 
 constexpr int row_slots(int M) { return M <= 2 ? 4 : (M <= 4 ? 2 : 1); }
 
@@ -24,6 +36,7 @@ __global__ __launch_bounds__(kBlock) void gemv_f32_kernel(
     const float *__restrict__ x, const float4 *__restrict__ w, float *__restrict__ y, int N,
     int K, int S, int seg4) {
     constexpr int R = row_slots(M);
+    constexpr int UB = batch(M);
     constexpr int RG = q4::kWave / LPR;
     constexpr int RPW = R * RG;
     extern __shared__ float lds[];
@@ -56,20 +69,22 @@ __global__ __launch_bounds__(kBlock) void gemv_f32_kernel(
         const int part = (segC + S - 1) / S;
         const int lo = s0 + ks * part;
         const int hi = min(s0 + segC, lo + part);
-        for (int base = lo + li; base < hi; base += kUnroll * LPR) {
-            float4 wv[kUnroll][R];
+        auto load = [&](float4 (&wv)[UB][R], int bs) {
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int c = base + u * LPR;
+            for (int u = 0; u < UB; ++u) {
+                const int c = bs + u * LPR;
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     const int row = min(row0 + r * RG, N - 1);
-                    wv[u][r] = c < hi ? w[(size_t)row * C4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
+                    wv[u][r] = c < hi ? ldnt(&w[(size_t)row * C4 + c])
+                                      : make_float4(0.f, 0.f, 0.f, 0.f);
                 }
             }
+        };
+        auto comp = [&](const float4 (&wv)[UB][R], int bs) {
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int c = base + u * LPR;
+            for (int u = 0; u < UB; ++u) {
+                const int c = bs + u * LPR;
                 if (c < hi) {
 #pragma unroll
                     for (int m = 0; m < M; ++m) {
@@ -86,6 +101,20 @@ __global__ __launch_bounds__(kBlock) void gemv_f32_kernel(
                     }
                 }
             }
+        };
+        float4 wa[UB][R], wb[UB][R];
+        int bs = lo + li;
+        if (bs < hi) load(wa, bs);
+        while (bs < hi) {
+            const int n1 = bs + UB * LPR;
+            if (n1 < hi) load(wb, n1);
+            comp(wa, bs);
+            bs = n1;
+            if (bs >= hi) break;
+            const int n2 = bs + UB * LPR;
+            if (n2 < hi) load(wa, n2);
+            comp(wb, bs);
+            bs = n2;
         }
     }
 
@@ -138,14 +167,33 @@ Geometry plan(int M, int N, int K) {
     p.LPR = C4 <= 16 ? 16 : (C4 <= 32 ? 32 : 64);
     const int rpw = row_slots(M) * (q4::kWave / p.LPR);
     const long row_waves = ((long)N + rpw - 1) / rpw;
-    p.S = 1;
-    while (p.S < kWaves && 2 * p.S * p.LPR <= C4 && row_waves * p.S < 2048) p.S *= 2;
-    const int comb = p.S > 1 ? kWaves * rpw * M * 4 : 0;
-    const int max_seg = (kLdsBytes - comb) / (M * 16);
-    p.seg4 = C4 < max_seg ? C4 : max_seg;
-    const long rows_per_wg = (long)rpw * (kWaves / p.S);
-    p.grid = (int)((N + rows_per_wg - 1) / rows_per_wg);
-    p.lds = M * p.seg4 * 16 + comb;
+    // K split S: at least two wavefronts per SIMD where the rows allow it;
+    // then, among the splits that stage x in no more segments, the one whose
+    // workgroups spread most evenly over the CUs (896 workgroups of the
+    // 4096 -> 14336 shape leave half the CUs a fourth one; 1792 do not).
+    auto shape = [&](int S, Geometry &g) {
+        g.S = S;
+        const int comb = S > 1 ? kWaves * rpw * M * 4 : 0;
+        const int max_seg = (kLdsBytes - comb) / (M * 16);
+        g.seg4 = C4 < max_seg ? C4 : max_seg;
+        const long rows_per_wg = (long)rpw * (kWaves / S);
+        g.grid = (int)((N + rows_per_wg - 1) / rows_per_wg);
+        g.lds = M * g.seg4 * 16 + comb;
+    };
+    int S = 1;
+    while (S < kWaves && 2 * S * p.LPR <= C4 && row_waves * S < 2048) S *= 2;
+    shape(S, p);
+    const int segs = (C4 + p.seg4 - 1) / p.seg4;
+    auto spread = [](long grid) {   // workgroups per CU over the most any CU gets
+        const long per = (grid + kCUs - 1) / kCUs;
+        return (double)grid / (double)(per * kCUs);
+    };
+    for (int s2 = S * 2; s2 <= kWaves && 2 * s2 * p.LPR <= C4; s2 *= 2) {
+        Geometry g = p;
+        shape(s2, g);
+        if ((C4 + g.seg4 - 1) / g.seg4 > segs) break;
+        if (spread(g.grid) > spread(p.grid) + 0.01) p = g;
+    }
     return p;
 }
 

@@ -409,8 +409,9 @@ def test_dequant_codes_only_and_weights_only():
 
 # ---------------------------------------------------------------- gemv_f32
 
+# (2, 9000, 4096) and (1, 4097, 4096): K splits chosen to spread the workgroups evenly
 F32 = [(1, 1, 4), (1, 33, 60), (2, 65, 128), (1, 1000, 896), (8, 129, 4096), (3, 77, 16400),
-       (1, 4097, 4096), (5, 31, 20000)]
+       (1, 4097, 4096), (5, 31, 20000), (2, 9000, 4096)]
 
 
 @pytest.mark.parametrize("M,N,K", F32, ids=[f"M{a}N{b}K{c}" for a, b, c in F32])
