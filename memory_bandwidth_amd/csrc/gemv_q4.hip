@@ -1451,9 +1451,12 @@ bool plan_integer(Geometry &p, int N, int K, const Knobs &k) {
     if (p.LPR == 32) {
         // Short rows (512 < K <= 1024): two rows per load instruction, no
         // K-split, one chunk per lane; 8 wavefronts once that still gives
-        // every CU a workgroup, else 4.
+        // every CU a workgroup, else 4.  2 row slots below 16384 rows (more,
+        // smaller wavefronts for these latency-bound shapes: 896 x 896 g32
+        // 3.32 -> 2.78 us, 4864 x 896 3.41 -> 3.12 us), else 4 (the 151936-row
+        // LM head: 17.4 against 18.9 us with 2, 24.1 with 8).
         if (k.ksplit && k.ksplit != 1) return false;
-        const int R = row_slots(1);
+        const int R = N < 16384 ? 2 : row_slots(1);
         const long groups = ((long)N + 2 * R - 1) / (2 * R);
         const int W = k.waves ? k.waves : (groups >= 8L * kCUs ? 8 : 4);
         const long grid = (groups + W - 1) / W;
@@ -1801,18 +1804,18 @@ void dispatch_jp(const Geometry &p, const float *x, const uint8_t *wq, const uin
     }
 }
 
-template <int W, int JP, int S, bool MULTI, int LPR = 64>
+template <int W, int JP, int S, bool MULTI, int LPR = 64, int RS = row_slots(1)>
 void launch_integer(const Geometry &p, const float *x, const uint8_t *wq, const uint16_t *scales,
                     const uint8_t *zeros, float *y, int N, int K, int gshift, hipStream_t st) {
     if constexpr (S == 1) {
         if (p.swi) {
-            hipLaunchKernelGGL((gemv_q4_int_kernel<W, LPR, JP, row_slots(1), S, MULTI, true>), dim3(p.grid),
+            hipLaunchKernelGGL((gemv_q4_int_kernel<W, LPR, JP, RS, S, MULTI, true>), dim3(p.grid),
                                dim3(W * 64), lds_bytes(p), st, x, wq, scales, zeros, y, N, K, gshift, p.rpg, 0,
                                p.swi->wq, p.swi->scales, p.swi->zeros);
             return;
         }
     }
-    hipLaunchKernelGGL((gemv_q4_int_kernel<W, LPR, JP, row_slots(1), S, MULTI>), dim3(p.grid), dim3(W * 64),
+    hipLaunchKernelGGL((gemv_q4_int_kernel<W, LPR, JP, RS, S, MULTI>), dim3(p.grid), dim3(W * 64),
                        lds_bytes(p), st, x, wq, scales, zeros, y, N, K, gshift, p.rpg, p.epi,
                        nullptr, nullptr, nullptr);
 }
@@ -1821,8 +1824,9 @@ template <int W, int S>
 void dispatch_integer_jp(const Geometry &p, const float *x, const uint8_t *wq, const uint16_t *scales,
                          const uint8_t *zeros, float *y, int N, int K, int gshift, hipStream_t st) {
     if constexpr (S == 1) {
-        if (p.LPR == 32) {
-            launch_integer<W, 1, 1, false, 32>(p, x, wq, scales, zeros, y, N, K, gshift, st);
+        if (p.LPR == 32) {   // two rows per load instruction: 2 row slots (4 rows) or 4
+            if (p.rows_per_wave == 4) launch_integer<W, 1, 1, false, 32, 2>(p, x, wq, scales, zeros, y, N, K, gshift, st);
+            else launch_integer<W, 1, 1, false, 32>(p, x, wq, scales, zeros, y, N, K, gshift, st);
             return;
         }
     }
