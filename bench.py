@@ -686,8 +686,14 @@ def run_configs(torch, q4, dev, W, two_pt: dict, floor: dict | None, cpu_s: floa
     y = [torch.empty((1, s.N), device=dev) for _ in mats]
     add("lm-head", "LM head 896->151936 g32, one matrix looped", cell_record(
         "gemv_q4", time_pass(torch, q4_pass(x, mats[:1], y[:1], s.g, 8), 8), nb, nb))
-    add("lm-head", "LM head 896->151936 g32, 8 matrices rotated", cell_record(
-        "gemv_q4", time_pass(torch, q4_pass(x, mats, y, s.g), 8), nb, 8 * nb))
+    rot = cell_record("gemv_q4", time_pass(torch, q4_pass(x, mats, y, s.g), 8), nb, 8 * nb)
+    del mats
+    torch.cuda.empty_cache()
+    fl = run_read_floor(torch, q4, dev, nb, 8)
+    add("lm-head", "LM head 896->151936 g32, 8 matrices rotated", with_floor(rot, fl))
+    add("lm-head", "read_reduce over 8 distinct 78.7 MB buffers (one launch each)",
+        cell_record("read_reduce", fl["stats"], nb, 8 * nb, workgroups=fl["workgroups"]))
+    mats = dev_mats(torch, dev, {k: v for k, v in d.items() if k != "x"}, 1, gen)
     ws = [dequant(mats[0], s.g)]
     ws.append(ws[0].clone())
     fbytes = 4 * s.N * s.K
@@ -737,7 +743,17 @@ def run_configs(torch, q4, dev, W, two_pt: dict, floor: dict | None, cpu_s: floa
         if not r:
             continue
         st = {q: (v * 1e-6 if v is not None and q != "n" else v) for q, v in r["per_launch_us"].items()}
-        add("stream", name, cell_record(k, st, b, ws_))
+        rec = cell_record(k, st, b, ws_)
+        if k == "gemv_q4" and floor:
+            rec = with_floor(rec, floor)
+        if k == "gemv_q4_swiglu":
+            fl = run_read_floor(torch, q4, dev, b, wl.STREAM_MATRICES // 2)
+            rec = with_floor(rec, fl)
+            add("stream", name, rec)
+            add("stream", "read_reduce over 16 distinct 61 MB buffers (one launch each)",
+                cell_record("read_reduce", fl["stats"], b, ws_, workgroups=fl["workgroups"]))
+            continue
+        add("stream", name, rec)
     if floor:
         add("stream", "read_reduce over 32 distinct 30.5 MB buffers (one launch each)",
             cell_record("read_reduce", floor["stats"], floor["bytes_per_launch"], floor["working_set_bytes"],
@@ -747,18 +763,24 @@ def run_configs(torch, q4, dev, W, two_pt: dict, floor: dict | None, cpu_s: floa
             "cpu_oracle": {str(k): v for k, v in cpu.items()}}
 
 
-FLOOR_GRIDS = (256, 512, 768, 1024, 1536, 2048)
+FLOOR_GRIDS = (256, 512, 768, 1024, 1536, 2048, 4096)
 
 
 def run_stream_floor(torch, q4, dev) -> dict:
     """The single-launch read floor of the headline's size: read_reduce over
     32 distinct buffers of 30,507,008 B (one stream matrix's bytes; 976 MB
-    cycled, past the Infinity Cache), one launch per buffer, non-temporal
-    loads, at the fastest of FLOOR_GRIDS workgroup counts."""
+    cycled, past the Infinity Cache), one launch per buffer."""
     nbytes = wl.q4_weight_bytes(wl.STREAM_SHAPE.N, wl.STREAM_SHAPE.K, wl.STREAM_SHAPE.g)
+    return run_read_floor(torch, q4, dev, nbytes, wl.STREAM_MATRICES)
+
+
+def run_read_floor(torch, q4, dev, nbytes: int, count: int) -> dict:
+    """The single-launch read floor of a launch that reads nbytes: read_reduce
+    over `count` distinct buffers of that size, one launch per buffer,
+    non-temporal loads, at the fastest of FLOOR_GRIDS workgroup counts."""
     nf = nbytes // 4
-    buf = torch.rand(wl.STREAM_MATRICES * nf, device=dev)
-    bufs = [buf[i * nf:(i + 1) * nf] for i in range(wl.STREAM_MATRICES)]
+    buf = torch.rand(count * nf, device=dev)
+    bufs = [buf[i * nf:(i + 1) * nf] for i in range(count)]
     parts = torch.empty(max(FLOOR_GRIDS), device=dev)
     best = None
     for grid in FLOOR_GRIDS:
@@ -766,15 +788,22 @@ def run_stream_floor(torch, q4, dev) -> dict:
             for b in bufs:
                 q4.read_reduce(b, grid, partials=parts)
         st = time_pass(torch, fn, len(bufs))
-        log(f"single-launch floor, {grid} workgroups: {st['median'] * 1e6:.3f} us/launch, "
+        log(f"single-launch floor over {nbytes} B, {grid} workgroups: {st['median'] * 1e6:.3f} us/launch, "
             f"{nbytes / st['median'] / 1e9:.1f} GB/s")
         if best is None or st["median"] < best[0]["median"]:
             best = (st, grid)
     del buf, bufs
     torch.cuda.empty_cache()
     return {"stats": best[0], "workgroups": best[1], "bytes_per_launch": nbytes,
-            "working_set_bytes": wl.STREAM_MATRICES * nbytes,
+            "working_set_bytes": count * nbytes,
             "GBps_median": round(nbytes / best[0]["median"] / 1e9, 1)}
+
+
+def with_floor(rec: dict, fl: dict) -> dict:
+    """A streaming cell with the single-launch read floor of its own size."""
+    us = fl["stats"]["median"] * 1e6
+    return dict(rec, single_launch_floor_us=round(us, 3),
+                frac_of_single_launch_floor=round(us / rec["us_per_launch"]["median"], 4))
 
 
 # ---------------------------------------------------------------- block formats

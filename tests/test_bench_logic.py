@@ -179,3 +179,11 @@ def test_summarize_counters_derived_lines(tmp_path, monkeypatch):
     assert f"{4096 * 500 / (bench.SIMDS * us * 1e3):.3f} issued per SIMD per ns" in text
     assert "LDS busy 25.0% of the dispatch's CU cycles" in text and "bank-conflict cycles 7" in text
     assert "fp32 FMA 20.0% of the VALU instructions" in text
+
+
+def test_with_floor_records_the_fraction():
+    """A streaming cell carries the read floor of its own size and its share of it."""
+    rec = {"us_per_launch": {"median": 10.0}}
+    out = bench.with_floor(rec, {"stats": {"median": 8e-6}})
+    assert out["single_launch_floor_us"] == 8.0 and out["frac_of_single_launch_floor"] == 0.8
+    assert "single_launch_floor_us" not in rec
