@@ -1356,7 +1356,7 @@ def summarize_counters(dirs: list[str], name: str, command: str) -> str:
     per, dur, grid = {}, {}, {}
     for d in dirs:
         for k, r in _keyed_rows(d):
-            if not re.match(r"(gemv_q4|gemv_blk|read_reduce|fm_sum_parts)", k):
+            if not re.match(r"(gemv_q4|gemv_blk|read_reduce|fm_sum_parts|scan2)", k):
                 continue
             per.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
             dur.setdefault(k, {})[(d, r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
