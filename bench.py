@@ -1191,6 +1191,8 @@ def run_blocks_only(args):
     only = set(args.block_shapes.split(",")) if args.block_shapes else None
     dev = torch.device("cuda:0")
     out = {"unit": "GB/s", "peak": SPEC_PEAK_GBS}
+    # the same geometries as the default run
+    out["geometry_profile"] = apply_tuned_profile(dev)
     if not only or only - {"scan", "layer", "sweep", "ffn"}:
         out["block_formats"] = run_block_formats(torch, q4, dev, only=only)
     if not only or "scan" in only:
