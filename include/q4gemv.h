@@ -57,12 +57,15 @@ enum q4_status {
 /* int4 decode GEMV: y[M, N] = x[M, K] . dequant(W_q[N, K])^T, fp32 accumulate
  * (gerbil "WGSL Kernel Reference", section 3 MatMulInt4, "Dequantization").
  * Two arithmetic paths (gemv_q4_path tells which one a shape takes):
- *   - fused multiply-add (2 to 8 rows; one row with K <= 512 or
- *     K > 19264): (q - z) formed exactly (in fp32 for 2 to 8 rows, in
- *     binary16 for one row), multiplied by the fp32 x with fp32 fused
- *     multiply-adds, the group scale applied per 32-code chunk;
- *   - integer (M == 1: 512 < K <= 19264; 2 to 8 rows with K > 1024 only when
- *     fixed with gemv_q4_set_geometry): every chunk of 32 values
+ *   - fused multiply-add (2 to 8 rows; one row with K <= 512, or with K
+ *     past the integer path's limit below): (q - z) formed exactly (in fp32
+ *     for 2 to 8 rows, in binary16 for one row), multiplied by the fp32 x
+ *     with fp32 fused multiply-adds, the group scale applied per 32-code
+ *     chunk;
+ *   - integer (M == 1: 512 < K <= 19232, or <= 19264 where N is small
+ *     enough for 4-wavefront workgroups, as the LDS must hold the chunk
+ *     records of all of x; 2 to 8 rows with K > 1024 only when fixed with
+ *     gemv_q4_set_geometry): every chunk of 32 values
  *     of an x row (x[m][32c .. 32c+31]) is written as X + r with
  *     X = rint(x * 2^sh) an integer, |X| <= 2^26 (2^(25-sh) <= max|x| over
  *     the chunk < 2^(26-sh)), and r the exact residual; the sum of (q - z) * X

@@ -186,7 +186,8 @@ def test_geometry_covers_every_row(shape):
 PATHS = [
     # M, N, K, g, path: one activation row with more than 16 chunks per row takes the integer path
     (1, 14336, 4096, 128, 1), (1, 4096, 14336, 128, 1), (1, 65, 2048, 128, 1),
-    (1, 1, 18688, 128, 1), (1, 1, 19200, 128, 1), (1, 4, 19328, 128, 0), (1, 2, 19264, 32, 1), (1, 896, 896, 32, 1), (1, 151936, 896, 32, 1),
+    (1, 1, 18688, 128, 1), (1, 1, 19200, 128, 1), (1, 4, 19328, 128, 0), (1, 2, 19264, 32, 1),
+    (1, 4096, 19232, 32, 1), (1, 4096, 19264, 32, 0), (1, 896, 896, 32, 1), (1, 151936, 896, 32, 1),
     (1, 63, 2016, 32, 1), (1, 7, 1024, 32, 1), (1, 9, 512, 32, 0), (1, 9, 544, 32, 1),
     # 2 to 8 activation rows take the fp32 multiply-add path (the integer one only on request)
     (2, 14336, 4096, 128, 0), (8, 4096, 14336, 128, 0),
