@@ -8,6 +8,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -248,6 +249,20 @@ def test_workspace_size(M, N, K, g, split):
     else:
         assert n == 0
     assert q4.gemv_q4_workspace_size(M, 0, K, g) == 0
+
+
+def test_static_array_holds_every_planned_workspace():
+    """gemv_q4_static's 512 KiB array must cover every K split the planner
+    makes, or the entry point would refuse shapes gemv_q4_ws serves."""
+    rng = np.random.default_rng(8)
+    shapes = [(M, N, K, g) for M in range(1, 9) for g in (32, 128)
+              for N in (1, 64, 896, 2048, 2049, 4096, 8192, 16384, 151936)
+              for K in (g, 1024, 4096, 14336, 16384, 28672, 1 << 20) if K % g == 0]
+    for _ in range(3000):
+        g = int(rng.choice([32, 128]))
+        shapes.append((int(rng.integers(1, 9)), int(rng.integers(1, 300000)), g * int(rng.integers(1, 2049)), g))
+    worst = max(q4.gemv_q4_workspace_size(*s) for s in shapes)
+    assert 0 < worst <= 512 * 1024
 
 
 def test_workspace_entry_points_validate(L):
