@@ -1216,17 +1216,22 @@ PMC_BLOCK_MATRICES = 8
 PMC_READ_KERNEL = "read_reduce_kernel<true>"   # read_reduce's (non-temporal) kernel
 PMC_FLOOR_GRID = 2048       # workgroups of the single-launch floor (its fastest in FLOOR_GRIDS)
 PMC_FFN_MATRICES = 8        # distinct matrices per FFN projection at M = 4 and 8
+PMC_LM_MATRICES = 4         # distinct LM head matrices (315 MB, past the 256 MB MALL)
 
 
 def run_pmc_workload(args):
     """A short, fixed dispatch sequence for counter collection: 64 gemv_q4 launches
     over the 32 stream matrices, 2 read_reduce and 2 write_fill over 2 GiB (the
-    calibration kernels of known size), 4 gemv_f32 launches; then 16 gemv_block
-    launches per format at the stream shape over 8 distinct matrices, and 8
-    scans of distinct 65,536 x 768 corpora."""
+    calibration kernels of known size), 4 gemv_f32 launches; the read floor;
+    4 and 8 rows of each FFN projection; 8 LM head launches over 4 distinct
+    matrices; then 16 gemv_block launches per format at the stream shape over 8
+    distinct matrices, and 8 scans of distinct 65,536 x 768 corpora.  The tuned
+    geometry profile is applied first, so the counters describe the launches
+    the default run times."""
     import torch
     import memory_bandwidth_amd as q4
     dev = torch.device("cuda:0")
+    apply_tuned_profile(dev)
     W = setup_stream(torch, q4, dev)
     s = W["shape"]
     for _ in range(2):
@@ -1263,6 +1268,19 @@ def run_pmc_workload(args):
                 q4.gemv_q4(xx, m["wq"], m["scales"], m["zeros"], sh.g, out=y)
             torch.cuda.synchronize()
             del mats
+    torch.cuda.empty_cache()
+    # the LM head 896 -> 151936 g32: PMC_LM_MATRICES distinct matrices (more
+    # bytes than the MALL holds), each launched twice
+    sh = wl.LM_HEAD
+    h = wl.make_q4_problem(wl.workload_seed(2), sh)
+    xx = torch.from_numpy(h["x"]).to(dev)
+    mats = dev_mats(torch, dev, {k: v for k, v in h.items() if k != "x"}, PMC_LM_MATRICES, gen)
+    y = torch.empty((1, sh.N), device=dev)
+    for _ in range(2):
+        for m in mats:
+            q4.gemv_q4(xx, m["wq"], m["scales"], m["zeros"], sh.g, out=y)
+    torch.cuda.synchronize()
+    del mats
     torch.cuda.empty_cache()
     # every block format at the stream shape, 8 distinct matrices launched twice
     gen = torch.Generator(device=dev)
@@ -1368,8 +1386,10 @@ def summarize_counters(dirs: list[str], name: str, command: str) -> str:
              "(the stream kernel: 64 launches over 32 matrices; the read floor: 32 buffers of "
              "30.5 MB, one launch each; 4 and 8 rows: 8 matrices per FFN projection, the "
              "up projection 4096 -> 14336 plain, the down projection 14336 -> 4096 split over "
-             "K with a workspace (marked K split, then fm_sum_parts adds the parts); the block "
-             "formats at the stream shape: 16 launches over 8 matrices each).  "
+             "K with a workspace (marked K split, then fm_sum_parts adds the parts); the LM "
+             "head 896 -> 151936 g32 (the short-row kernel, 32 lanes per row): 8 launches over "
+             "4 matrices; the block formats at the stream shape: 16 launches over 8 matrices "
+             "each).  "
              "Durations are those of the counter runs (serialised dispatches).", ""]
     ctrs = [c for p in PMC_COUNTER_PASSES for c in p.split()]
     for k in sorted(per):
@@ -1511,6 +1531,12 @@ def summarize_pmc(fetch_dir: str, write_dir: str, name: str, command: str) -> st
             w = mean.get((k, "WRITE_SIZE"), 0.0) * 1024 * write_factor
             lines.append(f"{k} per launch (an FFN projection, {a} B of weights): {f:.0f} B fetched "
                          f"(ratio {f / a:.4f}), {w:.0f} B written.")
+        elif k.startswith("gemv_q4_int_kernel<8, 32,"):
+            lm = wl.LM_HEAD
+            a = wl.q4_weight_bytes(lm.N, lm.K, lm.g)
+            f = mean[(k, "FETCH_SIZE")] * 1024 * fetch_factor
+            lines.append(f"{k} per launch (the LM head 896 -> 151936 g32, {a} B): {f:.0f} B "
+                         f"fetched, ratio {f / a:.4f}.")
         elif k == "fm_sum_parts":
             f = mean[(k, "FETCH_SIZE")] * 1024 * fetch_factor
             w = mean.get((k, "WRITE_SIZE"), 0.0) * 1024 * write_factor
