@@ -112,6 +112,7 @@ def _counter_csv(path, rows):
 FM = "void (anonymous namespace)::gemv_q4_fm_kernel<8, 8, 2, 16, 1, 8, 2, true>(float const*, int)"
 SUM = "(anonymous namespace)::fm_sum_parts(float*, float const*, int, int, int)"
 INT = "void (anonymous namespace)::gemv_q4_int_kernel<8, 64, 2, 4, 1, false, false, 16>(float const*)"
+LM = "void (anonymous namespace)::gemv_q4_int_kernel<8, 32, 1, 4, 1, false, false, 16>(float const*)"
 RR = "void (anonymous namespace)::read_reduce_kernel<true>(float const*, float*, long)"
 WF = "void (anonymous namespace)::write_fill_kernel(float*, float, long)"
 
@@ -150,12 +151,17 @@ def test_summarize_pmc_scales_by_the_probes(tmp_path, monkeypatch):
         write.append(_row(i, INT, "WRITE_SIZE", 64.0))
     fetch.append(_row(99, FM, "FETCH_SIZE", 16000.0))
     write.append(_row(99, FM, "WRITE_SIZE", 400.0))
+    lm_kib = bench.wl.q4_weight_bytes(bench.wl.LM_HEAD.N, bench.wl.LM_HEAD.K, bench.wl.LM_HEAD.g) / 1024 / 2
+    for i in range(100, 108):     # the LM head kernel: fewer dispatches, not taken for the stream
+        fetch.append(_row(i, LM, "FETCH_SIZE", lm_kib))
+        write.append(_row(i, LM, "WRITE_SIZE", 593.5))
     _counter_csv(tmp_path / "f" / "run_counter_collection.csv", fetch)
     _counter_csv(tmp_path / "w" / "run_counter_collection.csv", write)
-    bench.summarize_pmc(str(tmp_path / "f"), str(tmp_path / "w"), "t", "cmd")
+    out = bench.summarize_pmc(str(tmp_path / "f"), str(tmp_path / "w"), "t", "cmd")
+    assert "(the LM head 896 -> 151936 g32, 78702848 B): 78702848 B fetched, ratio 1.0000" in open(out).read()
     j = json.load(open(tmp_path / "profiles" / "pmc.json"))
     assert j["fetch_factor"] == pytest.approx(2.0) and j["write_factor"] == pytest.approx(1.0)
-    assert j["kernel"].startswith("gemv_q4_int_kernel")
+    assert j["kernel"].startswith("gemv_q4_int_kernel<8, 64")
     assert j["gemv_q4_fetch_bytes_per_launch"] == round(15000.0 * 1024 * 2)
     assert j["gemv_q4_write_bytes_per_launch"] == 64 * 1024
     assert j["kernel_source_sha256_16"] == bench.kernel_source_hash()
