@@ -150,6 +150,8 @@ RAGGED = [
     (7, 257, 4864, 32), (8, 67, 14336, 128), (1, 45, 14336, 128), (2, 300, 8192, 128),
     (1, 1, 16384, 128), (8, 9, 18432, 128), (1, 4097, 384, 128), (8, 1, 32, 32),
     (8, 100, 32768, 128), (3, 70, 32768, 32), (1, 33, 32768, 128),
+    # the longest rows the one-row integer kernel takes: all of x's records fill the LDS
+    (1, 4096, 19232, 32), (1, 2, 19264, 32),
     # several x segments of the multiply-add kernel, the last one shorter
     (3, 300, 14336, 128), (5, 200, 14336, 128), (4, 96, 14336, 32), (6, 50, 9216, 128),
 ]
@@ -162,6 +164,26 @@ def test_gemv_q4_ragged(M, N, K, g):
     y = run_q4(dev(d), g)
     y_ref, b = oracle.gemv_q4(d["x"], d["wq"], d["scales"], d["zeros"], g)
     assert_within(y, y_ref, b, f"M{M} N{N} K{K} g{g}")
+
+
+LONGEST = [(1, 3, 1 << 24, 128), (8, 2, 1 << 24, 32), (3, 5, (1 << 24) - 128, 128)]
+
+
+@pytest.mark.parametrize("M,N,K,g", LONGEST, ids=[f"M{a}N{b}K{c}g{d}" for a, b, c, d in LONGEST])
+def test_gemv_q4_longest_k(M, N, K, g):
+    """The longest K a call accepts (2^24): every 32-bit buffer offset of the
+    kernels is then at its largest.  With and without a workspace (a K split
+    over workgroups where the plan makes one)."""
+    print(f"longest K: M{M} N{N} K{K} g{g}", flush=True)
+    s = wl.Q4Shape(M, N, K, g, 0.002, 0.02)
+    d = wl.make_q4_problem(4242 + M, s)
+    t = dev(d)
+    y_ref, b = oracle.gemv_q4(d["x"], d["wq"], d["scales"], d["zeros"], g)
+    y = q4.gemv_q4(t["x"], t["wq"], t["scales"], t["zeros"], g)
+    y_plain = q4.gemv_q4(t["x"], t["wq"], t["scales"], t["zeros"], g, workspace=False)
+    torch.cuda.synchronize()
+    assert_within(y.cpu().numpy(), y_ref, b, f"longest K M{M} N{N} K{K} g{g}")
+    assert_within(y_plain.cpu().numpy(), y_ref, b, f"longest K, no workspace, M{M} N{N} K{K} g{g}")
 
 
 EXACT = [(1, 14336, 4096, 128), (1, 4096, 14336, 128), (8, 333, 14336, 128), (4, 515, 4096, 128),
